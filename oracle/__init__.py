@@ -1,0 +1,198 @@
+"""CPU oracle of the Q8_0 weight product -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its binding) never
+does; the two share no code.  The arithmetic lives in ``q8_oracle.c`` (plain C,
+fp64 / int64), built by ``oracle/build.py``; this module marshals numpy arrays
+to it.
+
+Every array here is in the canonical layout of the pages
+(logicaffeine_compile/spatial/passes/from_q8.rs, module doc): values ``q`` are
+``K x N`` int8 (k outer), scales ``s`` are ``K/32 x N`` fp32, the activation
+``x`` is ``m x K`` bf16 given as its raw uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+BLOCK = 32
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build  # compiles the C oracle with gcc
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.q8o_set_threads.argtypes = [ctypes.c_int]
+    lib.q8o_threads.restype = ctypes.c_int
+    lib.q8o_quantize_exact.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.q8o_quantize_exact.restype = ctypes.c_int
+    lib.q8o_dequant.argtypes = [_p, _p, _i64, _i64, _p]
+    lib.q8o_quantize_act.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.q8o_gemv_bf16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+    lib.q8o_gemv_bf16.restype = ctypes.c_int
+    lib.q8o_block_dots.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p]
+    lib.q8o_block_dots.restype = ctypes.c_int
+    lib.q8o_gemv_q8.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+    lib.q8o_gemv_q8.restype = ctypes.c_int
+    lib.q8o_view_rows.argtypes = [_i64, _i64]
+    lib.q8o_view_rows.restype = _i64
+    lib.q8o_fold_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64,
+                                   ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use (0: the OpenMP default)."""
+    _load().q8o_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(_load().q8o_threads())
+
+
+def _cols(cols: Optional[Sequence[int]], N: int):
+    if cols is None:
+        return None, N
+    c = _c(cols, np.int64)
+    if c.ndim != 1 or (c.size and (c.min() < 0 or c.max() >= N)):
+        raise ValueError("column list out of range")
+    return c, int(c.size)
+
+
+def quantize_exact(w: np.ndarray) -> Optional[Tuple[np.ndarray, np.ndarray]]:
+    """The pages' exact Q8_0 encoder (from_q8.rs, fn quantize): ``(q, s)``, or
+    ``None`` when some block is not an int8 multiple of its fp32 ``amax/127``."""
+    w = _c(w, np.float64)
+    K, N = w.shape
+    q = np.zeros((K, N), np.int8)
+    s = np.zeros((K // BLOCK, N), np.float32)
+    rc = _load().q8o_quantize_exact(_ptr(w), K, N, _ptr(q), _ptr(s))
+    if rc < 0:
+        raise ValueError(f"bad shape {w.shape}: K must be a positive multiple of {BLOCK}")
+    return (q, s) if rc == 1 else None
+
+
+def dequant(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """``w = q * d`` per element, fp64."""
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    K, N = q.shape
+    w = np.empty((K, N), np.float64)
+    _load().q8o_dequant(_ptr(q), _ptr(s), K, N, _ptr(w))
+    return w
+
+
+def quantize_act(x_bf16: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-32-block int8 activation and its fp32 scales (reading in q8_oracle.c)."""
+    x = _c(x_bf16, np.uint16)
+    m, K = x.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    xq = np.empty((m, K), np.int8)
+    dx = np.empty((m, K // BLOCK), np.float32)
+    _load().q8o_quantize_act(_ptr(x), m, K, _ptr(xq), _ptr(dx))
+    return xq, dx
+
+
+def gemv_bf16(x_bf16: np.ndarray, q: np.ndarray, s: np.ndarray,
+              cols: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """``(y, bound)``, both fp64 ``m x len(cols)``: ``y = x . W`` and
+    ``bound = sum_k |x_k w_kn|`` for bf16 activations."""
+    x = _c(x_bf16, np.uint16)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    m, K = x.shape
+    K2, N = q.shape
+    if K2 != K or s.shape != (K // BLOCK, N):
+        raise ValueError("shape mismatch")
+    c, nc = _cols(cols, N)
+    y = np.empty((m, nc), np.float64)
+    b = np.empty((m, nc), np.float64)
+    rc = _load().q8o_gemv_bf16(_ptr(x), _ptr(q), _ptr(s), m, K, N,
+                               None if c is None else _ptr(c), nc, _ptr(y), _ptr(b))
+    if rc:
+        raise ValueError("bad shape")
+    return y, b
+
+
+def block_dots(xq: np.ndarray, q: np.ndarray,
+               cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """int64 ``D[r, b, j] = sum_i xq[r, 32b+i] * q[32b+i, cols[j]]``."""
+    xq = _c(xq, np.int8)
+    q = _c(q, np.int8)
+    m, K = xq.shape
+    K2, N = q.shape
+    if K2 != K:
+        raise ValueError("shape mismatch")
+    c, nc = _cols(cols, N)
+    D = np.empty((m, K // BLOCK, nc), np.int64)
+    rc = _load().q8o_block_dots(_ptr(xq), _ptr(q), m, K, N,
+                                None if c is None else _ptr(c), nc, _ptr(D))
+    if rc:
+        raise ValueError("bad shape")
+    return D
+
+
+def gemv_q8(xq: np.ndarray, dx: np.ndarray, q: np.ndarray, s: np.ndarray,
+            cols: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """``(y, bound)`` for int8 activations ``x_k = dx[r, k/32] * xq[r, k]``."""
+    xq = _c(xq, np.int8)
+    dx = _c(dx, np.float32)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    m, K = xq.shape
+    K2, N = q.shape
+    if K2 != K or dx.shape != (m, K // BLOCK) or s.shape != (K // BLOCK, N):
+        raise ValueError("shape mismatch")
+    c, nc = _cols(cols, N)
+    y = np.empty((m, nc), np.float64)
+    b = np.empty((m, nc), np.float64)
+    rc = _load().q8o_gemv_q8(_ptr(xq), _ptr(dx), _ptr(q), _ptr(s), m, K, N,
+                             None if c is None else _ptr(c), nc, _ptr(y), _ptr(b))
+    if rc:
+        raise ValueError("bad shape")
+    return y, b
+
+
+def view_rows(m: int, K: int) -> int:
+    """Rows of the ``K/32 x 32`` activation view (from_q8.rs, fn q8_view_rows)."""
+    return int(_load().q8o_view_rows(m, K))
+
+
+def fold_bytes(m: int, K: int, N: int, wb: int, x_bytes: int) -> Tuple[int, int]:
+    """``(weight, view_reads)`` bytes of the fold by the byte gate of
+    from_q8.rs, fn q8_gemv (32-wide column tiles, 1024-row K chunks)."""
+    w = _i64()
+    v = _i64()
+    _load().q8o_fold_bytes(m, K, N, wb, x_bytes, ctypes.byref(w), ctypes.byref(v))
+    return int(w.value), int(v.value)
+
+
+def tolerance_ok(y_gpu: np.ndarray, y_ref: np.ndarray, bound: np.ndarray,
+                 rel: float = 1e-5, abs_: float = 1e-6) -> np.ndarray:
+    """Elementwise ``|y_gpu - y_ref| <= rel * bound + abs_``."""
+    return np.abs(np.asarray(y_gpu, np.float64) - y_ref) <= rel * bound + abs_

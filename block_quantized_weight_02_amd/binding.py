@@ -1,0 +1,221 @@
+"""ctypes binding of libq8gemv.so, the C ABI in include/q8gemv.h.
+
+Argument marshalling only: every function has the C name, takes device
+buffers as torch tensors (or raw integer addresses), sizes as ints and an
+optional stream (default: torch's current stream on the current device), and
+raises ``Q8Error`` carrying the status and ``q8_last_error()`` on failure.
+All arithmetic runs in the library's HIP kernels; when the library is not
+built, every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq8gemv.so")
+
+Q8_ACT_BF16 = 0
+Q8_ACT_Q8_0 = 1
+Q8_KERNEL_VALU = 0
+Q8_KERNEL_MFMA = 1
+
+STATUS = {0: "Q8_OK", 1: "Q8_ERR_SHAPE", 2: "Q8_ERR_ACT_FMT", 3: "Q8_ERR_NULL",
+          4: "Q8_ERR_ALIGN", 5: "Q8_ERR_WORKSPACE", 6: "Q8_ERR_HIP", 7: "Q8_ERR_PLAN"}
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class q8_plan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"q8_plan(kernel={self.kernel}, rows={self.rows}, "
+                f"split_k={self.split_k}, waves={self.waves})")
+
+
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_p = ctypes.c_void_p
+_int = ctypes.c_int
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "q8_padded_cols": (_i64, [_i64]),
+    "q8_packed_values_bytes": (_sz, [_i64, _i64]),
+    "q8_packed_scales_bytes": (_sz, [_i64, _i64]),
+    "q8_act_scales_offset": (_sz, [_i64, _i64]),
+    "q8_act_bytes": (_sz, [_i64, _i64]),
+    "q8_gemv_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
+    "q8_repack": (_int, [_p, _p, _i64, _i64, _p, _p, _p]),
+    "q8_unpack": (_int, [_p, _p, _i64, _i64, _p, _p, _p]),
+    "q8_quantize_act": (_int, [_p, _p, _i64, _i64, _p]),
+    "q8_gemv": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
+    "q8_gemv_ws": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _p, _sz]),
+    "q8_gemv_block_dots": (_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "q8_gemv_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_plan)]),
+    "q8_plan_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), _i64, _i64, _i64]),
+    "q8_gemv_planned": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int,
+                               ctypes.POINTER(q8_plan), _p, _p, _sz]),
+    "q8_gemv_block_dots_planned": (_int, [_p, _p, _p, _i64, _i64, _i64,
+                                          ctypes.POINTER(q8_plan), _p]),
+    "q8_status_string": (ctypes.c_char_p, [_int]),
+    "q8_last_error": (ctypes.c_char_p, []),
+    "q8_release_workspaces": (_int, []),
+    "q8_layout_version": (_int, []),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise Q8Error(6, f"{LIB_PATH} is not built: run "
+                                 "`python -m block_quantized_weight_02_amd.build`")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(handle, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def exported_names():
+    return list(_SIGS)
+
+
+def _addr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = lib().q8_last_error()
+        raise Q8Error(status, msg.decode() if msg else "")
+
+
+# ---- sizes ---------------------------------------------------------------------
+
+def q8_padded_cols(N: int) -> int:
+    return int(lib().q8_padded_cols(N))
+
+
+def q8_packed_values_bytes(K: int, N: int) -> int:
+    return int(lib().q8_packed_values_bytes(K, N))
+
+
+def q8_packed_scales_bytes(K: int, N: int) -> int:
+    return int(lib().q8_packed_scales_bytes(K, N))
+
+
+def q8_act_scales_offset(m: int, K: int) -> int:
+    return int(lib().q8_act_scales_offset(m, K))
+
+
+def q8_act_bytes(m: int, K: int) -> int:
+    return int(lib().q8_act_bytes(m, K))
+
+
+def q8_gemv_workspace_bytes(m: int, K: int, N: int, act_fmt: int) -> int:
+    return int(lib().q8_gemv_workspace_bytes(m, K, N, act_fmt))
+
+
+# ---- calls ----------------------------------------------------------------------
+
+def q8_repack(q_kn, s_kn, K, N, W_q8, W_q8_scale, stream=None) -> None:
+    _check(lib().q8_repack(_addr(q_kn), _addr(s_kn), K, N, _addr(W_q8),
+                           _addr(W_q8_scale), _stream(stream)))
+
+
+def q8_unpack(W_q8, W_q8_scale, K, N, q_kn, s_kn, stream=None) -> None:
+    _check(lib().q8_unpack(_addr(W_q8), _addr(W_q8_scale), K, N, _addr(q_kn),
+                           _addr(s_kn), _stream(stream)))
+
+
+def q8_quantize_act(x_bf16, x_q8, m, K, stream=None) -> None:
+    _check(lib().q8_quantize_act(_addr(x_bf16), _addr(x_q8), m, K, _stream(stream)))
+
+
+def q8_gemv(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream=None) -> None:
+    _check(lib().q8_gemv(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y),
+                         m, K, N, act_fmt, _stream(stream)))
+
+
+def q8_gemv_ws(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream, workspace,
+               ws_bytes) -> None:
+    _check(lib().q8_gemv_ws(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y),
+                            m, K, N, act_fmt, _stream(stream), _addr(workspace),
+                            ws_bytes))
+
+
+def q8_gemv_block_dots(x_q8, W_q8, dots, m, K, N, stream=None) -> None:
+    _check(lib().q8_gemv_block_dots(_addr(x_q8), _addr(W_q8), _addr(dots), m, K, N,
+                                    _stream(stream)))
+
+
+def q8_gemv_default_plan(m, K, N, act_fmt) -> q8_plan:
+    p = q8_plan()
+    _check(lib().q8_gemv_default_plan(m, K, N, act_fmt, ctypes.byref(p)))
+    return p
+
+
+def q8_plan_workspace_bytes(plan: q8_plan, m, K, N) -> int:
+    return int(lib().q8_plan_workspace_bytes(ctypes.byref(plan), m, K, N))
+
+
+def q8_gemv_planned(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, plan: q8_plan,
+                    stream=None, workspace=None, ws_bytes=0) -> None:
+    _check(lib().q8_gemv_planned(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y),
+                                 m, K, N, act_fmt, ctypes.byref(plan), _stream(stream),
+                                 _addr(workspace), ws_bytes))
+
+
+def q8_gemv_block_dots_planned(x_q8, W_q8, dots, m, K, N, plan: q8_plan,
+                               stream=None) -> None:
+    _check(lib().q8_gemv_block_dots_planned(_addr(x_q8), _addr(W_q8), _addr(dots),
+                                            m, K, N, ctypes.byref(plan), _stream(stream)))
+
+
+def q8_status_string(status: int) -> str:
+    return lib().q8_status_string(status).decode()
+
+
+def q8_last_error() -> str:
+    return lib().q8_last_error().decode()
+
+
+def q8_release_workspaces() -> None:
+    _check(lib().q8_release_workspaces())
+
+
+def q8_layout_version() -> int:
+    return int(lib().q8_layout_version())

@@ -1,0 +1,445 @@
+// q8_api.cpp -- host side of the C ABI declared in include/q8gemv.h:
+// argument validation (before any launch), the launch plan, the split-K
+// workspace cache, and error reporting.
+//
+// Shape rules follow docs.logicaffeine.com, logicaffeine_compile/spatial/
+// passes/from_q8.rs, fn q8_gemv_applies (1 <= m <= 32 rows, K > 0 and whole
+// 32-row blocks, N > 0, the last column tile zero-padded) and the whole-block
+// check of codegen_cuda/lane/plan.rs, fn whole_blocks, whose error names the
+// declared length and the next whole bound.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/q8gemv.h"
+#include "q8_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return Q8_OK;
+}
+
+int64_t round_up(int64_t v, int64_t to) { return (v + to - 1) / to * to; }
+
+// Largest sizes the 32-bit launch arithmetic admits (checked, not assumed).
+constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+int check_kn(int64_t K, int64_t N) {
+  if (K <= 0 || K > kMaxK)
+    return fail(Q8_ERR_SHAPE, "K = %lld out of range: need 0 < K <= %lld",
+                (long long)K, (long long)kMaxK);
+  if (K % Q8_BLOCK != 0)
+    return fail(Q8_ERR_SHAPE,
+                "K = %lld is not whole %d-row blocks: declared %lld, bound %lld",
+                (long long)K, Q8_BLOCK, (long long)K,
+                (long long)round_up(K, Q8_BLOCK));
+  if (N < 1 || N > kMaxN)
+    return fail(Q8_ERR_SHAPE, "N = %lld out of range: need 1 <= N <= %lld",
+                (long long)N, (long long)kMaxN);
+  if (K * round_up(N, Q8_TILE_COLS) >= (int64_t(1) << 40))
+    return fail(Q8_ERR_SHAPE, "K*N_pad = %lld exceeds 2^40",
+                (long long)(K * round_up(N, Q8_TILE_COLS)));
+  return Q8_OK;
+}
+
+int check_m(int64_t m) {
+  if (m < 1 || m > Q8_MAX_ROWS)
+    return fail(Q8_ERR_SHAPE, "m = %lld out of range: need 1 <= m <= %d",
+                (long long)m, Q8_MAX_ROWS);
+  return Q8_OK;
+}
+
+int check_act(int act_fmt) {
+  if (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)
+    return fail(Q8_ERR_ACT_FMT, "act_fmt = %d: no kernel for it (0 bf16, 1 Q8_0)",
+                act_fmt);
+  return Q8_OK;
+}
+
+int check_ptr(const void *p, const char *name) {
+  if (!p) return fail(Q8_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(Q8_ERR_ALIGN, "%s = %p is not 16-byte aligned", name, p);
+  return Q8_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(Q8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t act_scales_offset(int64_t m, int64_t K) {
+  return (size_t)round_up(m * K, 256);
+}
+
+// ---- device facts -----------------------------------------------------------
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+// ---- plans --------------------------------------------------------------------
+
+int rows_for(int64_t m) {
+  int r = 1;
+  while (r < m) r *= 2;
+  return r;
+}
+
+// The default launch: the VALU kernel at the smallest row count >= m; K split
+// across workgroups until the grid holds about four workgroups per CU, while
+// each split keeps at least 16 blocks (4 waves x 4 blocks in flight).
+q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
+  (void)act_fmt;
+  const int64_t NB = K / Q8_BLOCK;
+  const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
+  const int64_t cus = device_cus();
+  const int64_t want = 4 * cus;
+  int64_t S = (want + T - 1) / T;
+  const int64_t smax = NB / 16 > 0 ? NB / 16 : 1;
+  if (S > smax) S = smax;
+  if (S < 1) S = 1;
+  q8_plan p;
+  p.kernel = Q8_KERNEL_VALU;
+  p.rows = rows_for(m);
+  p.split_k = (int32_t)S;
+  p.waves = 4;
+  return p;
+}
+
+int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
+  if (!p) return fail(Q8_ERR_NULL, "plan is NULL");
+  const int64_t NB = K / Q8_BLOCK;
+  if (p->rows < m || p->rows > Q8_MAX_ROWS || (p->rows & (p->rows - 1)) != 0)
+    return fail(Q8_ERR_PLAN, "plan rows = %d: need a power of two in [m = %lld, %d]",
+                p->rows, (long long)m, Q8_MAX_ROWS);
+  if (p->split_k < 1 || p->split_k > NB)
+    return fail(Q8_ERR_PLAN, "plan split_k = %d: need 1 <= split_k <= K/32 = %lld",
+                p->split_k, (long long)NB);
+  if (!q8::gemv_instantiated(p->kernel, p->rows, act, dots, p->waves))
+    return fail(Q8_ERR_PLAN, "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d",
+                p->kernel, p->rows, act, (int)dots, p->waves);
+  return Q8_OK;
+}
+
+// Workspace layout: arrival counters first, one uint32 per column tile at a
+// fixed place (tile t at byte 4t) for every shape, then the partial carries.
+// Every call leaves its counters at zero and nothing else writes that region,
+// so a workspace zeroed once stays valid for calls of any shape.
+constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4;
+
+size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N) {
+  if (p.split_k <= 1) return 0;
+  const int64_t Npad = round_up(N, Q8_TILE_COLS);
+  return kCounterBytes + (size_t)round_up((int64_t)p.split_k * m * Npad * 4, 256);
+}
+
+// ---- library-owned workspaces, per (device, stream) ---------------------------
+
+struct Workspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+std::vector<std::pair<int, void *>> g_ws_retired;  // freed by q8_release_workspaces
+
+int library_workspace(hipStream_t stream, size_t need, void **out) {
+  *out = nullptr;
+  if (need == 0) return Q8_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace &w = g_ws[{dev, stream}];
+  if (w.bytes < need) {
+    // Work already queued on the stream may still use the old buffer: retire
+    // it rather than free it.
+    if (w.ptr) g_ws_retired.push_back({dev, w.ptr});
+    w.ptr = nullptr;
+    w.bytes = 0;
+    const size_t bytes = (size_t)round_up((int64_t)need, 1 << 20);
+    void *p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    // Zero once: the arrival counters start at zero and every call leaves
+    // them at zero.
+    e = hipMemsetAsync(p, 0, bytes, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "hipMemsetAsync(workspace)");
+    }
+    w.ptr = p;
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return Q8_OK;
+}
+
+int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+             float *y, int32_t *dots, int64_t m, int64_t K, int64_t N,
+             int act_fmt, const q8_plan &plan, hipStream_t stream,
+             void *workspace, size_t ws_bytes) {
+  const bool write_dots = dots != nullptr;
+  int st = check_plan(&plan, m, K, act_fmt, write_dots);
+  if (st) return st;
+  const int64_t Npad = round_up(N, Q8_TILE_COLS);
+  q8::GemvArgs a{};
+  a.x = x;
+  a.wq = W_q8;
+  a.wsc = W_q8_scale;
+  a.y = y;
+  a.dots = dots;
+  a.m = (int)m;
+  a.K = (int)K;
+  a.NB = (int)(K / Q8_BLOCK);
+  a.Npad = (int)Npad;
+  a.T = (int)(Npad / Q8_TILE_COLS);
+  a.split_k = plan.split_k;
+  a.act_scale_off = (unsigned)act_scales_offset(m, K);
+  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "activation too large");
+  if (!write_dots && plan.split_k > 1) {
+    const size_t need = plan_ws_bytes(plan, m, N);
+    if (!workspace || ws_bytes < need)
+      return fail(Q8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? ws_bytes : (size_t)0, need);
+    a.counters = static_cast<unsigned *>(workspace);
+    a.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+  }
+  (void)hipGetLastError();  // clear a stale error so the launch's own is seen
+  hipError_t e = q8::launch_gemv(plan.kernel, plan.rows, act_fmt, write_dots,
+                                 plan.waves, a, stream);
+  if (e != hipSuccess) return hip_fail(e, "gemv launch");
+  return ok();
+}
+
+int check_gemv_args(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                    const void *out, const char *out_name, int64_t m, int64_t K,
+                    int64_t N, int act_fmt, bool need_scales) {
+  int st;
+  if ((st = check_m(m))) return st;
+  if ((st = check_kn(K, N))) return st;
+  if ((st = check_act(act_fmt))) return st;
+  if ((st = check_ptr(x, "x"))) return st;
+  if ((st = check_ptr(W_q8, "W_q8"))) return st;
+  if (need_scales && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
+  if ((st = check_ptr(out, out_name))) return st;
+  return Q8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t q8_padded_cols(int64_t N) {
+  if (N < 1) return -1;
+  return round_up(N, Q8_TILE_COLS);
+}
+
+size_t q8_packed_values_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || K % Q8_BLOCK || N < 1) return 0;
+  return (size_t)K * (size_t)round_up(N, Q8_TILE_COLS);
+}
+
+size_t q8_packed_scales_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || K % Q8_BLOCK || N < 1) return 0;
+  return (size_t)(K / Q8_BLOCK) * (size_t)round_up(N, Q8_TILE_COLS) * 4;
+}
+
+size_t q8_act_scales_offset(int64_t m, int64_t K) {
+  if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
+  return act_scales_offset(m, K);
+}
+
+size_t q8_act_bytes(int64_t m, int64_t K) {
+  if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
+  return act_scales_offset(m, K) + (size_t)(m * (K / Q8_BLOCK)) * 4;
+}
+
+size_t q8_gemv_workspace_bytes(int64_t m, int64_t K, int64_t N, int act_fmt) {
+  if (check_m(m) || check_kn(K, N) || check_act(act_fmt)) return 0;
+  return plan_ws_bytes(default_plan(m, K, N, act_fmt), m, N);
+}
+
+int q8_repack(const int8_t *q_kn, const float *s_kn, int64_t K, int64_t N,
+              int8_t *W_q8, float *W_q8_scale, hipStream_t stream) {
+  int st;
+  if ((st = check_kn(K, N))) return st;
+  if ((st = check_ptr(q_kn, "q_kn")) || (st = check_ptr(s_kn, "s_kn")) ||
+      (st = check_ptr(W_q8, "W_q8")) || (st = check_ptr(W_q8_scale, "W_q8_scale")))
+    return st;
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_repack(q_kn, s_kn, (int)K, (int)N, W_q8, W_q8_scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  return ok();
+}
+
+int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K, int64_t N,
+              int8_t *q_kn, float *s_kn, hipStream_t stream) {
+  int st;
+  if ((st = check_kn(K, N))) return st;
+  if ((st = check_ptr(W_q8, "W_q8")) || (st = check_ptr(W_q8_scale, "W_q8_scale")) ||
+      (st = check_ptr(q_kn, "q_kn")) || (st = check_ptr(s_kn, "s_kn")))
+    return st;
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_unpack(W_q8, W_q8_scale, (int)K, (int)N, q_kn, s_kn, stream);
+  if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  return ok();
+}
+
+int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
+                    hipStream_t stream) {
+  int st;
+  if ((st = check_m(m))) return st;
+  if ((st = check_kn(K, 1))) return st;
+  if ((st = check_ptr(x_bf16, "x_bf16")) || (st = check_ptr(x_q8, "x_q8"))) return st;
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_quantize_act(x_bf16, x_q8, (int)m, (int)K,
+                                         (unsigned)act_scales_offset(m, K), stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_act launch");
+  return ok();
+}
+
+int q8_gemv_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, q8_plan *plan) {
+  int st;
+  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  *plan = default_plan(m, K, N, act_fmt);
+  return ok();
+}
+
+size_t q8_plan_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K, int64_t N) {
+  if (!plan || check_m(m) || check_kn(K, N)) return 0;
+  return plan_ws_bytes(*plan, m, N);
+}
+
+int q8_gemv_planned(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                    float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+                    const q8_plan *plan, hipStream_t stream, void *workspace,
+                    size_t ws_bytes) {
+  int st = check_gemv_args(x, W_q8, W_q8_scale, y, "y", m, K, N, act_fmt, true);
+  if (st) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  if (workspace && (st = check_ptr(workspace, "workspace"))) return st;
+  return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, *plan,
+                  stream, workspace, ws_bytes);
+}
+
+int q8_gemv_ws(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+               float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+               hipStream_t stream, void *workspace, size_t ws_bytes) {
+  int st = check_gemv_args(x, W_q8, W_q8_scale, y, "y", m, K, N, act_fmt, true);
+  if (st) return st;
+  if (workspace && (st = check_ptr(workspace, "workspace"))) return st;
+  const q8_plan plan = default_plan(m, K, N, act_fmt);
+  return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, plan,
+                  stream, workspace, ws_bytes);
+}
+
+int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+            float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+            hipStream_t stream) {
+  int st = check_gemv_args(x, W_q8, W_q8_scale, y, "y", m, K, N, act_fmt, true);
+  if (st) return st;
+  const q8_plan plan = default_plan(m, K, N, act_fmt);
+  const size_t need = plan_ws_bytes(plan, m, N);
+  void *ws = nullptr;
+  if ((st = library_workspace(stream, need, &ws))) return st;
+  return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, plan,
+                  stream, ws, need);
+}
+
+int q8_gemv_block_dots_planned(const void *x_q8, const int8_t *W_q8,
+                               int32_t *dots, int64_t m, int64_t K, int64_t N,
+                               const q8_plan *plan, hipStream_t stream) {
+  int st = check_gemv_args(x_q8, W_q8, nullptr, dots, "dots", m, K, N,
+                           Q8_ACT_Q8_0, false);
+  if (st) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  return run_gemv(x_q8, W_q8, nullptr, nullptr, dots, m, K, N, Q8_ACT_Q8_0,
+                  *plan, stream, nullptr, 0);
+}
+
+int q8_gemv_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
+                       int64_t m, int64_t K, int64_t N, hipStream_t stream) {
+  int st = check_gemv_args(x_q8, W_q8, nullptr, dots, "dots", m, K, N,
+                           Q8_ACT_Q8_0, false);
+  if (st) return st;
+  const q8_plan plan = default_plan(m, K, N, Q8_ACT_Q8_0);
+  return run_gemv(x_q8, W_q8, nullptr, nullptr, dots, m, K, N, Q8_ACT_Q8_0,
+                  plan, stream, nullptr, 0);
+}
+
+const char *q8_status_string(int status) {
+  switch (status) {
+    case Q8_OK: return "Q8_OK";
+    case Q8_ERR_SHAPE: return "Q8_ERR_SHAPE";
+    case Q8_ERR_ACT_FMT: return "Q8_ERR_ACT_FMT";
+    case Q8_ERR_NULL: return "Q8_ERR_NULL";
+    case Q8_ERR_ALIGN: return "Q8_ERR_ALIGN";
+    case Q8_ERR_WORKSPACE: return "Q8_ERR_WORKSPACE";
+    case Q8_ERR_HIP: return "Q8_ERR_HIP";
+    case Q8_ERR_PLAN: return "Q8_ERR_PLAN";
+    default: return "Q8_ERR_UNKNOWN";
+  }
+}
+
+const char *q8_last_error(void) { return g_last_error.c_str(); }
+
+int q8_release_workspaces(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (g_ws.empty() && g_ws_retired.empty()) return ok();
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  auto release = [&](int dev, void *p) {
+    (void)hipSetDevice(dev);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(p);
+  };
+  for (auto &kv : g_ws)
+    if (kv.second.ptr) release(kv.first.first, kv.second.ptr);
+  for (auto &r : g_ws_retired) release(r.first, r.second);
+  g_ws.clear();
+  g_ws_retired.clear();
+  (void)hipSetDevice(cur);
+  return ok();
+}
+
+int q8_layout_version(void) { return q8::kLayoutVersion; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// q8_internal.h -- declarations shared by the host API (q8_api.cpp) and the
+// gfx950 kernels (q8_kernels.hip).  Not installed; the public ABI is
+// include/q8gemv.h.
+//
+// Packed weight layout (version 1), private to this library:
+//   N is padded to N_pad = 64*T columns; the weight is T column tiles of 64.
+//   K is NB = K/32 Q8_0 blocks.  Tile t, block b is one contiguous 2048-byte
+//   chunk at byte (t*NB + b)*2048, itself two 1024-byte halves h (k 0..15 and
+//   k 16..31 of the block); half h holds, for each of the 64 columns c, the
+//   column's 16 values at byte h*1024 + c*16 + (k mod 16).  A tile's chunks are
+//   consecutive, so one tile over all K is one contiguous run of K*64 bytes.
+//   Scales: fp32 at index (t*NB + b)*64 + c -- a 256-byte row per chunk.
+//   Pad columns carry zero values and zero scales.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace q8 {
+
+constexpr int kBlock = 32;          // K rows of a Q8_0 block
+constexpr int kTile = 64;           // columns of a packed tile
+constexpr int kChunkBytes = 2048;   // one tile x one block of values
+constexpr int kHalfBytes = 1024;    // 16 k-values of each of the 64 columns
+constexpr int kLayoutVersion = 1;
+
+enum Act { kActBf16 = 0, kActQ8 = 1 };
+
+// Everything a product launch needs; pointers are device pointers.
+struct GemvArgs {
+  const void *x;          // bf16 m x K, or the quantized activation buffer
+  const int8_t *wq;       // packed values
+  const float *wsc;       // packed scales (unused when writing dots)
+  float *y;               // m x Npad
+  float *partial;         // split_k x m x Npad (split_k > 1)
+  unsigned *counters;     // T arrival counters (split_k > 1), zero between calls
+  int32_t *dots;          // m x NB x Npad (dot mode)
+  int m, K, NB, Npad, T;
+  int split_k;
+  unsigned act_scale_off; // byte offset of the activation scales (Q8 mode)
+};
+
+// Launchers (q8_kernels.hip).  Return the launch's hipError_t.
+hipError_t launch_repack(const int8_t *q_kn, const float *s_kn, int K, int N,
+                         int8_t *wq, float *wsc, hipStream_t stream);
+hipError_t launch_unpack(const int8_t *wq, const float *wsc, int K, int N,
+                         int8_t *q_kn, float *s_kn, hipStream_t stream);
+hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
+                               unsigned scale_off, hipStream_t stream);
+// kernel: 0 VALU, 1 MFMA; rows: 1,2,4,8,16,32; act: Act; waves: 4 or 8.
+// Returns hipErrorInvalidValue for a combination that is not instantiated.
+hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots,
+                       int waves, const GemvArgs &a, hipStream_t stream);
+bool gemv_instantiated(int kernel, int rows, int act, bool write_dots,
+                       int waves);
+
+}  // namespace q8

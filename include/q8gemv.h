@@ -1,0 +1,212 @@
+/*
+ * q8gemv.h -- C ABI of the MI355X (gfx950) Q8_0 weight product.
+ *
+ * The operation (docs.logicaffeine.com, logicaffeine_compile/spatial/passes/
+ * from_q8.rs, module doc): a Q8_0 weight keeps each column's rows in blocks
+ * of 32 with one fp32 scale d and 32 int8 values q per block, w = q*d; it is
+ * two tensors, the values (K x N int8) and the scales (K/32 x N fp32).  For an
+ * m-row activation x (1 <= m <= 32, fn q8_gemv_applies)
+ *
+ *     y[r,n] = sum_b s[b,n] * sum_i x[r,32b+i] * q[32b+i,n]
+ *
+ * carried in fp32, the weight streamed once for all m rows.  The activation
+ * is bf16, or its quantized form (int8 values and one fp32 scale per 32
+ * values: codegen_cuda/lane/plan.rs, const QBLOCK and struct Buffer).
+ *
+ * Conventions for every call below:
+ *   - Pointers are DEVICE pointers (memory of the current HIP device) unless
+ *     stated otherwise.  The caller allocates and owns every buffer; the
+ *     library keeps no pointer past the call's stream work.
+ *   - Work is enqueued on `stream` (0 = the null stream) and is asynchronous:
+ *     a return of Q8_OK means "validated and launched"; device faults surface
+ *     at the caller's synchronize.
+ *   - Every precondition is checked on the host before any launch.  Failures
+ *     return a q8_status; q8_last_error() then gives a thread-local message
+ *     naming the argument, its value and the bound.  No exception crosses the
+ *     ABI.
+ *   - Inputs are read-only.  Outputs must not overlap inputs.
+ *   - Device pointers must be 16-byte aligned (Q8_ERR_ALIGN otherwise).
+ *
+ * Layouts:
+ *   canonical values  q_kn : K x N int8, row-major (row k, stride N)
+ *   canonical scales  s_kn : K/32 x N fp32, row-major
+ *   packed values     W_q8 : library-private layout written by q8_repack,
+ *                            q8_packed_values_bytes(K, N) bytes
+ *   packed scales     W_q8_scale : q8_packed_scales_bytes(K, N) bytes
+ *   bf16 activation   x    : m x K bf16 (uint16 bit patterns), row-major
+ *   quantized act.    x_q8 : one buffer of q8_act_bytes(m, K) bytes: int8
+ *                            values m x K row-major at offset 0, fp32 scales
+ *                            m x K/32 row-major at q8_act_scales_offset(m, K)
+ *   output            y    : m x N_pad fp32 row-major, N_pad = q8_padded_cols(N);
+ *                            columns N..N_pad-1 are written and are exactly +0
+ *                            (pad values and scales are zero: from_q8.rs,
+ *                            fn q8_gemv_applies)
+ */
+#ifndef Q8GEMV_H
+#define Q8GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Activation formats. */
+typedef enum {
+  Q8_ACT_BF16 = 0, /* x is m x K bf16 */
+  Q8_ACT_Q8_0 = 1  /* x is the q8_quantize_act buffer */
+} q8_act_fmt;
+
+/* Status codes (errors are values, as the pages' lowering returns its
+ * rejections: from_q8.rs SpatialReject, plan.rs LaneError). */
+typedef enum {
+  Q8_OK = 0,
+  Q8_ERR_SHAPE = 1,     /* m, K or N out of range; K not whole 32-blocks      */
+  Q8_ERR_ACT_FMT = 2,   /* unknown act_fmt                                    */
+  Q8_ERR_NULL = 3,      /* a required pointer is NULL                         */
+  Q8_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned            */
+  Q8_ERR_WORKSPACE = 5, /* workspace missing or smaller than required         */
+  Q8_ERR_HIP = 6,       /* a HIP call failed (message from hipGetErrorString) */
+  Q8_ERR_PLAN = 7       /* an explicit plan is not valid for the shape        */
+} q8_status;
+
+#define Q8_BLOCK 32     /* K rows per Q8_0 block                              */
+#define Q8_MAX_ROWS 32  /* most activation rows per call (fn q8_gemv_applies) */
+#define Q8_TILE_COLS 64 /* column tile: N is padded to a multiple of this     */
+
+/* ---- sizes (host functions, no device work) ---------------------------- */
+
+/* ceil(N/64)*64, or -1 when N < 1. */
+int64_t q8_padded_cols(int64_t N);
+/* K * N_pad: bytes of the packed values. 0 on a bad shape. */
+size_t q8_packed_values_bytes(int64_t K, int64_t N);
+/* 4 * (K/32) * N_pad: bytes of the packed scales. 0 on a bad shape. */
+size_t q8_packed_scales_bytes(int64_t K, int64_t N);
+/* Byte offset of the fp32 scales inside a quantized activation buffer:
+ * m*K rounded up to 256. */
+size_t q8_act_scales_offset(int64_t m, int64_t K);
+/* Total bytes of a quantized activation buffer. 0 on a bad shape. */
+size_t q8_act_bytes(int64_t m, int64_t K);
+/* Bytes of the split-K workspace q8_gemv_ws needs for this shape (may be 0). */
+size_t q8_gemv_workspace_bytes(int64_t m, int64_t K, int64_t N, int act_fmt);
+
+/* ---- weight layout ------------------------------------------------------ */
+
+/*
+ * q8_repack: canonical -> packed (from_q8.rs, enum Q8Part: what the host
+ * repacks from the checkpoint's blocks into the two stored tensors).
+ * Reads q_kn (K x N int8) and s_kn (K/32 x N fp32); writes W_q8 and
+ * W_q8_scale in the packed layout over N_pad columns, the pad columns' values
+ * and scales zero.  Requires K > 0, K % 32 == 0, N >= 1.
+ */
+int q8_repack(const int8_t *q_kn, const float *s_kn, int64_t K, int64_t N,
+              int8_t *W_q8, float *W_q8_scale, hipStream_t stream);
+
+/*
+ * q8_unpack: packed -> canonical, the inverse of q8_repack on the N real
+ * columns.  Writes q_kn (K x N) and s_kn (K/32 x N).
+ */
+int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K,
+              int64_t N, int8_t *q_kn, float *s_kn, hipStream_t stream);
+
+/* ---- activation --------------------------------------------------------- */
+
+/*
+ * q8_quantize_act: bf16 activation -> its quantized form, per row and per
+ * 32-value block (plan.rs, const QBLOCK: "int8 values and a scale per 32").
+ * The pages do not give the formula; this library computes
+ *     amax = max|x|,  d = fp32(amax / 127)  (amax == 0: d = 0, xq = 0),
+ *     xq   = clamp(round_half_away_from_zero(fp32(x / d)), -127, 127)
+ * with correctly rounded divisions.  Requires 1 <= m <= 32, K > 0,
+ * K % 32 == 0.  x_q8 receives q8_act_bytes(m, K) bytes.
+ */
+int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
+                    hipStream_t stream);
+
+/* ---- the product ---------------------------------------------------------- */
+
+/*
+ * q8_gemv: y = x . W over the packed Q8_0 weight (from_q8.rs, module doc and
+ * fn q8_fold).  x per act_fmt; y is m x N_pad fp32.  Requires 1 <= m <= 32,
+ * K > 0, K % 32 == 0, N >= 1.  When the chosen plan splits K across
+ * workgroups it uses a workspace the library allocates on first need and
+ * keeps per (device, stream) until q8_release_workspaces(); that first call
+ * allocates, so it must not be inside a graph capture.  Calls on one stream
+ * are ordered; calls on different streams use different workspaces.
+ */
+int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+            float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+            hipStream_t stream);
+
+/*
+ * q8_gemv_ws: q8_gemv with the caller's workspace (device memory of at least
+ * q8_gemv_workspace_bytes(m, K, N, act_fmt) bytes, 16-byte aligned, or NULL
+ * when that size is 0).  Its first 1 MiB holds split-K arrival counters at
+ * fixed places (one per 64-column tile); they must be zero at the first use,
+ * and every call leaves them at zero again, so a workspace zeroed once serves
+ * calls of any shape.  Calls that share a workspace must be ordered (one
+ * stream).  Q8_ERR_WORKSPACE when too small.
+ */
+int q8_gemv_ws(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+               float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+               hipStream_t stream, void *workspace, size_t ws_bytes);
+
+/*
+ * q8_gemv_block_dots: test hook of the int8 path.  Runs the same device code
+ * as q8_gemv with Q8_ACT_Q8_0 but writes the exact per-block int32 dots
+ *     dots[r, b, n] = sum_i xq[r,32b+i] * q[32b+i,n]
+ * as an m x K/32 x N_pad int32 array (pad columns 0) instead of scaling them.
+ */
+int q8_gemv_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
+                       int64_t m, int64_t K, int64_t N, hipStream_t stream);
+
+/* ---- plans: what q8_gemv launches, and an explicit choice for tuning ----- */
+
+typedef enum {
+  Q8_KERNEL_VALU = 0, /* lane per column, activation broadcast from SGPRs    */
+  Q8_KERNEL_MFMA = 1  /* 16x16x32 matrix-core block dots, activation in LDS  */
+} q8_kernel;
+
+typedef struct q8_plan {
+  int32_t kernel;  /* q8_kernel                                                */
+  int32_t rows;    /* row count the kernel is built for (1,2,4,8,16,32) >= m   */
+  int32_t split_k; /* K splits across workgroups, 1..K/32                      */
+  int32_t waves;   /* waves (64 lanes) per workgroup: 4 or 8                   */
+} q8_plan;
+
+/* The plan q8_gemv would launch for this shape on the current device. */
+int q8_gemv_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
+                         q8_plan *plan /* host pointer */);
+/* Workspace bytes an explicit plan needs. */
+size_t q8_plan_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K,
+                               int64_t N);
+/* q8_gemv_ws with an explicit plan (Q8_ERR_PLAN when it does not fit). */
+int q8_gemv_planned(const void *x, const int8_t *W_q8,
+                    const float *W_q8_scale, float *y, int64_t m, int64_t K,
+                    int64_t N, int act_fmt, const q8_plan *plan,
+                    hipStream_t stream, void *workspace, size_t ws_bytes);
+/* q8_gemv_block_dots with an explicit plan. */
+int q8_gemv_block_dots_planned(const void *x_q8, const int8_t *W_q8,
+                               int32_t *dots, int64_t m, int64_t K, int64_t N,
+                               const q8_plan *plan, hipStream_t stream);
+
+/* ---- errors and resources ------------------------------------------------ */
+
+/* Static name of a status code. */
+const char *q8_status_string(int status);
+/* Thread-local message of this thread's last failing call ("" if none). */
+const char *q8_last_error(void);
+/* Frees the workspaces q8_gemv allocated (synchronizes the device first). */
+int q8_release_workspaces(void);
+/* Version of the packed layout: weights packed by another version are
+ * rejected by no check -- repack them. */
+int q8_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8GEMV_H */

@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 weight product on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch: for bf16 activations one
+q8_gemv call; for Q8_0 activations q8_quantize_act followed by q8_gemv.  The
+weight is repacked once before timing (it is a load-time step).  Inputs are
+seeded synthetic tensors of the workload's shape, resident in HBM.  Every
+step reads a different copy of the weight, enough copies to span twice the
+256 MB last-level cache, so the weight streams from HBM rather than from the
+cache.
+
+Prints ONE JSON line on stdout.  `value` is the whole-job rate in GB/s of
+algorithmic bytes (weight values + fp32 scales + activation + output) over
+the timed steps; `roofline` prices the product kernel's own average duration
+(HIP events around each launch, on the launch stream) against 8 TB/s;
+`cpu_baseline` times the CPU oracle on the same workload on this host;
+`by_rows` gives the same measurement at m = 16 and m = 32.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20      # MI355X Infinity Cache
+METRIC = "Q8_0 GEMV effective HBM GB/s (% of peak) and weights/s at m=1,16,32"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the product must move once: weight values and scales over the
+    padded columns, the activation as the kernel reads it, and the output."""
+    Npad = (w.N + 63) // 64 * 64
+    values = w.K * Npad
+    scales = 4 * (w.K // 32) * Npad
+    if w.act == "bf16":
+        x = 2 * w.m * w.K
+    else:
+        x = w.m * w.K + 4 * w.m * (w.K // 32)
+    y = 4 * w.m * Npad
+    return {"values": values, "scales": scales, "x": x, "y": y,
+            "total": values + scales + x + y}
+
+
+def csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "block_quantized_weight_02_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("csrc_hash") != csrc_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Setup:
+    """Device buffers of one workload: rotating packed weight copies, the
+    activation (bf16, and its quantized buffer), the output."""
+
+    def __init__(self, w, rotate=True):
+        import torch
+        import block_quantized_weight_02_amd as q8
+        from block_quantized_weight_02_amd import inputs
+        self.w = w
+        self.q8 = q8
+        dev = "cuda:0"
+        x, q, s = inputs.generate(w)
+        self.host = (x, q, s)
+        K, N, m = w.K, w.N, w.m
+        vb, sb = q8.q8_packed_values_bytes(K, N), q8.q8_packed_scales_bytes(K, N)
+        self.copies = max(2, math.ceil(2 * MALL_BYTES / (vb + sb))) if rotate else 1
+        qd = torch.from_numpy(q).to(dev)
+        sd = torch.from_numpy(s).to(dev)
+        self.W = []
+        for _ in range(self.copies):
+            Wq = torch.empty(vb, dtype=torch.uint8, device=dev)
+            Ws = torch.empty(sb // 4, dtype=torch.float32, device=dev)
+            q8.q8_repack(qd, sd, K, N, Wq, Ws)
+            self.W.append((Wq, Ws))
+        del qd, sd
+        self.x = torch.from_numpy(x.view(np.int16)).to(dev)
+        self.xq = torch.empty(max(16, q8.q8_act_bytes(m, K)), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((m, q8.q8_padded_cols(N)), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        # pre-marshalled raw arguments: the timed loop is one ctypes call per launch
+        lib = q8.lib()
+        self._gemv = lib.q8_gemv
+        self._quant = lib.q8_quantize_act
+        sp = self.stream.cuda_stream
+        act = q8.Q8_ACT_BF16 if w.act == "bf16" else q8.Q8_ACT_Q8_0
+        xin = self.x.data_ptr() if w.act == "bf16" else self.xq.data_ptr()
+        self._gemv_args = [(xin, Wq.data_ptr(), Ws.data_ptr(), self.y.data_ptr(), m, K, N, act, sp)
+                           for (Wq, Ws) in self.W]
+        self._quant_args = (self.x.data_ptr(), self.xq.data_ptr(), m, K, sp)
+        self.plan = q8.q8_gemv_default_plan(m, K, N, act)
+
+    def step(self, i):
+        if self.w.act != "bf16":
+            rc = self._quant(*self._quant_args)
+            if rc:
+                raise RuntimeError(self.q8.q8_last_error())
+        rc = self._gemv(*self._gemv_args[i % self.copies])
+        if rc:
+            raise RuntimeError(self.q8.q8_last_error())
+
+    def gemv_only(self, i):
+        rc = self._gemv(*self._gemv_args[i % self.copies])
+        if rc:
+            raise RuntimeError(self.q8.q8_last_error())
+
+
+def time_loop(fn, steps):
+    """Milliseconds per step of `steps` back-to-back steps on the stream."""
+    import torch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_each(fn, steps):
+    """Per-launch durations (ms) from an event pair around every launch."""
+    import torch
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def measure(w, steps, warmup, rotate=True):
+    import torch
+    st = Setup(w, rotate=rotate)
+    b = algorithmic_bytes(w)
+    log(f"[bench] {w.name}: m={w.m} K={w.K} N={w.N} act={w.act} copies={st.copies} "
+        f"plan={st.plan} bytes/step={b['total']}")
+    for i in range(warmup):
+        st.step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_loop(st.step, steps)
+    wall = time.perf_counter() - t0
+    each = time_each(st.gemv_only, steps)
+    log(f"[bench] {w.name}: {ms * 1e3:.2f} us/step (loop), gemv kernel mean "
+        f"{each.mean() * 1e3:.2f} us median {np.median(each) * 1e3:.2f} us")
+    step_bytes = b["total"]
+    weights = w.K * w.N
+    res = {
+        "workload": w.name, "m": w.m, "K": w.K, "N": w.N, "act": w.act,
+        "ms_per_step": ms, "us_per_step": ms * 1e3,
+        "gbs": step_bytes / (ms * 1e-3) / 1e9,
+        "weights_per_s": weights / (ms * 1e-3),
+        "macs_per_s": w.m * weights / (ms * 1e-3),
+        "kernel_us_mean": float(each.mean() * 1e3),
+        "kernel_us_median": float(np.median(each) * 1e3),
+        "kernel_us_p10": float(np.percentile(each, 10) * 1e3),
+        "kernel_us_p90": float(np.percentile(each, 90) * 1e3),
+        "bytes": b, "copies": st.copies, "wall_s": wall,
+        "plan": {"kernel": st.plan.kernel, "rows": st.plan.rows,
+                 "split_k": st.plan.split_k, "waves": st.plan.waves},
+    }
+    gemv_bytes = step_bytes if w.act == "bf16" else step_bytes  # quantized x is read by the gemv
+    res["kernel_gbs"] = gemv_bytes / (res["kernel_us_mean"] * 1e-6) / 1e9
+    res["pct_hbm_peak"] = 100.0 * res["gbs"] / HBM_PEAK_GBS
+    res["kernel_pct_hbm_peak"] = 100.0 * res["kernel_gbs"] / HBM_PEAK_GBS
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The CPU oracle (as it stands) on this host, on the same workload."""
+    import oracle
+    from block_quantized_weight_02_amd import inputs
+    x, q, s = inputs.generate(w)
+    if w.act == "bf16":
+        run = lambda: oracle.gemv_bf16(x, q, s)  # noqa: E731
+    else:
+        def run():
+            xq, dx = oracle.quantize_act(x)
+            return oracle.gemv_q8(xq, dx, q, s)
+    run()  # warm (page in)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 200:
+            break
+    per = el / reps
+    b = algorithmic_bytes(w)["total"]
+    return {"value": b / per / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{reps} full {w.name} products (m={w.m} K={w.K} N={w.N}), "
+                      f"{per * 1e3:.1f} ms each, fp64 C oracle, OpenMP",
+            "ms_per_step": per * 1e3, "weights_per_s": w.K * w.N / per}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default=None, help="headline workload name (default: the m=1 decode shape)")
+    ap.add_argument("--no-rows", action="store_true", help="skip the m=16 and m=32 rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the product shards by columns across GPUs with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_quantized_weight_02_amd import inputs
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import block_quantized_weight_02_amd as q8
+    q8.lib()  # fails loudly when the HIP library is not built
+
+    name = args.workload or inputs.HEADLINE
+    w = inputs.WORKLOADS[name]
+    head = measure(w, args.steps, args.warmup, rotate=not args.no_rotate)
+
+    by_rows = {}
+    if not args.no_rows:
+        for other in ("batch16_k4096_n14336", "q8act_m32_k5120_n32000"):
+            if other == name:
+                continue
+            r = measure(inputs.WORKLOADS[other], max(200, args.steps // 4), max(20, args.warmup // 4),
+                        rotate=not args.no_rotate)
+            by_rows[f"m{inputs.WORKLOADS[other].m}"] = {
+                k: r[k] for k in ("workload", "us_per_step", "gbs", "pct_hbm_peak", "weights_per_s",
+                                  "macs_per_s", "kernel_us_mean", "kernel_gbs", "kernel_pct_hbm_peak", "plan")}
+
+    traffic = traffic_from_profile(w.name)
+    achieved = head["kernel_gbs"]
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "kernel": "gemv_valu_kernel", "kernel_us_mean": head["kernel_us_mean"],
+            "bytes_per_launch": head["bytes"]["total"]}
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(w)
+
+    out = {
+        "metric": METRIC,
+        "value": head["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": w.m, "K": w.K, "N": w.N, "act": w.act,
+                   "weight": "q8_0: int8 values + fp32 scale per 32 rows",
+                   "weight_copies": head["copies"], "plan": head["plan"],
+                   "parallelism": "single GPU"},
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "weights_per_s": head["weights_per_s"],
+        "macs_per_s": head["macs_per_s"],
+        "kernel_us": {k: head[k] for k in ("kernel_us_mean", "kernel_us_median", "kernel_us_p10", "kernel_us_p90")},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "by_rows": by_rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,20 +94,28 @@ size_t act_scales_offset(int64_t m, int64_t K) {
 
 // ---- device facts -----------------------------------------------------------
 
-int device_cus() {
+struct DeviceFacts {
+  int cus = 256;
+  int lds_per_block = 64 * 1024;
+};
+
+DeviceFacts device_facts() {
+  DeviceFacts f;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipGetDevice(&dev) != hipSuccess) return f;
   static std::mutex mu;
-  static std::map<int, int> cache;
+  static std::map<int, DeviceFacts> cache;
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(dev);
   if (it != cache.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  cache[dev] = cus;
-  return cus;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+    f.cus = v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+      v > 0)
+    f.lds_per_block = v;
+  cache[dev] = f;
+  return f;
 }
 
 // ---- plans --------------------------------------------------------------------
@@ -118,24 +126,41 @@ int rows_for(int64_t m) {
   return r;
 }
 
-// The default launch: the VALU kernel at the smallest row count >= m; K split
-// across workgroups until the grid holds about four workgroups per CU, while
-// each split keeps at least 16 blocks (4 waves x 4 blocks in flight).
+// The default launch.
+//  * VALU kernel (lane per column) while the rows are few enough that the
+//    vector ALU keeps up with HBM: bf16 up to 4 rows, int8 up to 8 rows;
+//    MFMA kernel above.
+//  * VALU: 16 waves per workgroup; K split across workgroups only when the
+//    column tiles alone leave CUs idle (splits = CUs / tiles, each split at
+//    least 8 blocks).
+//  * MFMA: the fewest K splits whose staged activation fits the LDS budget,
+//    then more while the tiles leave CUs idle.
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
-  (void)act_fmt;
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
-  const int64_t cus = device_cus();
-  const int64_t want = 4 * cus;
-  int64_t S = (want + T - 1) / T;
-  const int64_t smax = NB / 16 > 0 ? NB / 16 : 1;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
+  const DeviceFacts dev = device_facts();
+  const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
   q8_plan p;
-  p.kernel = Q8_KERNEL_VALU;
-  p.rows = rows_for(m);
+  const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 4 : 8;
+  if (m <= valu_rows) {
+    p.kernel = Q8_KERNEL_VALU;
+    p.rows = rows_for(m);
+    p.waves = p.rows <= 4 ? 16 : 8;
+    int64_t S = dev.cus / T;
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    p.split_k = (int32_t)S;
+    return p;
+  }
+  p.kernel = Q8_KERNEL_MFMA;
+  p.rows = m <= 16 ? 16 : 32;
+  p.waves = 8;
+  int64_t S = dev.cus / T;
+  if (S < 1) S = 1;
+  const size_t budget = (size_t)dev.lds_per_block;
+  while (S < NB && q8::mfma_lds_bytes(p.rows, act_fmt, p.waves, (int)NB, (int)S) > budget) ++S;
+  if (S > NB) S = NB;
   p.split_k = (int32_t)S;
-  p.waves = 4;
   return p;
 }
 
@@ -151,6 +176,13 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
   if (!q8::gemv_instantiated(p->kernel, p->rows, act, dots, p->waves))
     return fail(Q8_ERR_PLAN, "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d",
                 p->kernel, p->rows, act, (int)dots, p->waves);
+  if (p->kernel == Q8_KERNEL_MFMA) {
+    const size_t need = q8::mfma_lds_bytes(p->rows, act, p->waves, (int)NB, p->split_k);
+    const size_t have = (size_t)device_facts().lds_per_block;
+    if (need > have)
+      return fail(Q8_ERR_PLAN, "plan needs %zu bytes of LDS per workgroup, the device has %zu: "
+                  "raise split_k", need, have);
+  }
   return Q8_OK;
 }
 

@@ -9,7 +9,9 @@
 //   k 16..31 of the block); half h holds, for each of the 64 columns c, the
 //   column's 16 values at byte h*1024 + c*16 + (k mod 16).  A tile's chunks are
 //   consecutive, so one tile over all K is one contiguous run of K*64 bytes.
-//   Scales: fp32 at index (t*NB + b)*64 + c -- a 256-byte row per chunk.
+//   Scales: one 64-float (256-byte) row per chunk at (t*NB + b)*64; column
+//   c = i + 16g (i < 16, g < 4) sits at position 4i + g of the row, so the
+//   four columns a 16-column MFMA lane group touches are one 16-byte load.
 //   Pad columns carry zero values and zero scales.
 #pragma once
 
@@ -24,7 +26,7 @@ constexpr int kBlock = 32;          // K rows of a Q8_0 block
 constexpr int kTile = 64;           // columns of a packed tile
 constexpr int kChunkBytes = 2048;   // one tile x one block of values
 constexpr int kHalfBytes = 1024;    // 16 k-values of each of the 64 columns
-constexpr int kLayoutVersion = 1;
+constexpr int kLayoutVersion = 2;
 
 enum Act { kActBf16 = 0, kActQ8 = 1 };
 
@@ -49,11 +51,13 @@ hipError_t launch_unpack(const int8_t *wq, const float *wsc, int K, int N,
                          int8_t *q_kn, float *s_kn, hipStream_t stream);
 hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
                                unsigned scale_off, hipStream_t stream);
-// kernel: 0 VALU, 1 MFMA; rows: 1,2,4,8,16,32; act: Act; waves: 4 or 8.
+// kernel: 0 VALU, 1 MFMA; rows: 1,2,4,8,16,32; act: Act; waves: 4, 8 or 16.
 // Returns hipErrorInvalidValue for a combination that is not instantiated.
 hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots,
                        int waves, const GemvArgs &a, hipStream_t stream);
 bool gemv_instantiated(int kernel, int rows, int act, bool write_dots,
                        int waves);
+// Dynamic LDS bytes an MFMA launch needs (activation staging or wave carries).
+size_t mfma_lds_bytes(int rows, int act, int waves, int NB, int split_k);
 
 }  // namespace q8

@@ -42,6 +42,27 @@ __device__ __forceinline__ float bf16_hi(uint32_t pair) {  // element 2p+1
   return __uint_as_float(pair & 0xffff0000u);
 }
 
+// Loads of the weight stream: non-temporal (the weight is read once per call
+// and must not displace the activation or the carries from the caches).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void *p) {
+  const u32x2_t v = __builtin_nontemporal_load(static_cast<const u32x2_t *>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float ld_stream4f(const float *p) {
+  return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ float4 ld_stream16f(const float4 *p) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // The four signed bytes of a dword as fp32 (exact); byte j is k = 4d + j.
 __device__ __forceinline__ void i8x4_to_f32(uint32_t v, float *f) {
   f[0] = (float)(int8_t)(v);
@@ -49,6 +70,12 @@ __device__ __forceinline__ void i8x4_to_f32(uint32_t v, float *f) {
   f[2] = (float)(int8_t)(v >> 16);
   f[3] = (float)((int32_t)v >> 24);
 }
+
+// Position of column c's scale inside a chunk's 64-float scale row: the four
+// columns c = i + 16g (g = 0..3) of one lane index i sit together, so an MFMA
+// lane reads its four column groups' scales as one 16-byte load and a VALU
+// lane (column c) one dword.
+__device__ __forceinline__ int scale_pos(int c) { return ((c & 15) << 2) | (c >> 4); }
 
 // ---------------------------------------------------------------------------
 // weight repack / unpack (from_q8.rs, enum Q8Part: the host repacks the
@@ -76,7 +103,7 @@ repack_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
       d[j >> 2] |= (uint32_t)(uint8_t)q[(size_t)(k0 + j) * N + n] << (8 * (j & 3));
   }
   *reinterpret_cast<uint4 *>(wq + run * 16) = make_uint4(d[0], d[1], d[2], d[3]);
-  if (h == 0) wsc[tb * kTile + c] = (n < N) ? s[(size_t)b * N + n] : 0.0f;
+  if (h == 0) wsc[tb * kTile + scale_pos(c)] = (n < N) ? s[(size_t)b * N + n] : 0.0f;
 }
 
 __global__ void __launch_bounds__(256)
@@ -98,7 +125,7 @@ unpack_kernel(const int8_t *__restrict__ wq, const float *__restrict__ wsc,
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     q[(size_t)(k0 + j) * N + n] = (int8_t)(d[j >> 2] >> (8 * (j & 3)));
-  if (h == 0) s[(size_t)b * N + n] = wsc[tb * kTile + c];
+  if (h == 0) s[(size_t)b * N + n] = wsc[tb * kTile + scale_pos(c)];
 }
 
 // ---------------------------------------------------------------------------
@@ -133,11 +160,201 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ xq,
 }
 
 // ---------------------------------------------------------------------------
-// the product, VALU form
+// the product: shared pieces
 // ---------------------------------------------------------------------------
 
-// Blocks a wave has in flight per step of its block loop.
-constexpr int kUnroll = 4;
+// The workgroup's row range of blocks [b_lo, b_hi) of split s of S.
+__device__ __forceinline__ void split_range(int NB, int s, int S, int &b_lo, int &b_hi) {
+  b_lo = (int)(((long long)NB * s) / S);
+  b_hi = (int)(((long long)NB * (s + 1)) / S);
+}
+
+// Epilogue of both kernels.  red[w][r][c] holds wave w's fp32 carry of row r,
+// tile column c (already written, __syncthreads() done by the caller).  Sums
+// the waves in order; with S == 1 stores y, otherwise publishes the partial
+// and the last workgroup of the tile sums the S partials in split order.
+//
+// The partial carries are written and read with system-scope relaxed atomic
+// stores and loads, which go through to memory and bypass the per-XCD L2s;
+// their completion is awaited (s_waitcnt 0) before the arrival count is
+// bumped.  So no workgroup needs a device-scope fence, whose L2 write-back and
+// invalidate would cost each workgroup microseconds.
+template <int MR, int W>
+__device__ __forceinline__ void finish_tile(const float *red, float *__restrict__ y,
+                                            float *__restrict__ partial,
+                                            unsigned *__restrict__ counters, int m, int Npad,
+                                            int t, int s, int S) {
+  const size_t col0 = (size_t)t * kTile;
+  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
+    const int r = idx >> 6, c = idx & 63;
+    if (r < m) {
+      float v = red[idx];
+#pragma unroll
+      for (int w = 1; w < W; ++w) v += red[w * MR * 64 + idx];
+      if (S == 1)
+        y[(size_t)r * Npad + col0 + c] = v;
+      else
+        __hip_atomic_store(&partial[((size_t)s * m + r) * Npad + col0 + c], v,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+  if (S == 1) return;
+  __shared__ int is_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = (__hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(S - 1))
+                  ? 1 : 0;
+  __syncthreads();
+  if (!is_last) return;
+  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
+    const int r = idx >> 6, c = idx & 63;
+    if (r < m) {
+      float v = __hip_atomic_load(&partial[(size_t)r * Npad + col0 + c], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+      for (int ss = 1; ss < S; ++ss)
+        v += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col0 + c],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      y[(size_t)r * Npad + col0 + c] = v;
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// ---------------------------------------------------------------------------
+// the product, VALU form: lane = column, activation in scalar registers
+// ---------------------------------------------------------------------------
+
+// Blocks a wave loads per stage; two stages are in flight (double buffer).
+#ifndef Q8_VALU_UNROLL
+#define Q8_VALU_UNROLL 1
+#endif
+constexpr int kUnroll = Q8_VALU_UNROLL;
+
+// Rows whose activation is prefetched with the stage (scalar registers): one
+// bf16 row is 16 dwords a block, an int8 row 8 dwords and its scale; more
+// rows than two would overflow the scalar registers.
+template <int MR, int ACT>
+struct ValuX {
+  static constexpr bool kPrefetch = MR <= 2;
+  static constexpr int kRows = kPrefetch ? MR : 1;
+  static constexpr int kWords = (ACT == kActBf16) ? 16 : 8;
+};
+
+template <int MR, int ACT, bool DOTS>
+struct ValuStage {
+  uint4 wa[kUnroll], wb[kUnroll];
+  float sc[kUnroll];
+  uint32_t x[kUnroll][ValuX<MR, ACT>::kRows][ValuX<MR, ACT>::kWords];
+  float dx[kUnroll][ValuX<MR, ACT>::kRows];
+};
+
+// Issue the loads of the stage's blocks b0 + u*W; a block past the range
+// reloads the range's last block (in bounds) and is not used.
+template <int MR, int ACT, bool DOTS, int W>
+__device__ __forceinline__ void valu_load(ValuStage<MR, ACT, DOTS> &st, const int8_t *wtile,
+                                          const float *stile, int b0, int b_hi,
+                                          const void *__restrict__ xv, int m, int K, int NB,
+                                          unsigned act_scale_off) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int b = min(b0 + u * W, b_hi - 1);
+    const int8_t *c = wtile + (size_t)b * kChunkBytes;
+    st.wa[u] = ld_stream16(c);
+    st.wb[u] = ld_stream16(c + kHalfBytes);
+    if constexpr (!DOTS) st.sc[u] = ld_stream4f(stile + (size_t)b * kTile);
+    if constexpr (ValuX<MR, ACT>::kPrefetch) {
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const int rr = min(r, m - 1);   // rows past m reload row m-1, unused
+        if constexpr (ACT == kActBf16) {
+          const uint32_t *xr = reinterpret_cast<const uint32_t *>(
+              static_cast<const uint16_t *>(xv) + (size_t)rr * K + (size_t)b * kBlock);
+#pragma unroll
+          for (int p = 0; p < 16; ++p) st.x[u][r][p] = xr[p];
+        } else {
+          const uint32_t *xr = reinterpret_cast<const uint32_t *>(
+              static_cast<const int8_t *>(xv) + (size_t)rr * K + (size_t)b * kBlock);
+#pragma unroll
+          for (int p = 0; p < 8; ++p) st.x[u][r][p] = xr[p];
+          if constexpr (!DOTS)
+            st.dx[u][r] = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
+                                                          act_scale_off)[(size_t)rr * NB + b];
+        }
+      }
+    }
+  }
+}
+
+template <int MR, int ACT, bool DOTS, int W>
+__device__ __forceinline__ void valu_compute(const ValuStage<MR, ACT, DOTS> &st, float *acc,
+                                             int b0, int b_hi, const void *__restrict__ xv,
+                                             int32_t *__restrict__ dots, int m, int K, int NB,
+                                             int Npad, int t, int lane,
+                                             unsigned act_scale_off) {
+  constexpr bool kPre = ValuX<MR, ACT>::kPrefetch;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int b = b0 + u * W;
+    if (b >= b_hi) break;
+    const uint32_t wd[8] = {st.wa[u].x, st.wa[u].y, st.wa[u].z, st.wa[u].w,
+                            st.wb[u].x, st.wb[u].y, st.wb[u].z, st.wb[u].w};
+    if constexpr (ACT == kActBf16) {
+      float wf[32];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) i8x4_to_f32(wd[d], wf + 4 * d);
+      const uint16_t *xb = static_cast<const uint16_t *>(xv);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        if (r < m) {
+          const uint32_t *xr =
+              reinterpret_cast<const uint32_t *>(xb + (size_t)r * K + (size_t)b * kBlock);
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            uint32_t lo, hi;
+            if constexpr (kPre) {
+              lo = st.x[u][r][p];
+              hi = st.x[u][r][p + 8];
+            } else {
+              lo = xr[p];
+              hi = xr[p + 8];
+            }
+            p0 = fmaf(bf16_lo(lo), wf[2 * p], p0);
+            p0 = fmaf(bf16_hi(lo), wf[2 * p + 1], p0);
+            p1 = fmaf(bf16_lo(hi), wf[16 + 2 * p], p1);
+            p1 = fmaf(bf16_hi(hi), wf[16 + 2 * p + 1], p1);
+          }
+          acc[r] = fmaf(st.sc[u], p0 + p1, acc[r]);
+        }
+      }
+    } else {
+      const int8_t *xq = static_cast<const int8_t *>(xv);
+      const float *dxp =
+          reinterpret_cast<const float *>(static_cast<const char *>(xv) + act_scale_off);
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        if (r < m) {
+          const int *xr = reinterpret_cast<const int *>(xq + (size_t)r * K + (size_t)b * kBlock);
+          int D = 0;
+#pragma unroll
+          for (int d = 0; d < 8; ++d)
+            D = __builtin_amdgcn_sdot4((int)wd[d], kPre ? (int)st.x[u][r][d] : xr[d], D, false);
+          if constexpr (DOTS) {
+            dots[((size_t)r * NB + b) * Npad + (size_t)t * kTile + lane] = D;
+          } else {
+            const float dxv = kPre ? st.dx[u][r] : dxp[(size_t)r * NB + b];
+            acc[r] = fmaf(dxv * st.sc[u], (float)D, acc[r]);
+          }
+        }
+      }
+    }
+  }
+}
 
 template <int MR, int ACT, bool DOTS, int W>
 __global__ void __launch_bounds__(64 * W)
@@ -150,165 +367,393 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x / S;
   const int s = blockIdx.x - t * S;
-  const int b_lo = (int)(((long long)NB * s) / S);
-  const int b_hi = (int)(((long long)NB * (s + 1)) / S);
+  int b_lo, b_hi;
+  split_range(NB, s, S, b_lo, b_hi);
 
   const int8_t *wtile = wq + (size_t)t * NB * kChunkBytes + lane * 16;
-  const float *stile = wsc + (size_t)t * NB * kTile + lane;
+  const float *stile = wsc + (size_t)t * NB * kTile + scale_pos(lane);
 
   float acc[MR];
 #pragma unroll
   for (int r = 0; r < MR; ++r) acc[r] = 0.0f;
 
-  for (int b0 = b_lo + wave; b0 < b_hi; b0 += W * kUnroll) {
-    uint4 wa[kUnroll], wb[kUnroll];
-    float sc[kUnroll];
-    // Issue every load of the step first; a block past the range reloads the
-    // last block of the range (in bounds) and is not used.
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int b = min(b0 + u * W, b_hi - 1);
-      const int8_t *c = wtile + (size_t)b * kChunkBytes;
-      wa[u] = *reinterpret_cast<const uint4 *>(c);
-      wb[u] = *reinterpret_cast<const uint4 *>(c + kHalfBytes);
-      if constexpr (!DOTS) sc[u] = stile[(size_t)b * kTile];
+  // Two stages in flight: the next stage's loads are issued before the
+  // current stage is computed, so HBM is never idle while the wave computes.
+  // Each path issues its prefetch unconditionally just before the compute it
+  // overlaps, which lets the compiler wait only for the older stage.
+  constexpr int step = W * kUnroll;
+  int b = b_lo + wave;
+  if (b < b_hi) {
+    ValuStage<MR, ACT, DOTS> A, B;
+    valu_load<MR, ACT, DOTS, W>(A, wtile, stile, b, b_hi, xv, m, K, NB, act_scale_off);
+    while (true) {
+      if (b + step >= b_hi) {
+        valu_compute<MR, ACT, DOTS, W>(A, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
+                                       act_scale_off);
+        break;
+      }
+      valu_load<MR, ACT, DOTS, W>(B, wtile, stile, b + step, b_hi, xv, m, K, NB, act_scale_off);
+      valu_compute<MR, ACT, DOTS, W>(A, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
+                                     act_scale_off);
+      b += step;
+      if (b + step >= b_hi) {
+        valu_compute<MR, ACT, DOTS, W>(B, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
+                                       act_scale_off);
+        break;
+      }
+      valu_load<MR, ACT, DOTS, W>(A, wtile, stile, b + step, b_hi, xv, m, K, NB, act_scale_off);
+      valu_compute<MR, ACT, DOTS, W>(B, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
+                                     act_scale_off);
+      b += step;
     }
+  }
+  if constexpr (DOTS) return;
+
+  __shared__ float red[W * MR * 64];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int b = b0 + u * W;
-      if (b >= b_hi) break;
-      const uint32_t wd[8] = {wa[u].x, wa[u].y, wa[u].z, wa[u].w,
-                              wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+  for (int r = 0; r < MR; ++r) red[(wave * MR + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+}
+
+// ---------------------------------------------------------------------------
+// the product, MFMA form: 16x16x32 matrix-core block dots
+// ---------------------------------------------------------------------------
+//
+// One block of one 16-column group is one MFMA per 16 activation rows:
+// D[r, c] = sum_{k<32} x[r, 32b+k] * q[32b+k, c], which is exactly the
+// per-block dot the method scales, so the scale is still applied once per
+// block, on the vector ALU, to D.  The 32-deep K of the instruction is one
+// Q8_0 block: blocks with different scales never mix.
+//
+// Lane l (i = l % 16, quarter j = l / 16) feeds A with row i's k = 8j..8j+7
+// and B with column i's k = 8j..8j+7, and receives D rows 4j..4j+3 of
+// column i.  The workgroup's activation rows for its whole K range sit in LDS
+// (bf16: 64 B per row and block; int8: 32 B plus the fp32 block scale), rows
+// m..MR-1 zero.  A wave owns blocks b_lo + wave + W*n and all 64 columns of
+// the tile; waves meet in LDS at the end as in the VALU form.
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+#ifndef Q8_MFMA_UNROLL
+#define Q8_MFMA_UNROLL 1
+#endif
+constexpr int kMfmaUnroll = Q8_MFMA_UNROLL;   // blocks per stage; two stages in flight
+
+struct MfmaStage {
+  uint2 w[kMfmaUnroll][4];       // 8 values of column 16g + i, k = 8j..8j+7
+  float4 sc[kMfmaUnroll];        // scales of columns i + 16g, g = 0..3
+};
+
+template <bool DOTS, int W>
+__device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
+                                          const float4 *slane, int b0, int b_hi) {
+#pragma unroll
+  for (int u = 0; u < kMfmaUnroll; ++u) {
+    const int b = min(b0 + u * W, b_hi - 1);
+    const int8_t *c = wlane + (size_t)b * kChunkBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) st.w[u][g] = ld_stream8(c + g * 256);
+    if constexpr (!DOTS) st.sc[u] = ld_stream16f(slane + (size_t)b * (kTile / 4));
+  }
+}
+
+// Eight int8 -> eight bf16 (exact: |q| <= 127 needs 8 significant bits).
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint2 v) {
+  float f[8];
+  i8x4_to_f32(v.x, f);
+  i8x4_to_f32(v.y, f + 4);
+  uint32_t p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    p[e] = __builtin_amdgcn_perm(__float_as_uint(f[2 * e + 1]), __float_as_uint(f[2 * e]),
+                                 0x07060302u);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
+}
+
+template <int MR, int ACT, bool DOTS, int W>
+__global__ void __launch_bounds__(64 * W)
+gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
+                 const float *__restrict__ wsc, float *__restrict__ y,
+                 float *__restrict__ partial, unsigned *__restrict__ counters,
+                 int32_t *__restrict__ dots, int m, int K, int NB, int Npad,
+                 int S, unsigned act_scale_off) {
+  constexpr int RG = MR / 16;
+  constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;   // one row of one block in LDS
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lj = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x / S;
+  const int s = blockIdx.x - t * S;
+  int b_lo, b_hi;
+  split_range(NB, s, S, b_lo, b_hi);
+  const int nblk = b_hi - b_lo;
+
+  // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
+  const int8_t *wlane = wq + (size_t)t * NB * kChunkBytes + (lj >> 1) * kHalfBytes + li * 16 +
+                        (lj & 1) * 8;
+  const float4 *slane =
+      reinterpret_cast<const float4 *>(wsc + (size_t)t * NB * kTile) + li;
+
+  constexpr int step = W * kMfmaUnroll;
+  int b = b_lo + wave;
+  MfmaStage A, B;
+  if (b < b_hi) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
+
+  // Stage the activation rows of [b_lo, b_hi) into LDS while the first weight
+  // loads are in flight: layout [block][row][kRowBytes], then (int8) the fp32
+  // block scales [block][row].
+  {
+    // Eight 16-byte pieces in flight per thread, then their LDS writes.  The
+    // loads are unconditional (indices clamped in bounds) so the compiler can
+    // keep all eight in flight; values past the range or past row m-1 are
+    // replaced by zero.
+    constexpr int kBatch = 8;
+    constexpr int ppr = kRowBytes / 16;   // pieces per row of a block
+    const int total = nblk * MR * ppr;
+    const char *xbase = static_cast<const char *>(xv);
+    for (int p0 = threadIdx.x; p0 < total; p0 += 64 * W * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = min(p0 + j * 64 * W, total - 1);
+        const int piece = p % ppr;
+        const int r = (p / ppr) % MR;
+        const int bb = p / (ppr * MR);
+        const int rr = min(r, m - 1);
+        v[j] = *reinterpret_cast<const uint4 *>(
+            xbase + ((size_t)rr * K + (size_t)(b_lo + bb) * kBlock) * (kRowBytes / 32) +
+            piece * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = p0 + j * 64 * W;
+        const int r = (p / ppr) % MR;
+        if (p < total)
+          *reinterpret_cast<uint4 *>(lds + (size_t)p * 16) =
+              (r < m) ? v[j] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if constexpr (ACT == kActQ8) {
+      float *dxs = reinterpret_cast<float *>(lds + (size_t)nblk * MR * kRowBytes);
+      const float *dxp = reinterpret_cast<const float *>(xbase + act_scale_off);
+      const int nd = nblk * MR;
+      for (int p0 = threadIdx.x; p0 < nd; p0 += 64 * W * kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int p = min(p0 + j * 64 * W, nd - 1);
+          const int r = p % MR, bb = p / MR;
+          v[j] = dxp[(size_t)min(r, m - 1) * NB + b_lo + bb];
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int p = p0 + j * 64 * W;
+          if (p < nd) dxs[p] = (p % MR < m) ? v[j] : 0.0f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[RG][4];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[rg][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const MfmaStage &st, int b0) {
+#pragma unroll
+    for (int u = 0; u < kMfmaUnroll; ++u) {
+      const int bb = b0 + u * W;
+      if (bb >= b_hi) break;
+      const int lb = bb - b_lo;
       if constexpr (ACT == kActBf16) {
-        float wf[32];
+        bf16x8_t a[RG];
 #pragma unroll
-        for (int d = 0; d < 8; ++d) i8x4_to_f32(wd[d], wf + 4 * d);
-        const uint16_t *xb = static_cast<const uint16_t *>(xv);
+        for (int rg = 0; rg < RG; ++rg)
+          a[rg] = *reinterpret_cast<const bf16x8_t *>(
+              lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 16);
+        const float scs[4] = {st.sc[u].x, st.sc[u].y, st.sc[u].z, st.sc[u].w};
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          if (r < m) {
-            const uint32_t *xr = reinterpret_cast<const uint32_t *>(
-                xb + (size_t)r * K + (size_t)b * kBlock);
-            float p0 = 0.0f, p1 = 0.0f;
+        for (int g = 0; g < 4; ++g) {
+          const bf16x8_t bw = i8x8_to_bf16(st.w[u][g]);
 #pragma unroll
-            for (int p = 0; p < 8; ++p) {
-              const uint32_t lo = xr[p], hi = xr[p + 8];
-              p0 = fmaf(bf16_lo(lo), wf[2 * p], p0);
-              p0 = fmaf(bf16_hi(lo), wf[2 * p + 1], p0);
-              p1 = fmaf(bf16_lo(hi), wf[16 + 2 * p], p1);
-              p1 = fmaf(bf16_hi(hi), wf[16 + 2 * p + 1], p1);
-            }
-            acc[r] = fmaf(sc[u], p0 + p1, acc[r]);
+          for (int rg = 0; rg < RG; ++rg) {
+            const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a[rg], bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rg][g][e] = fmaf(scs[g], d[e], acc[rg][g][e]);
           }
         }
       } else {
-        const int8_t *xq = static_cast<const int8_t *>(xv);
-        const float *dxp = reinterpret_cast<const float *>(
-            static_cast<const char *>(xv) + act_scale_off);
+        long a[RG];
+        float4 dx4[RG];
+        const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          if (r < m) {
-            const int *xr = reinterpret_cast<const int *>(
-                xq + (size_t)r * K + (size_t)b * kBlock);
-            int D = 0;
+        for (int rg = 0; rg < RG; ++rg) {
+          a[rg] = *reinterpret_cast<const long *>(
+              lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 8);
+          if constexpr (!DOTS)
+            dx4[rg] = *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + rg * 16 + lj * 4);
+        }
 #pragma unroll
-            for (int d = 0; d < 8; ++d)
-              D = __builtin_amdgcn_sdot4((int)wd[d], xr[d], D, false);
+        for (int g = 0; g < 4; ++g) {
+          const long bw = __builtin_bit_cast(long, st.w[u][g]);
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg) {
+            const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                a[rg], bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
             if constexpr (DOTS) {
-              dots[((size_t)r * NB + b) * Npad + (size_t)t * kTile + lane] = D;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = rg * 16 + lj * 4 + e;
+                if (r < m)
+                  dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + g * 16 + li] = d[e];
+              }
             } else {
-              const float dxs = dxp[(size_t)r * NB + b];
-              acc[r] = fmaf(dxs * sc[u], (float)D, acc[r]);
+              const float scg = (g == 0) ? st.sc[u].x : (g == 1) ? st.sc[u].y
+                              : (g == 2) ? st.sc[u].z : st.sc[u].w;
+              const float dxv[4] = {dx4[rg].x, dx4[rg].y, dx4[rg].z, dx4[rg].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[rg][g][e] = fmaf(dxv[e] * scg, (float)d[e], acc[rg][g][e]);
             }
           }
         }
       }
     }
+  };
+
+  if (b < b_hi) {
+    while (true) {
+      if (b + step >= b_hi) {
+        compute(A, b);
+        break;
+      }
+      mfma_load<DOTS, W>(B, wlane, slane, b + step, b_hi);
+      compute(A, b);
+      b += step;
+      if (b + step >= b_hi) {
+        compute(B, b);
+        break;
+      }
+      mfma_load<DOTS, W>(A, wlane, slane, b + step, b_hi);
+      compute(B, b);
+      b += step;
+    }
   }
   if constexpr (DOTS) return;
 
-  // Carries of the W waves meet in LDS, summed in wave order.
-  __shared__ float red[W][MR][64];
-#pragma unroll
-  for (int r = 0; r < MR; ++r) red[wave][r][lane] = acc[r];
+  // Waves meet in LDS (the staging area is free once every wave is done).
   __syncthreads();
-  const size_t col0 = (size_t)t * kTile;
-  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
-    const int r = idx >> 6, c = idx & 63;
-    if (r < m) {
-      float v = red[0][r][c];
+  float *red = reinterpret_cast<float *>(lds);
 #pragma unroll
-      for (int w = 1; w < W; ++w) v += red[w][r][c];
-      if (S == 1)
-        y[(size_t)r * Npad + col0 + c] = v;
-      else
-        partial[((size_t)s * m + r) * Npad + col0 + c] = v;
-    }
-  }
-  if (S == 1) return;
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
+  __syncthreads();
+  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+}
 
-  // Split K: the last workgroup of the tile to arrive sums the S partial
-  // carries in split order and resets the tile's counter for the next call.
-  __shared__ int is_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    is_last = (atomicAdd(&counters[t], 1u) == (unsigned)(S - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
-    const int r = idx >> 6, c = idx & 63;
-    if (r < m) {
-      float v = partial[(size_t)r * Npad + col0 + c];
-      for (int ss = 1; ss < S; ++ss)
-        v += partial[((size_t)ss * m + r) * Npad + col0 + c];
-      y[(size_t)r * Npad + col0 + c] = v;
-    }
-  }
-  if (threadIdx.x == 0) counters[t] = 0u;
+// Dynamic LDS bytes of an MFMA launch: the staged activation of the largest
+// split, or the wave carries, whichever is larger.
+size_t mfma_lds_bytes_of(int rows, int act, int waves, int NB, int S) {
+  const size_t nblk = (size_t)((NB + S - 1) / S);
+  const size_t stage = nblk * rows * (act == kActBf16 ? 64 : 36);
+  const size_t red = (size_t)waves * rows * 64 * 4;
+  return stage > red ? stage : red;
 }
 
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.T * a.split_k));
-  const dim3 block(64 * W);
-  gemv_valu_kernel<MR, ACT, DOTS, W><<<grid, block, 0, stream>>>(
+  gemv_valu_kernel<MR, ACT, DOTS, W><<<grid, dim3(64 * W), 0, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB,
       a.Npad, a.split_k, a.act_scale_off);
   return hipGetLastError();
 }
 
+template <int MR, int ACT, bool DOTS, int W>
+hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.T * a.split_k));
+  const size_t lds = mfma_lds_bytes_of(MR, ACT, W, a.NB, a.split_k);
+  auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W>;
+  // Above the default 64 KiB the kernel must be allowed more dynamic LDS;
+  // the largest size granted so far is remembered per instantiation.
+  static size_t granted = 64 * 1024;
+  if (lds > granted) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    granted = lds;
+  }
+  (void)hipGetLastError();
+  kern<<<grid, dim3(64 * W), lds, stream>>>(a.x, a.wq, a.wsc, a.y, a.partial, a.counters,
+                                            a.dots, a.m, a.K, a.NB, a.Npad, a.split_k,
+                                            a.act_scale_off);
+  return hipGetLastError();
+}
+
 using Launcher = hipError_t (*)(const GemvArgs &, hipStream_t);
 
+// VALU instantiations: 16 waves up to 4 rows, 8 waves up to 8 rows (more rows
+// would exceed the VGPRs the larger workgroups allow), 4 waves for any row count.
 template <int ACT, bool DOTS, int W>
 Launcher pick_valu_rows(int rows) {
   switch (rows) {
     case 1: return &launch_valu<1, ACT, DOTS, W>;
     case 2: return &launch_valu<2, ACT, DOTS, W>;
     case 4: return &launch_valu<4, ACT, DOTS, W>;
-    case 8: return &launch_valu<8, ACT, DOTS, W>;
-    case 16: return &launch_valu<16, ACT, DOTS, W>;
-    case 32: return &launch_valu<32, ACT, DOTS, W>;
+    default: break;
+  }
+  if constexpr (W <= 8) {
+    if (rows == 8) return &launch_valu<8, ACT, DOTS, W>;
+  }
+  if constexpr (W <= 4) {
+    if (rows == 16) return &launch_valu<16, ACT, DOTS, W>;
+    if (rows == 32) return &launch_valu<32, ACT, DOTS, W>;
+  }
+  return nullptr;
+}
+
+template <int ACT, bool DOTS, int W>
+Launcher pick_mfma_rows(int rows) {
+  switch (rows) {
+    case 16: return &launch_mfma<16, ACT, DOTS, W>;
+    case 32: return &launch_mfma<32, ACT, DOTS, W>;
     default: return nullptr;
   }
 }
 
 template <int W>
-Launcher pick_valu(int rows, int act, bool dots) {
-  if (act == kActBf16) return dots ? nullptr : pick_valu_rows<kActBf16, false, W>(rows);
-  if (act == kActQ8)
-    return dots ? pick_valu_rows<kActQ8, true, W>(rows)
-                : pick_valu_rows<kActQ8, false, W>(rows);
+Launcher pick_w(int kernel, int rows, int act, bool dots) {
+  if (kernel == 0) {
+    if (act == kActBf16) return dots ? nullptr : pick_valu_rows<kActBf16, false, W>(rows);
+    if (act == kActQ8)
+      return dots ? pick_valu_rows<kActQ8, true, W>(rows) : pick_valu_rows<kActQ8, false, W>(rows);
+  } else if (kernel == 1) {
+    if (act == kActBf16) return dots ? nullptr : pick_mfma_rows<kActBf16, false, W>(rows);
+    if (act == kActQ8)
+      return dots ? pick_mfma_rows<kActQ8, true, W>(rows) : pick_mfma_rows<kActQ8, false, W>(rows);
+  }
   return nullptr;
 }
 
 Launcher pick(int kernel, int rows, int act, bool dots, int waves) {
-  if (kernel == 0) {
-    if (waves == 4) return pick_valu<4>(rows, act, dots);
-    if (waves == 8 && rows <= 8) return pick_valu<8>(rows, act, dots);
+  switch (waves) {
+    case 4: return pick_w<4>(kernel, rows, act, dots);
+    case 8: return pick_w<8>(kernel, rows, act, dots);
+    case 16: return pick_w<16>(kernel, rows, act, dots);
+    default: return nullptr;
   }
-  return nullptr;
 }
 
 unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
@@ -338,6 +783,10 @@ hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
   float *dx = reinterpret_cast<float *>(static_cast<char *>(x_q8) + scale_off);
   quantize_act_kernel<<<blocks_for(total), 256, 0, stream>>>(x, xq, dx, total);
   return hipGetLastError();
+}
+
+size_t mfma_lds_bytes(int rows, int act, int waves, int NB, int split_k) {
+  return mfma_lds_bytes_of(rows, act, waves, NB, split_k);
 }
 
 bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves) {

@@ -174,7 +174,7 @@ typedef struct q8_plan {
   int32_t kernel;  /* q8_kernel                                                */
   int32_t rows;    /* row count the kernel is built for (1,2,4,8,16,32) >= m   */
   int32_t split_k; /* K splits across workgroups, 1..K/32                      */
-  int32_t waves;   /* waves (64 lanes) per workgroup: 4 or 8                   */
+  int32_t waves;   /* waves (64 lanes) per workgroup: 4, 8 or 16               */
 } q8_plan;
 
 /* The plan q8_gemv would launch for this shape on the current device. */

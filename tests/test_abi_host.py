@@ -45,7 +45,7 @@ def test_sizes():
     assert q8.q8_act_scales_offset(32, 5120) == 163840
     assert q8.q8_act_bytes(32, 5120) == 163840 + 32 * 160 * 4
     assert q8.q8_act_scales_offset(1, 32) == 256
-    assert q8.q8_layout_version() == 1
+    assert q8.q8_layout_version() == 2
 
 
 def expect(status, fn, *args):

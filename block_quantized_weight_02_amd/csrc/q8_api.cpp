@@ -126,15 +126,14 @@ int rows_for(int64_t m) {
   return r;
 }
 
-// The default launch.
+// The default launch (settled by measurement on MI355X, see the design notes):
 //  * VALU kernel (lane per column) while the rows are few enough that the
 //    vector ALU keeps up with HBM: bf16 up to 4 rows, int8 up to 8 rows;
 //    MFMA kernel above.
-//  * VALU: 16 waves per workgroup; K split across workgroups only when the
+//  * VALU: 8 waves per workgroup; K split across workgroups only when the
 //    column tiles alone leave CUs idle (splits = CUs / tiles, each split at
 //    least 8 blocks).
-//  * MFMA: the fewest K splits whose staged activation fits the LDS budget,
-//    then more while the tiles leave CUs idle.
+//  * MFMA: 16 waves; the fewest K splits whose staged activation fits the LDS.
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
@@ -145,7 +144,7 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   if (m <= valu_rows) {
     p.kernel = Q8_KERNEL_VALU;
     p.rows = rows_for(m);
-    p.waves = p.rows <= 4 ? 16 : 8;
+    p.waves = 8;
     int64_t S = dev.cus / T;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
@@ -154,12 +153,10 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   }
   p.kernel = Q8_KERNEL_MFMA;
   p.rows = m <= 16 ? 16 : 32;
-  p.waves = 8;
-  int64_t S = dev.cus / T;
-  if (S < 1) S = 1;
+  p.waves = 16;
+  int64_t S = 1;
   const size_t budget = (size_t)dev.lds_per_block;
   while (S < NB && q8::mfma_lds_bytes(p.rows, act_fmt, p.waves, (int)NB, (int)S) > budget) ++S;
-  if (S > NB) S = NB;
   p.split_k = (int32_t)S;
   return p;
 }

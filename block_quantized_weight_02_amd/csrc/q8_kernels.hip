@@ -629,6 +629,9 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     }
   };
 
+  // One compute site: the next stage is loaded into B while A is computed,
+  // then copied into A (the copy waits for B, which the next compute needs
+  // anyway).  Keeping a single site keeps the carries in fixed registers.
   if (b < b_hi) {
     while (true) {
       if (b + step >= b_hi) {
@@ -636,14 +639,9 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         break;
       }
       mfma_load<DOTS, W>(B, wlane, slane, b + step, b_hi);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
       compute(A, b);
-      b += step;
-      if (b + step >= b_hi) {
-        compute(B, b);
-        break;
-      }
-      mfma_load<DOTS, W>(A, wlane, slane, b + step, b_hi);
-      compute(B, b);
+      A = B;
       b += step;
     }
   }

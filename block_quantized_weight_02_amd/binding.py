@@ -21,6 +21,7 @@ Q8_ACT_BF16 = 0
 Q8_ACT_Q8_0 = 1
 Q8_KERNEL_VALU = 0
 Q8_KERNEL_MFMA = 1
+Q8_KERNEL_MFMA_COLS = 2
 
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_SHAPE", 2: "Q8_ERR_ACT_FMT", 3: "Q8_ERR_NULL",
           4: "Q8_ERR_ALIGN", 5: "Q8_ERR_WORKSPACE", 6: "Q8_ERR_HIP", 7: "Q8_ERR_PLAN"}
@@ -35,11 +36,12 @@ class Q8Error(RuntimeError):
 
 class q8_plan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("rows", ctypes.c_int32),
-                ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("kslices", ctypes.c_int32)]
 
     def __repr__(self):
-        return (f"q8_plan(kernel={self.kernel}, rows={self.rows}, "
-                f"split_k={self.split_k}, waves={self.waves})")
+        return (f"q8_plan(kernel={self.kernel}, rows={self.rows}, split_k={self.split_k}, "
+                f"waves={self.waves}, kslices={self.kslices})")
 
 
 _i64 = ctypes.c_int64

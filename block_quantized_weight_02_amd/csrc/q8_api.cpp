@@ -92,6 +92,9 @@ size_t act_scales_offset(int64_t m, int64_t K) {
   return (size_t)round_up(m * K, 256);
 }
 
+// LDS per workgroup kept free for the kernels' static shared variables.
+constexpr size_t kStaticLdsReserve = 1024;
+
 // ---- device facts -----------------------------------------------------------
 
 struct DeviceFacts {
@@ -133,13 +136,15 @@ int rows_for(int64_t m) {
 //  * VALU: 8 waves per workgroup; K split across workgroups only when the
 //    column tiles alone leave CUs idle (splits = CUs / tiles, each split at
 //    least 8 blocks).
-//  * MFMA: 16 waves; the fewest K splits whose staged activation fits the LDS.
+//  * MFMA (see below): 16 waves; the fewest K splits whose staged activation
+//    fits the LDS.
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   const DeviceFacts dev = device_facts();
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
   q8_plan p;
+  p.kslices = 1;
   const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 4 : 8;
   if (m <= valu_rows) {
     p.kernel = Q8_KERNEL_VALU;
@@ -151,12 +156,19 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
     p.split_k = (int32_t)S;
     return p;
   }
-  p.kernel = Q8_KERNEL_MFMA;
+  // Matrix cores.  bf16 activations: waves split K and each covers the whole
+  // tile, so one LDS fragment read serves four MFMAs.  int8 activations: each
+  // wave owns a 16-column group and the workgroup walks tiles with the
+  // activation staged once (measured faster for the int8 shapes).
+  p.kernel = act_fmt == Q8_ACT_BF16 ? Q8_KERNEL_MFMA : Q8_KERNEL_MFMA_COLS;
   p.rows = m <= 16 ? 16 : 32;
   p.waves = 16;
+  p.kslices = 1;
   int64_t S = 1;
   const size_t budget = (size_t)dev.lds_per_block;
-  while (S < NB && q8::mfma_lds_bytes(p.rows, act_fmt, p.waves, (int)NB, (int)S) > budget) ++S;
+  while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
+                                      (int)S) > budget - kStaticLdsReserve)
+    ++S;
   p.split_k = (int32_t)S;
   return p;
 }
@@ -170,12 +182,15 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
   if (p->split_k < 1 || p->split_k > NB)
     return fail(Q8_ERR_PLAN, "plan split_k = %d: need 1 <= split_k <= K/32 = %lld",
                 p->split_k, (long long)NB);
-  if (!q8::gemv_instantiated(p->kernel, p->rows, act, dots, p->waves))
-    return fail(Q8_ERR_PLAN, "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d",
-                p->kernel, p->rows, act, (int)dots, p->waves);
-  if (p->kernel == Q8_KERNEL_MFMA) {
-    const size_t need = q8::mfma_lds_bytes(p->rows, act, p->waves, (int)NB, p->split_k);
-    const size_t have = (size_t)device_facts().lds_per_block;
+  if (!q8::gemv_instantiated(p->kernel, p->rows, act, dots, p->waves, p->kslices))
+    return fail(Q8_ERR_PLAN,
+                "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d kslices=%d",
+                p->kernel, p->rows, act, (int)dots, p->waves, p->kslices);
+  if (p->kernel != Q8_KERNEL_VALU) {
+    const size_t need =
+        q8::gemv_lds_bytes(p->kernel, p->rows, act, p->waves, p->kslices, (int)NB, p->split_k);
+    // keep room for the kernels' own static LDS (a few bytes of flags)
+    const size_t have = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
     if (need > have)
       return fail(Q8_ERR_PLAN, "plan needs %zu bytes of LDS per workgroup, the device has %zu: "
                   "raise split_k", need, have);
@@ -183,11 +198,12 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
   return Q8_OK;
 }
 
-// Workspace layout: arrival counters first, one uint32 per column tile at a
-// fixed place (tile t at byte 4t) for every shape, then the partial carries.
-// Every call leaves its counters at zero and nothing else writes that region,
-// so a workspace zeroed once stays valid for calls of any shape.
-constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4;
+// Workspace layout: arrival counters first, at fixed places for every shape
+// (the VALU kernel uses one per 64-column tile, the MFMA kernel one per
+// 16-column group: 4 per tile), then the partial carries.  Every call leaves
+// its counters at zero and nothing else writes that region, so a workspace
+// zeroed once stays valid for calls of any shape.
+constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4 * 4;
 
 size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N) {
   if (p.split_k <= 1) return 0;
@@ -270,8 +286,11 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   }
   (void)hipGetLastError();  // clear a stale error so the launch's own is seen
   hipError_t e = q8::launch_gemv(plan.kernel, plan.rows, act_fmt, write_dots,
-                                 plan.waves, a, stream);
-  if (e != hipSuccess) return hip_fail(e, "gemv launch");
+                                 plan.waves, plan.kslices, a, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // do not leave the failure for the caller's next HIP call
+    return hip_fail(e, "gemv launch");
+  }
   return ok();
 }
 

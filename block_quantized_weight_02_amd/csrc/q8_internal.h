@@ -37,7 +37,8 @@ struct GemvArgs {
   const float *wsc;       // packed scales (unused when writing dots)
   float *y;               // m x Npad
   float *partial;         // split_k x m x Npad (split_k > 1)
-  unsigned *counters;     // T arrival counters (split_k > 1), zero between calls
+  unsigned *counters;     // arrival counters (split_k > 1), zero between calls:
+                          // VALU one per tile, MFMA one per 16-column group
   int32_t *dots;          // m x NB x Npad (dot mode)
   int m, K, NB, Npad, T;
   int split_k;
@@ -51,13 +52,15 @@ hipError_t launch_unpack(const int8_t *wq, const float *wsc, int K, int N,
                          int8_t *q_kn, float *s_kn, hipStream_t stream);
 hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
                                unsigned scale_off, hipStream_t stream);
-// kernel: 0 VALU, 1 MFMA; rows: 1,2,4,8,16,32; act: Act; waves: 4, 8 or 16.
+// kernel: 0 VALU, 1 MFMA (waves split K, each over all 64 columns), 2 MFMA
+// (waves own 16-column groups); rows: 1,2,4,8,16,32; act: Act; waves: 4, 8
+// or 16; kslices: waves sharing one column group's K range (kernel 2 only).
 // Returns hipErrorInvalidValue for a combination that is not instantiated.
-hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots,
-                       int waves, const GemvArgs &a, hipStream_t stream);
-bool gemv_instantiated(int kernel, int rows, int act, bool write_dots,
-                       int waves);
-// Dynamic LDS bytes an MFMA launch needs (activation staging or wave carries).
-size_t mfma_lds_bytes(int rows, int act, int waves, int NB, int split_k);
+hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots, int waves, int kslices,
+                       const GemvArgs &a, hipStream_t stream);
+bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves, int kslices);
+// Dynamic LDS bytes a launch needs (activation stage plus carries; 0 for VALU).
+size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int NB,
+                      int split_k);
 
 }  // namespace q8

@@ -417,7 +417,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 }
 
 // ---------------------------------------------------------------------------
-// the product, MFMA form: 16x16x32 matrix-core block dots
+// the product, MFMA forms: 16x16x32 matrix-core block dots
 // ---------------------------------------------------------------------------
 //
 // One block of one 16-column group is one MFMA per 16 activation rows:
@@ -428,35 +428,45 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 //
 // Lane l (i = l % 16, quarter j = l / 16) feeds A with row i's k = 8j..8j+7
 // and B with column i's k = 8j..8j+7, and receives D rows 4j..4j+3 of
-// column i.  The workgroup's activation rows for its whole K range sit in LDS
-// (bf16: 64 B per row and block; int8: 32 B plus the fp32 block scale), rows
-// m..MR-1 zero.  A wave owns blocks b_lo + wave + W*n and all 64 columns of
-// the tile; waves meet in LDS at the end as in the VALU form.
+// column i.
+//
+// Work split.  A wave owns one 16-column group g of a tile; KW waves split
+// the blocks of the workgroup's K range between them (wave kw takes blocks
+// kw, kw+KW, ...) and meet in LDS at the end of the tile; P groups of 4*KW
+// waves ("slots") work on P tiles side by side.  The workgroup's activation
+// rows for its K range are staged into LDS once (bf16: 64 B per row and
+// block; int8: 32 B plus the fp32 block scale; rows m..MR-1 zero) and serve
+// every tile the workgroup then walks through: tiles j*P + slot, stepping by
+// G*P over the grid's G workgroups per K split.
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
+// Blocks per stage (two stages in flight): the block-interleaved kernel
+// loads four 16-column groups per block, the column-group kernel one.
 #ifndef Q8_MFMA_UNROLL
 #define Q8_MFMA_UNROLL 1
 #endif
-constexpr int kMfmaUnroll = Q8_MFMA_UNROLL;   // blocks per stage; two stages in flight
+#ifndef Q8_COLS_UNROLL
+#define Q8_COLS_UNROLL 2
+#endif
+constexpr int kMfmaUnroll = Q8_MFMA_UNROLL;
+constexpr int kColsUnroll = Q8_COLS_UNROLL;
 
-struct MfmaStage {
-  uint2 w[kMfmaUnroll][4];       // 8 values of column 16g + i, k = 8j..8j+7
-  float4 sc[kMfmaUnroll];        // scales of columns i + 16g, g = 0..3
+struct ColsStage {
+  uint2 w[kColsUnroll];    // 8 values of the lane's column, k = 8j..8j+7
+  float sc[kColsUnroll];   // the lane's column scale
 };
 
-template <bool DOTS, int W>
-__device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
-                                          const float4 *slane, int b0, int b_hi) {
+template <bool DOTS, int KW>
+__device__ __forceinline__ void cols_load(ColsStage &st, const int8_t *wcol, const float *scol,
+                                          int b0, int b_hi) {
 #pragma unroll
-  for (int u = 0; u < kMfmaUnroll; ++u) {
-    const int b = min(b0 + u * W, b_hi - 1);
-    const int8_t *c = wlane + (size_t)b * kChunkBytes;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) st.w[u][g] = ld_stream8(c + g * 256);
-    if constexpr (!DOTS) st.sc[u] = ld_stream16f(slane + (size_t)b * (kTile / 4));
+  for (int u = 0; u < kColsUnroll; ++u) {
+    const int b = min(b0 + u * KW, b_hi - 1);
+    st.w[u] = ld_stream8(wcol + (size_t)b * kChunkBytes);
+    if constexpr (!DOTS) st.sc[u] = ld_stream4f(scol + (size_t)b * kTile);
   }
 }
 
@@ -473,13 +483,74 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint2 v) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
 }
 
-template <int MR, int ACT, bool DOTS, int W>
-__global__ void __launch_bounds__(64 * W)
-gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
-                 const float *__restrict__ wsc, float *__restrict__ y,
-                 float *__restrict__ partial, unsigned *__restrict__ counters,
-                 int32_t *__restrict__ dots, int m, int K, int NB, int Npad,
-                 int S, unsigned act_scale_off) {
+// Bytes of the activation stage of one workgroup (largest split).
+__host__ __device__ constexpr size_t mfma_stage_bytes(int rows, int act, int nblk) {
+  return (size_t)nblk * rows * (act == kActBf16 ? 64 : 36);
+}
+
+// Stage the activation rows of blocks [b_lo, b_lo + nblk) into LDS:
+// [block][row][kRowBytes], then (int8) the fp32 block scales [block][row].
+// Eight 16-byte pieces in flight per thread; the loads are unconditional
+// (indices clamped in bounds) and values past the range or past row m-1 are
+// replaced by zero at the LDS write.
+template <int MR, int ACT, int NTHREADS>
+__device__ __forceinline__ void stage_activation(char *lds, const void *__restrict__ xv, int m,
+                                                 int K, int NB, int b_lo, int nblk,
+                                                 unsigned act_scale_off) {
+  constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;
+  constexpr int kBatch = 8;
+  constexpr int ppr = kRowBytes / 16;
+  const int total = nblk * MR * ppr;
+  const char *xbase = static_cast<const char *>(xv);
+  for (int p0 = threadIdx.x; p0 < total; p0 += NTHREADS * kBatch) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int p = min(p0 + q * NTHREADS, total - 1);
+      const int piece = p % ppr;
+      const int r = (p / ppr) % MR;
+      const int bb = p / (ppr * MR);
+      v[q] = *reinterpret_cast<const uint4 *>(
+          xbase + ((size_t)min(r, m - 1) * K + (size_t)(b_lo + bb) * kBlock) * (kRowBytes / 32) +
+          piece * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int p = p0 + q * NTHREADS;
+      const int r = (p / ppr) % MR;
+      if (p < total)
+        *reinterpret_cast<uint4 *>(lds + (size_t)p * 16) =
+            (r < m) ? v[q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if constexpr (ACT == kActQ8) {
+    float *dxs = reinterpret_cast<float *>(lds + (size_t)nblk * MR * kRowBytes);
+    const float *dxp = reinterpret_cast<const float *>(xbase + act_scale_off);
+    const int nd = nblk * MR;
+    for (int p0 = threadIdx.x; p0 < nd; p0 += NTHREADS * kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int p = min(p0 + q * NTHREADS, nd - 1);
+        v[q] = dxp[(size_t)min(p % MR, m - 1) * NB + b_lo + p / MR];
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const int p = p0 + q * NTHREADS;
+        if (p < nd) dxs[p] = (p % MR < m) ? v[q] : 0.0f;
+      }
+    }
+  }
+}
+
+template <int MR, int ACT, bool DOTS, int KW, int P>
+__global__ void __launch_bounds__(256 * KW * P)
+gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
+                      const float *__restrict__ wsc, float *__restrict__ y,
+                      float *__restrict__ partial, unsigned *__restrict__ counters,
+                      int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
+                      int S, int G, int nblk_max, unsigned act_scale_off) {
+  constexpr int W = 4 * KW * P;
   constexpr int RG = MR / 16;
   constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;   // one row of one block in LDS
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -487,187 +558,370 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lj = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = blockIdx.x / S;
-  const int s = blockIdx.x - t * S;
+  const int g = wave & 3;
+  const int kw = (wave >> 2) % KW;
+  const int slot = wave / (4 * KW);
+  const int s = blockIdx.x % S;
+  const int jwg = blockIdx.x / S;
   int b_lo, b_hi;
   split_range(NB, s, S, b_lo, b_hi);
   const int nblk = b_hi - b_lo;
+  const int col_in_tile = 16 * g + li;
+  // lane's bytes in a chunk: half j/2, column 16g+i, k offset 8*(j%2)
+  const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + (size_t)col_in_tile * 16 + (lj & 1) * 8;
 
-  // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
-  const int8_t *wlane = wq + (size_t)t * NB * kChunkBytes + (lj >> 1) * kHalfBytes + li * 16 +
-                        (lj & 1) * 8;
-  const float4 *slane =
-      reinterpret_cast<const float4 *>(wsc + (size_t)t * NB * kTile) + li;
+  constexpr int step = KW * kColsUnroll;
+  int t = jwg * P + slot;
+  ColsStage A, B;
+  // First stage of the first tile in flight while the activation is staged.
+  if (t < T && b_lo + kw < b_hi)
+    cols_load<DOTS, KW>(A, wq + (size_t)t * NB * kChunkBytes + lane_off,
+                        wsc + (size_t)t * NB * kTile + scale_pos(col_in_tile), b_lo + kw, b_hi);
 
-  constexpr int step = W * kMfmaUnroll;
-  int b = b_lo + wave;
-  MfmaStage A, B;
-  if (b < b_hi) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
-
-  // Stage the activation rows of [b_lo, b_hi) into LDS while the first weight
-  // loads are in flight: layout [block][row][kRowBytes], then (int8) the fp32
-  // block scales [block][row].
-  {
-    // Eight 16-byte pieces in flight per thread, then their LDS writes.  The
-    // loads are unconditional (indices clamped in bounds) so the compiler can
-    // keep all eight in flight; values past the range or past row m-1 are
-    // replaced by zero.
-    constexpr int kBatch = 8;
-    constexpr int ppr = kRowBytes / 16;   // pieces per row of a block
-    const int total = nblk * MR * ppr;
-    const char *xbase = static_cast<const char *>(xv);
-    for (int p0 = threadIdx.x; p0 < total; p0 += 64 * W * kBatch) {
-      uint4 v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = min(p0 + j * 64 * W, total - 1);
-        const int piece = p % ppr;
-        const int r = (p / ppr) % MR;
-        const int bb = p / (ppr * MR);
-        const int rr = min(r, m - 1);
-        v[j] = *reinterpret_cast<const uint4 *>(
-            xbase + ((size_t)rr * K + (size_t)(b_lo + bb) * kBlock) * (kRowBytes / 32) +
-            piece * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = p0 + j * 64 * W;
-        const int r = (p / ppr) % MR;
-        if (p < total)
-          *reinterpret_cast<uint4 *>(lds + (size_t)p * 16) =
-              (r < m) ? v[j] : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    if constexpr (ACT == kActQ8) {
-      float *dxs = reinterpret_cast<float *>(lds + (size_t)nblk * MR * kRowBytes);
-      const float *dxp = reinterpret_cast<const float *>(xbase + act_scale_off);
-      const int nd = nblk * MR;
-      for (int p0 = threadIdx.x; p0 < nd; p0 += 64 * W * kBatch) {
-        float v[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int p = min(p0 + j * 64 * W, nd - 1);
-          const int r = p % MR, bb = p / MR;
-          v[j] = dxp[(size_t)min(r, m - 1) * NB + b_lo + bb];
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int p = p0 + j * 64 * W;
-          if (p < nd) dxs[p] = (p % MR < m) ? v[j] : 0.0f;
-        }
-      }
-    }
-  }
+  stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
   __syncthreads();
+  const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
+  float *red = reinterpret_cast<float *>(lds + mfma_stage_bytes(MR, ACT, nblk_max));
 
-  f32x4_t acc[RG][4];
+  for (; t < T; t += G * P) {
+    const int8_t *wcol = wq + (size_t)t * NB * kChunkBytes + lane_off;
+    const float *scol = wsc + (size_t)t * NB * kTile + scale_pos(col_in_tile);
+    f32x4_t acc[RG];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[rg][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const MfmaStage &st, int b0) {
+    auto compute = [&](const ColsStage &st, int b0) {
 #pragma unroll
-    for (int u = 0; u < kMfmaUnroll; ++u) {
-      const int bb = b0 + u * W;
-      if (bb >= b_hi) break;
-      const int lb = bb - b_lo;
-      if constexpr (ACT == kActBf16) {
-        bf16x8_t a[RG];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-          a[rg] = *reinterpret_cast<const bf16x8_t *>(
-              lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 16);
-        const float scs[4] = {st.sc[u].x, st.sc[u].y, st.sc[u].z, st.sc[u].w};
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const bf16x8_t bw = i8x8_to_bf16(st.w[u][g]);
+      for (int u = 0; u < kColsUnroll; ++u) {
+        const int bb = b0 + u * KW;
+        if (bb >= b_hi) break;
+        const int lb = bb - b_lo;
+        if constexpr (ACT == kActBf16) {
+          const bf16x8_t bw = i8x8_to_bf16(st.w[u]);
 #pragma unroll
           for (int rg = 0; rg < RG; ++rg) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 16);
             const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a[rg], bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                a, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rg][g][e] = fmaf(scs[g], d[e], acc[rg][g][e]);
+            for (int e = 0; e < 4; ++e) acc[rg][e] = fmaf(st.sc[u], d[e], acc[rg][e]);
           }
-        }
-      } else {
-        long a[RG];
-        float4 dx4[RG];
-        const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          a[rg] = *reinterpret_cast<const long *>(
-              lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 8);
-          if constexpr (!DOTS)
-            dx4[rg] = *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + rg * 16 + lj * 4);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const long bw = __builtin_bit_cast(long, st.w[u][g]);
+        } else {
+          const long bw = __builtin_bit_cast(long, st.w[u]);
 #pragma unroll
           for (int rg = 0; rg < RG; ++rg) {
-            const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                a[rg], bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+            const long a = *reinterpret_cast<const long *>(
+                lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 8);
+            const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw, i32x4_t{0, 0, 0, 0},
+                                                                   0, 0, 0);
             if constexpr (DOTS) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = rg * 16 + lj * 4 + e;
                 if (r < m)
-                  dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + g * 16 + li] = d[e];
+                  dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + col_in_tile] = d[e];
               }
             } else {
-              const float scg = (g == 0) ? st.sc[u].x : (g == 1) ? st.sc[u].y
-                              : (g == 2) ? st.sc[u].z : st.sc[u].w;
-              const float dxv[4] = {dx4[rg].x, dx4[rg].y, dx4[rg].z, dx4[rg].w};
+              const float4 dx4 =
+                  *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + rg * 16 + lj * 4);
+              const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                acc[rg][g][e] = fmaf(dxv[e] * scg, (float)d[e], acc[rg][g][e]);
+                acc[rg][e] = fmaf(dxv[e] * st.sc[u], (float)d[e], acc[rg][e]);
             }
           }
         }
       }
-    }
-  };
+    };
 
-  // One compute site: the next stage is loaded into B while A is computed,
-  // then copied into A (the copy waits for B, which the next compute needs
-  // anyway).  Keeping a single site keeps the carries in fixed registers.
-  if (b < b_hi) {
-    while (true) {
-      if (b + step >= b_hi) {
+    int b = b_lo + kw;
+    if (b < b_hi) {
+      if (t != jwg * P + slot)   // the first tile's first stage is already in flight
+        cols_load<DOTS, KW>(A, wcol, scol, b, b_hi);
+      // One compute site: the next stage is loaded into B while A is
+      // computed, then copied into A (the copy waits for B, which the next
+      // compute needs anyway).
+      while (true) {
+        if (b + step >= b_hi) {
+          compute(A, b);
+          break;
+        }
+        cols_load<DOTS, KW>(B, wcol, scol, b + step, b_hi);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
         compute(A, b);
-        break;
+        A = B;
+        b += step;
       }
-      mfma_load<DOTS, W>(B, wlane, slane, b + step, b_hi);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
-      compute(A, b);
-      A = B;
-      b += step;
     }
-  }
-  if constexpr (DOTS) return;
+    if constexpr (DOTS) continue;
 
-  // Waves meet in LDS (the staging area is free once every wave is done).
-  __syncthreads();
-  float *red = reinterpret_cast<float *>(lds);
+    if constexpr (KW > 1) {
+      // The KW waves of a column group meet in LDS, summed in kw order.
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+        for (int e = 0; e < 4; ++e)
+          red[(kw * MR + rg * 16 + lj * 4 + e) * 64 + col_in_tile] = acc[rg][e];
+      __syncthreads();
+      if (kw == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
-  __syncthreads();
-  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[rg][e];
+#pragma unroll
+            for (int w2 = 1; w2 < KW; ++w2) v += red[(w2 * MR + rg * 16 + lj * 4 + e) * 64 + col_in_tile];
+            acc[rg][e] = v;
+          }
+      }
+      __syncthreads();   // red is free again for the next tile
+      if (kw != 0) continue;
+    }
+
+    // This wave's 16 columns are final for its split: store, or publish the
+    // partial and let the last split to arrive sum them in split order (the
+    // same protocol as finish_tile, per 16-column group, inside one wave).
+    const size_t col = (size_t)t * kTile + col_in_tile;
+    if (S == 1) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rg * 16 + lj * 4 + e;
+          if (r < m) y[(size_t)r * Npad + col] = acc[rg][e];
+        }
+      continue;
+    }
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rg * 16 + lj * 4 + e;
+        if (r < m)
+          __hip_atomic_store(&partial[((size_t)s * m + r) * Npad + col], acc[rg][e],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    unsigned prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&counters[(size_t)t * 4 + g], 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_SYSTEM);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (unsigned)(S - 1)) continue;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rg * 16 + lj * 4 + e;
+        if (r < m) {
+          float v = __hip_atomic_load(&partial[(size_t)r * Npad + col], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_SYSTEM);
+          for (int ss = 1; ss < S; ++ss)
+            v += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+          y[(size_t)r * Npad + col] = v;
+        }
+      }
+    if (lane == 0)
+      __hip_atomic_store(&counters[(size_t)t * 4 + g], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
-// Dynamic LDS bytes of an MFMA launch: the staged activation of the largest
-// split, or the wave carries, whichever is larger.
+// ---------------------------------------------------------------------------
+// the product, MFMA form with block-interleaved waves
+// ---------------------------------------------------------------------------
+//
+// Every wave covers all 64 columns of the tile (four 16-column MFMAs per row
+// group and block) and the W waves split the blocks of the workgroup's K range
+// (wave w takes blocks w, w+W, ...), so one activation fragment read from LDS
+// serves four MFMAs.  The carries of the W waves meet in LDS at the end of
+// each tile.  The activation rows of the workgroup's K range are staged once
+// and serve every tile the workgroup walks through (tiles j, j+G, ...).
+
+struct MfmaStage {
+  uint2 w[kMfmaUnroll][4];   // 8 values of column 16g + i, k = 8j..8j+7
+  float4 sc[kMfmaUnroll];    // scales of columns i + 16g, g = 0..3
+};
+
+template <bool DOTS, int W>
+__device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
+                                          const float4 *slane, int b0, int b_hi) {
+#pragma unroll
+  for (int u = 0; u < kMfmaUnroll; ++u) {
+    const int b = min(b0 + u * W, b_hi - 1);
+    const int8_t *c = wlane + (size_t)b * kChunkBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) st.w[u][g] = ld_stream8(c + g * 256);
+    if constexpr (!DOTS) st.sc[u] = ld_stream16f(slane + (size_t)b * (kTile / 4));
+  }
+}
+
+template <int MR, int ACT, bool DOTS, int W>
+__global__ void __launch_bounds__(64 * W)
+gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
+                 const float *__restrict__ wsc, float *__restrict__ y,
+                 float *__restrict__ partial, unsigned *__restrict__ counters,
+                 int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
+                 int S, int G, int nblk_max, int red_on_stage, unsigned act_scale_off) {
+  constexpr int RG = MR / 16;
+  constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lj = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s = blockIdx.x % S;
+  const int jwg = blockIdx.x / S;
+  int b_lo, b_hi;
+  split_range(NB, s, S, b_lo, b_hi);
+  const int nblk = b_hi - b_lo;
+  // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
+  const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
+
+  constexpr int step = W * kMfmaUnroll;
+  MfmaStage A, B;
+  if (jwg < T && b_lo + wave < b_hi)
+    mfma_load<DOTS, W>(A, wq + (size_t)jwg * NB * kChunkBytes + lane_off,
+                       reinterpret_cast<const float4 *>(wsc + (size_t)jwg * NB * kTile) + li,
+                       b_lo + wave, b_hi);
+  stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
+  __syncthreads();
+  const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
+  // The carries' area: after the stage, or (when every workgroup has at most
+  // one tile, G >= T) on top of the stage, which is no longer read by then.
+  float *red = reinterpret_cast<float *>(
+      lds + (red_on_stage ? (size_t)0 : mfma_stage_bytes(MR, ACT, nblk_max)));
+
+  for (int t = jwg; t < T; t += G) {
+    const int8_t *wlane = wq + (size_t)t * NB * kChunkBytes + lane_off;
+    const float4 *slane = reinterpret_cast<const float4 *>(wsc + (size_t)t * NB * kTile) + li;
+    f32x4_t acc[RG][4];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[rg][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](const MfmaStage &st, int b0) {
+#pragma unroll
+      for (int u = 0; u < kMfmaUnroll; ++u) {
+        const int bb = b0 + u * W;
+        if (bb >= b_hi) break;
+        const int lb = bb - b_lo;
+        if constexpr (ACT == kActBf16) {
+          bf16x8_t a[RG];
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg)
+            a[rg] = *reinterpret_cast<const bf16x8_t *>(
+                lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 16);
+          const float scs[4] = {st.sc[u].x, st.sc[u].y, st.sc[u].z, st.sc[u].w};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const bf16x8_t bw = i8x8_to_bf16(st.w[u][g]);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  a[rg], bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[rg][g][e] = fmaf(scs[g], d[e], acc[rg][g][e]);
+            }
+          }
+        } else {
+          long a[RG];
+          float4 dx4[RG];
+#pragma unroll
+          for (int rg = 0; rg < RG; ++rg) {
+            a[rg] = *reinterpret_cast<const long *>(
+                lds + ((size_t)lb * MR + rg * 16 + li) * kRowBytes + lj * 8);
+            if constexpr (!DOTS)
+              dx4[rg] = *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + rg * 16 + lj * 4);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const long bw = __builtin_bit_cast(long, st.w[u][g]);
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+              const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                  a[rg], bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+              if constexpr (DOTS) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int r = rg * 16 + lj * 4 + e;
+                  if (r < m)
+                    dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + g * 16 + li] = d[e];
+                }
+              } else {
+                const float scg = (g == 0) ? st.sc[u].x : (g == 1) ? st.sc[u].y
+                                : (g == 2) ? st.sc[u].z : st.sc[u].w;
+                const float dxv[4] = {dx4[rg].x, dx4[rg].y, dx4[rg].z, dx4[rg].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  acc[rg][g][e] = fmaf(dxv[e] * scg, (float)d[e], acc[rg][g][e]);
+              }
+            }
+          }
+        }
+      }
+    };
+
+    int b = b_lo + wave;
+    if (b < b_hi) {
+      if (t != jwg) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
+      // One compute site: the next stage is loaded into B while A is
+      // computed, then copied into A (the copy waits for B, which the next
+      // compute needs anyway).
+      while (true) {
+        if (b + step >= b_hi) {
+          compute(A, b);
+          break;
+        }
+        mfma_load<DOTS, W>(B, wlane, slane, b + step, b_hi);
+        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+        compute(A, b);
+        A = B;
+        b += step;
+      }
+    }
+    if constexpr (DOTS) continue;
+
+    // The W waves meet in LDS, then the tile is stored (or its split-K
+    // partial published and combined by the last split to arrive).
+    if (red_on_stage) __syncthreads();   // every wave is done reading the stage
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
+    __syncthreads();
+    finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+    __syncthreads();   // red is free again for the next tile
+  }
+}
+
+// Dynamic LDS bytes of a block-interleaved MFMA launch: the staged activation
+// of the largest split and the W waves' carries of one tile, the carries
+// either after the stage or (one tile per workgroup) on top of it.
+size_t mfma_stage_of(int rows, int act, int NB, int S) {
+  return mfma_stage_bytes(rows, act, (NB + S - 1) / S);
+}
+size_t mfma_red_of(int rows, int waves) { return (size_t)waves * rows * 64 * 4; }
 size_t mfma_lds_bytes_of(int rows, int act, int waves, int NB, int S) {
-  const size_t nblk = (size_t)((NB + S - 1) / S);
-  const size_t stage = nblk * rows * (act == kActBf16 ? 64 : 36);
-  const size_t red = (size_t)waves * rows * 64 * 4;
-  return stage > red ? stage : red;
+  // the smaller form; the launch takes the larger one when it fits and pays
+  const size_t st = mfma_stage_of(rows, act, NB, S), rd = mfma_red_of(rows, waves);
+  return st > rd ? st : rd;
+}
+
+// Dynamic LDS bytes of a column-group MFMA launch: the staged activation of
+// the largest split, plus the KW-way carries of a tile when KW > 1.
+size_t cols_lds_bytes_of(int rows, int act, int kslices, int NB, int S) {
+  const int nblk = (NB + S - 1) / S;
+  const size_t red = kslices > 1 ? (size_t)kslices * rows * 64 * 4 : 0;
+  return mfma_stage_bytes(rows, act, nblk) + red;
 }
 
 template <int MR, int ACT, bool DOTS, int W>
@@ -679,24 +933,87 @@ hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Workgroups of a launch that fit on the device at once (per CU, from the
+// runtime's occupancy query for this kernel and LDS size, times the CUs).
+template <typename Kern>
+int resident_workgroups(Kern kern, int threads, size_t lds) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  int dev = 0, cus = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  return per_cu * cus;
+}
+
+// Grants the dynamic LDS above the default 64 KiB (once per size increase).
+template <typename Kern>
+hipError_t grant_lds(Kern kern, size_t lds, size_t &granted) {
+  if (lds <= granted) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) granted = lds;
+  return e;
+}
+
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.T * a.split_k));
-  const size_t lds = mfma_lds_bytes_of(MR, ACT, W, a.NB, a.split_k);
+  const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
+  const size_t st = mfma_stage_of(MR, ACT, a.NB, a.split_k), rd = mfma_red_of(MR, W);
+  const size_t lds_alias = st > rd ? st : rd;   // carries on top of the stage
+  const size_t lds_sep = st + rd;               // carries after the stage
   auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W>;
-  // Above the default 64 KiB the kernel must be allowed more dynamic LDS;
-  // the largest size granted so far is remembered per instantiation.
   static size_t granted = 64 * 1024;
-  if (lds > granted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  int dev = 0, max_lds = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+      hipSuccess)
+    max_lds = 64 * 1024;
+  // One tile per workgroup when all of them fit on the device at once (the
+  // carries then reuse the stage); otherwise a persistent grid that stages
+  // once and walks tiles j, j+G, ... (carries apart), if that fits in LDS.
+  hipError_t e = grant_lds(kern, lds_alias, granted);
+  if (e != hipSuccess) return e;
+  int G = a.T, red_on_stage = 1;
+  size_t lds = lds_alias;
+  const int fit_alias = resident_workgroups(kern, 64 * W, lds_alias) / a.split_k;
+  if (fit_alias < a.T && lds_sep + 1024 <= (size_t)max_lds) {
+    e = grant_lds(kern, lds_sep, granted);
     if (e != hipSuccess) return e;
-    granted = lds;
+    int g = resident_workgroups(kern, 64 * W, lds_sep) / a.split_k;
+    if (g < 1) g = 1;
+    G = g < a.T ? g : a.T;
+    red_on_stage = 0;
+    lds = lds_sep;
   }
   (void)hipGetLastError();
-  kern<<<grid, dim3(64 * W), lds, stream>>>(a.x, a.wq, a.wsc, a.y, a.partial, a.counters,
-                                            a.dots, a.m, a.K, a.NB, a.Npad, a.split_k,
-                                            a.act_scale_off);
+  kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
+      a.split_k, G, nblk_max, red_on_stage, a.act_scale_off);
+  return hipGetLastError();
+}
+
+template <int MR, int ACT, bool DOTS, int KW, int P>
+hipError_t launch_cols(const GemvArgs &a, hipStream_t stream) {
+  constexpr int W = 4 * KW * P;
+  const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
+  const size_t lds = cols_lds_bytes_of(MR, ACT, KW, a.NB, a.split_k);
+  auto kern = gemv_mfma_cols_kernel<MR, ACT, DOTS, KW, P>;
+  static size_t granted = 64 * 1024;
+  hipError_t e = grant_lds(kern, lds, granted);
+  if (e != hipSuccess) return e;
+  // G workgroups per K split, each walking tiles j*P + slot, step G*P.
+  const int want = (a.T + P - 1) / P;
+  int G = resident_workgroups(kern, 64 * W, lds) / a.split_k;
+  if (G < 1) G = 1;
+  if (G > want) G = want;
+  (void)hipGetLastError();
+  kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
+      a.split_k, G, nblk_max, a.act_scale_off);
   return hipGetLastError();
 }
 
@@ -732,26 +1049,66 @@ Launcher pick_mfma_rows(int rows) {
 }
 
 template <int W>
-Launcher pick_w(int kernel, int rows, int act, bool dots) {
-  if (kernel == 0) {
-    if (act == kActBf16) return dots ? nullptr : pick_valu_rows<kActBf16, false, W>(rows);
-    if (act == kActQ8)
-      return dots ? pick_valu_rows<kActQ8, true, W>(rows) : pick_valu_rows<kActQ8, false, W>(rows);
-  } else if (kernel == 1) {
-    if (act == kActBf16) return dots ? nullptr : pick_mfma_rows<kActBf16, false, W>(rows);
-    if (act == kActQ8)
-      return dots ? pick_mfma_rows<kActQ8, true, W>(rows) : pick_mfma_rows<kActQ8, false, W>(rows);
-  }
+Launcher pick_mfma(int rows, int act, bool dots) {
+  if (act == kActBf16) return dots ? nullptr : pick_mfma_rows<kActBf16, false, W>(rows);
+  if (act == kActQ8)
+    return dots ? pick_mfma_rows<kActQ8, true, W>(rows) : pick_mfma_rows<kActQ8, false, W>(rows);
   return nullptr;
 }
 
-Launcher pick(int kernel, int rows, int act, bool dots, int waves) {
-  switch (waves) {
-    case 4: return pick_w<4>(kernel, rows, act, dots);
-    case 8: return pick_w<8>(kernel, rows, act, dots);
-    case 16: return pick_w<16>(kernel, rows, act, dots);
+// Column-group MFMA instantiations: (k-slices, tile slots) in {(1,1), (1,2),
+// (1,4), (2,1), (4,1)}, i.e. 4, 8 or 16 waves.
+template <int ACT, bool DOTS, int KW, int P>
+Launcher pick_cols_rows(int rows) {
+  switch (rows) {
+    case 16: return &launch_cols<16, ACT, DOTS, KW, P>;
+    case 32: return &launch_cols<32, ACT, DOTS, KW, P>;
     default: return nullptr;
   }
+}
+
+template <int KW, int P>
+Launcher pick_cols(int rows, int act, bool dots) {
+  if (act == kActBf16) return dots ? nullptr : pick_cols_rows<kActBf16, false, KW, P>(rows);
+  if (act == kActQ8)
+    return dots ? pick_cols_rows<kActQ8, true, KW, P>(rows)
+                : pick_cols_rows<kActQ8, false, KW, P>(rows);
+  return nullptr;
+}
+
+template <int W>
+Launcher pick_valu(int rows, int act, bool dots) {
+  if (act == kActBf16) return dots ? nullptr : pick_valu_rows<kActBf16, false, W>(rows);
+  if (act == kActQ8)
+    return dots ? pick_valu_rows<kActQ8, true, W>(rows) : pick_valu_rows<kActQ8, false, W>(rows);
+  return nullptr;
+}
+
+Launcher pick(int kernel, int rows, int act, bool dots, int waves, int kslices) {
+  if (kernel == 0) {
+    switch (waves) {
+      case 4: return pick_valu<4>(rows, act, dots);
+      case 8: return pick_valu<8>(rows, act, dots);
+      case 16: return pick_valu<16>(rows, act, dots);
+      default: return nullptr;
+    }
+  }
+  if (kernel == 1) {
+    switch (waves) {
+      case 4: return pick_mfma<4>(rows, act, dots);
+      case 8: return pick_mfma<8>(rows, act, dots);
+      case 16: return pick_mfma<16>(rows, act, dots);
+      default: return nullptr;
+    }
+  }
+  if (kernel == 2) {
+    if (waves == 4 && kslices == 1) return pick_cols<1, 1>(rows, act, dots);
+    if (waves == 8 && kslices == 1) return pick_cols<1, 2>(rows, act, dots);
+    if (waves == 16 && kslices == 1) return pick_cols<1, 4>(rows, act, dots);
+    if (waves == 8 && kslices == 2) return pick_cols<2, 1>(rows, act, dots);
+    if (waves == 16 && kslices == 4) return pick_cols<4, 1>(rows, act, dots);
+  }
+  return nullptr;
 }
 
 unsigned blocks_for(long long n) { return (unsigned)((n + 255) / 256); }
@@ -783,17 +1140,20 @@ hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
   return hipGetLastError();
 }
 
-size_t mfma_lds_bytes(int rows, int act, int waves, int NB, int split_k) {
-  return mfma_lds_bytes_of(rows, act, waves, NB, split_k);
+size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int NB,
+                      int split_k) {
+  if (kernel == 1) return mfma_lds_bytes_of(rows, act, waves, NB, split_k);
+  if (kernel == 2) return cols_lds_bytes_of(rows, act, kslices, NB, split_k);
+  return 0;
 }
 
-bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves) {
-  return pick(kernel, rows, act, write_dots, waves) != nullptr;
+bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves, int kslices) {
+  return pick(kernel, rows, act, write_dots, waves, kslices) != nullptr;
 }
 
-hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots,
-                       int waves, const GemvArgs &a, hipStream_t stream) {
-  Launcher f = pick(kernel, rows, act, write_dots, waves);
+hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots, int waves, int kslices,
+                       const GemvArgs &a, hipStream_t stream) {
+  Launcher f = pick(kernel, rows, act, write_dots, waves, kslices);
   if (!f) return hipErrorInvalidValue;
   return f(a, stream);
 }

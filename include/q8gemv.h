@@ -144,8 +144,8 @@ int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
 /*
  * q8_gemv_ws: q8_gemv with the caller's workspace (device memory of at least
  * q8_gemv_workspace_bytes(m, K, N, act_fmt) bytes, 16-byte aligned, or NULL
- * when that size is 0).  Its first 1 MiB holds split-K arrival counters at
- * fixed places (one per 64-column tile); they must be zero at the first use,
+ * when that size is 0).  Its first 4 MiB hold split-K arrival counters at
+ * fixed places (per 16-column group); they must be zero at the first use,
  * and every call leaves them at zero again, so a workspace zeroed once serves
  * calls of any shape.  Calls that share a workspace must be ordered (one
  * stream).  Q8_ERR_WORKSPACE when too small.
@@ -166,15 +166,21 @@ int q8_gemv_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
 /* ---- plans: what q8_gemv launches, and an explicit choice for tuning ----- */
 
 typedef enum {
-  Q8_KERNEL_VALU = 0, /* lane per column, activation broadcast from SGPRs    */
-  Q8_KERNEL_MFMA = 1  /* 16x16x32 matrix-core block dots, activation in LDS  */
+  Q8_KERNEL_VALU = 0,     /* lane per column, activation broadcast from SGPRs     */
+  Q8_KERNEL_MFMA = 1,     /* 16x16x32 matrix-core block dots, activation in LDS;
+                             waves split K, each over all 64 columns of a tile    */
+  Q8_KERNEL_MFMA_COLS = 2 /* as MFMA, but each wave owns one 16-column group      */
 } q8_kernel;
 
 typedef struct q8_plan {
   int32_t kernel;  /* q8_kernel                                                */
-  int32_t rows;    /* row count the kernel is built for (1,2,4,8,16,32) >= m   */
+  int32_t rows;    /* row count the kernel is built for: VALU 1,2,4,8,16,32;
+                      MFMA 16 or 32; >= m                                       */
   int32_t split_k; /* K splits across workgroups, 1..K/32                      */
   int32_t waves;   /* waves (64 lanes) per workgroup: 4, 8 or 16               */
+  int32_t kslices; /* MFMA_COLS: waves that split one 16-column group's K range
+                      (1, 2 or 4; waves = 4 * kslices * tiles side by side);
+                      other kernels: ignored (all their waves split K)         */
 } q8_plan;
 
 /* The plan q8_gemv would launch for this shape on the current device. */

@@ -64,7 +64,7 @@ def block_dots(xbuf, Wq, m, K, N, plan=None):
     return d.cpu().numpy()
 
 
-def plan(kernel, rows, split_k, waves=4):
+def plan(kernel, rows, split_k, waves=4, kslices=1):
     p = q8.q8_plan()
-    p.kernel, p.rows, p.split_k, p.waves = kernel, rows, split_k, waves
+    p.kernel, p.rows, p.split_k, p.waves, p.kslices = kernel, rows, split_k, waves, kslices
     return p

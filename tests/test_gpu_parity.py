@@ -163,15 +163,28 @@ def test_gemv_q8_small(m, K, N):
 # ------------------------------------------------------------------------------
 
 def _plans(m, NB):
+    """Every (kernel, rows, split, waves, kslices) combination worth trying;
+    the ones the library does not build are rejected with Q8_ERR_PLAN."""
     out = []
-    for kernel in (q8.Q8_KERNEL_VALU, q8.Q8_KERNEL_MFMA):
-        for rows in (1, 2, 4, 8, 16, 32):
-            if rows < m:
-                continue
-            for waves in (4, 8):
-                for split in sorted({1, 2, 3, 7, NB}):
-                    if split <= NB:
-                        out.append((kernel, rows, split, waves))
+    splits = sorted({1, 2, 3, 7, NB})
+    for rows in (1, 2, 4, 8, 16, 32):
+        if rows < m:
+            continue
+        for waves in (4, 8, 16):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_VALU, rows, split, waves, 1))
+    for rows in (16, 32):
+        if rows < m:
+            continue
+        for waves in (4, 8, 16):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_MFMA, rows, split, waves, 1))
+        for (waves, ks) in ((4, 1), (8, 1), (16, 1), (8, 2), (16, 4)):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_MFMA_COLS, rows, split, waves, ks))
     return out
 
 
@@ -190,8 +203,8 @@ def test_every_plan(act, m):
         ref, bnd = oracle.gemv_q8(xq, dx, q, s)
         Dref = oracle.block_dots(xq, q)
     ran = 0
-    for (kernel, rows, split, waves) in _plans(m, K // 32):
-        p = g.plan(kernel, rows, split, waves)
+    for (kernel, rows, split, waves, ks) in _plans(m, K // 32):
+        p = g.plan(kernel, rows, split, waves, ks)
         try:
             y = g.gemv(xin, Wq, Ws, m, K, N, act, p)
         except q8.Q8Error as e:

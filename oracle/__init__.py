@@ -29,14 +29,8 @@ _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        from . import build as _build  # compiles the C oracle with gcc
-        _build.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
     lib.q8o_set_threads.argtypes = [ctypes.c_int]
     lib.q8o_threads.restype = ctypes.c_int
     lib.q8o_quantize_exact.argtypes = [_p, _i64, _i64, _p, _p]
@@ -53,8 +47,28 @@ def _load():
     lib.q8o_view_rows.restype = _i64
     lib.q8o_fold_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64,
                                    ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
-    _lib = lib
     return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build  # compiles the C oracle with gcc
+        _build.build()
+    _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def swap_library(path: Optional[str]):
+    """Use the oracle library at `path` (None: the built one) for the calls
+    below; returns the previous handle.  For the mutation tests, which plant
+    a mistake in a copy of q8_oracle.c and check that the pins catch it."""
+    global _lib
+    prev = _lib
+    _lib = None if path is None else _configure(ctypes.CDLL(path))
+    return prev
 
 
 def _ptr(a: np.ndarray):

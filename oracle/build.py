@@ -11,15 +11,15 @@ SRC = os.path.join(HERE, "q8_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
+    tmp = out + ".tmp"
     cmd = ["gcc", "-std=c99", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-           "-fPIC", "-shared", "-Wall", "-Wextra", SRC, "-o", tmp, "-lm"]
+           "-fPIC", "-shared", "-Wall", "-Wextra", src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,0 +1,113 @@
+"""The oracle's pins are sharp: each test here plants one plausible mistake in a
+copy of q8_oracle.c (a dropped term, a wrong sign, an off-by-one index, a
+wrong rounding rule or constant), builds it on the CPU, runs every pin of
+test_oracle_pins.py against it, and requires at least one pin to fail.
+
+Every mutation keeps all memory accesses in bounds (indices are shifted
+modulo their extent), so a mutant can only compute wrong values.
+"""
+import inspect
+import itertools
+import os
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "q8_oracle.c")
+
+# (name, original text, replacement); each original occurs in q8_oracle.c.
+MUTANTS = [
+    ("bf16 product drops the last term of a block",
+     "          blk += t;\n", "          blk += (i == Q8O_BLOCK - 1) ? 0.0 : t;\n"),
+    ("bf16 product takes the next block's scale",
+     "double sv = (double)s[b * N + n];", "double sv = (double)s[((b + 1) % NB) * N + n];"),
+    ("bound loses the absolute value of the scale",
+     "bnd += fabs(sv) * blk_abs;", "bnd += sv * blk_abs;"),
+    ("bf16 product reads the next activation row",
+     "bf16_value(x[r * K + k]) * (double)q[k * N + n]",
+     "bf16_value(x[((r + 1) % m) * K + k]) * (double)q[k * N + n]"),
+    ("bf16 product reads the neighbouring weight column",
+     "bf16_value(x[r * K + k]) * (double)q[k * N + n]",
+     "bf16_value(x[r * K + k]) * (double)q[k * N + (n + 1) % N]"),
+    ("block dots drop the first term",
+     "          acc += (int64_t)xq[r * K + k] * (int64_t)q[k * N + n];\n",
+     "          if (i) acc += (int64_t)xq[r * K + k] * (int64_t)q[k * N + n];\n"),
+    ("int8 product takes the next block's activation scale",
+     "double scale = (double)dx[r * NB + b] * (double)s[b * N + n];",
+     "double scale = (double)dx[r * NB + (b + 1) % NB] * (double)s[b * N + n];"),
+    ("activation quantizer rounds ties to even",
+     "double rv = round_half_away((double)quot);", "double rv = rint((double)quot);"),
+    ("activation quantizer divides by 128",
+     "float d = (float)(amax / 127.0);", "float d = (float)(amax / 128.0);"),
+    ("exact encoder uses amax/126",
+     "double d = amax / 127.0;", "double d = amax / 126.0;"),
+    ("exact encoder accepts non-integer multiples",
+     "if (fabs(v - r) > 1e-9 || fabs(r) > 127.0 || r * d != wv) return 0;",
+     "if (fabs(r) > 127.0) return 0;"),
+    ("dequant takes the next block's scale",
+     "(double)s[(k / Q8O_BLOCK) * N + n]",
+     "(double)s[((k / Q8O_BLOCK + 1) % (K / Q8O_BLOCK)) * N + n]"),
+    ("view rows drop the K tail",
+     "return m * ((K + chunk - 1) / chunk) * Q8O_BLOCK;", "return m * (K / chunk) * Q8O_BLOCK;"),
+    ("byte model counts 2-byte scales",
+     "*weight = K * padded + 4 * (K / Q8O_BLOCK) * padded;",
+     "*weight = K * padded + 2 * (K / Q8O_BLOCK) * padded;"),
+]
+
+
+def _pin_calls():
+    """Every pin of test_oracle_pins.py as (name, callable) with its
+    parametrize cases expanded."""
+    calls = []
+    for name, fn in sorted(vars(pins).items()):
+        if not (name.startswith("test_") and inspect.isfunction(fn)):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            calls.append((name, fn, {}))
+            continue
+        grids = []
+        for mk in marks:
+            argnames = [a.strip() for a in mk.args[0].split(",")] if isinstance(mk.args[0], str) \
+                else list(mk.args[0])
+            cases = [v if len(argnames) > 1 else (v,) for v in mk.args[1]]
+            grids.append([dict(zip(argnames, c)) for c in cases])
+        for combo in itertools.product(*grids):
+            kw = {}
+            for d in combo:
+                kw.update(d)
+            calls.append((name, fn, kw))
+    return calls
+
+
+def _failures():
+    failed = []
+    for name, fn, kw in _pin_calls():
+        try:
+            fn(**kw)
+        except Exception:   # an assertion, or a wrong-shaped result
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_the_oracle():
+    assert _failures() == []
+
+
+@pytest.mark.parametrize("label,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, label, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mutated = src.replace(old, new, 1)
+    path = tmp_path / "q8_oracle_mutant.c"
+    path.write_text(mutated)
+    lib = oracle_build.build(src=str(path), out=str(tmp_path / "liboracle_mutant.so"))
+    prev = oracle.swap_library(lib)
+    try:
+        failed = _failures()
+    finally:
+        oracle._lib = prev
+    assert failed, f"no pin caught: {label}"

@@ -325,3 +325,21 @@ def test_view_rows():
     assert oracle.view_rows(16, 4096) == 16 * 4 * 32
     assert oracle.view_rows(2, 1056) == 2 * 2 * 32     # tail chunk gets a whole tile row
     assert oracle.view_rows(32, 5120) == 32 * 5 * 32
+
+
+@pytest.mark.parametrize("m,K,N,seed", [(2, 96, 7, 61), (3, 1056, 5, 62)])
+def test_brute_force_signed_scales(m, K, N, seed):
+    # the product's definition takes any scale; signs exercise the bound's |s|
+    x, q, s = inputs.random_case(m, K, N, seed)
+    sign = np.where(np.random.default_rng(seed).random(s.shape) < 0.5, -1.0, 1.0)
+    s = (s * sign).astype(np.float32)
+    y, b = oracle.gemv_bf16(x, q, s)
+    ref = xval(x) @ dense_w(q, s)
+    babs = np.abs(xval(x)) @ np.abs(dense_w(q, s))
+    assert np.all(np.abs(y - ref) <= 1e-13 * babs + 1e-300)
+    np.testing.assert_allclose(b, babs, rtol=1e-13)
+    xq, dx = oracle.quantize_act(x)
+    xd = xq.astype(np.float64) * np.repeat(dx.astype(np.float64), 32, axis=1)
+    y8, b8 = oracle.gemv_q8(xq, dx, q, s)
+    np.testing.assert_allclose(b8, np.abs(xd) @ np.abs(dense_w(q, s)), rtol=1e-13)
+    assert np.all(np.abs(y8 - xd @ dense_w(q, s)) <= 1e-13 * b8 + 1e-300)

@@ -37,6 +37,7 @@ def _configure(lib):
     lib.q8o_quantize_exact.restype = ctypes.c_int
     lib.q8o_dequant.argtypes = [_p, _p, _i64, _i64, _p]
     lib.q8o_quantize_act.argtypes = [_p, _i64, _i64, _p, _p]
+    lib.q8o_quantize_rows_f32.argtypes = [_p, _i64, _i64, _p, _p]
     lib.q8o_gemv_bf16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
     lib.q8o_gemv_bf16.restype = ctypes.c_int
     lib.q8o_block_dots.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i64, _p]
@@ -130,6 +131,19 @@ def quantize_act(x_bf16: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     dx = np.empty((m, K // BLOCK), np.float32)
     _load().q8o_quantize_act(_ptr(x), m, K, _ptr(xq), _ptr(dx))
     return xq, dx
+
+
+def quantize_rows_f32(z: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """The quantized form of an fp32 ``m x K`` array (a product's output as the
+    next projection reads it): int8 values and one fp32 scale per 32."""
+    z = _c(z, np.float32)
+    m, K = z.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    zq = np.empty((m, K), np.int8)
+    dz = np.empty((m, K // BLOCK), np.float32)
+    _load().q8o_quantize_rows_f32(_ptr(z), m, K, _ptr(zq), _ptr(dz))
+    return zq, dz
 
 
 def gemv_bf16(x_bf16: np.ndarray, q: np.ndarray, s: np.ndarray,

@@ -167,6 +167,42 @@ void q8o_quantize_act(const uint16_t *x, int64_t m, int64_t K, int8_t *xq,
   }
 }
 
+/*
+ * The same quantizer on fp32 input: the quantized form of a product's own
+ * output, as the next projection reads it (codegen_cuda/lane/plan.rs, enum
+ * Launch, field `quant` of a projection: its epilogue quantizes the output;
+ * const QBLOCK).  z is m x K fp32, row-major; the reading is the one above:
+ *   amax = max |z| over the block, d = fp32(amax / 127),
+ *   zq = clamp(round_half_away(fp32(z / d)), -127, 127); amax == 0: zeros.
+ */
+void q8o_quantize_rows_f32(const float *z, int64_t m, int64_t K, int8_t *zq,
+                           float *dz) {
+  const int64_t NB = K / Q8O_BLOCK;
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t b = 0; b < NB; ++b) {
+      const float *zb = z + r * K + b * Q8O_BLOCK;
+      double amax = 0.0;
+      for (int i = 0; i < Q8O_BLOCK; ++i) {
+        double a = fabs((double)zb[i]);
+        if (a > amax) amax = a;
+      }
+      float d = (float)(amax / 127.0);
+      dz[r * NB + b] = d;
+      for (int i = 0; i < Q8O_BLOCK; ++i) {
+        int v = 0;
+        if (d != 0.0f) {
+          float quot = (float)((double)zb[i] / (double)d);
+          double rv = round_half_away((double)quot);
+          if (rv > 127.0) rv = 127.0;
+          if (rv < -127.0) rv = -127.0;
+          v = (int)rv;
+        }
+        zq[r * K + b * Q8O_BLOCK + i] = (int8_t)v;
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* [Q8] module doc -- the product                                            */
 /* ------------------------------------------------------------------------ */

@@ -50,6 +50,12 @@ MUTANTS = [
     ("dequant takes the next block's scale",
      "(double)s[(k / Q8O_BLOCK) * N + n]",
      "(double)s[((k / Q8O_BLOCK + 1) % (K / Q8O_BLOCK)) * N + n]"),
+    ("output quantizer rounds ties to even",
+     "float quot = (float)((double)zb[i] / (double)d);\n          double rv = round_half_away((double)quot);",
+     "float quot = (float)((double)zb[i] / (double)d);\n          double rv = rint((double)quot);"),
+    ("output quantizer scale reads the neighbouring block",
+     "float d = (float)(amax / 127.0);\n      dz[r * NB + b] = d;",
+     "float d = (float)(amax / 127.0);\n      dz[r * NB + (b + 1) % NB] = d;"),
     ("view rows drop the K tail",
      "return m * ((K + chunk - 1) / chunk) * Q8O_BLOCK;", "return m * (K / chunk) * Q8O_BLOCK;"),
     ("byte model counts 2-byte scales",

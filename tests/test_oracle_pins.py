@@ -343,3 +343,40 @@ def test_brute_force_signed_scales(m, K, N, seed):
     y8, b8 = oracle.gemv_q8(xq, dx, q, s)
     np.testing.assert_allclose(b8, np.abs(xd) @ np.abs(dense_w(q, s)), rtol=1e-13)
     assert np.all(np.abs(y8 - xd @ dense_w(q, s)) <= 1e-13 * b8 + 1e-300)
+
+
+# --------------------------------------------------------------------------
+# plan.rs, enum Launch (`quant`): the output's quantized form, fp32 input
+# --------------------------------------------------------------------------
+
+def test_quantize_rows_f32_ties_and_exact_multiples():
+    d = 3.0 * 2.0 ** -10              # not a power of two; every value below is exact in fp32
+    row = np.zeros(96, np.float32)
+    row[:6] = np.array([127, 2.5, -2.5, 0.5, -1.5, -127], np.float64) * d
+    rng = np.random.default_rng(70)
+    j = rng.integers(-127, 128, size=32)
+    j[5] = 127
+    row[64:] = j * 2.0 ** -20
+    zq, dz = oracle.quantize_rows_f32(row[None, :])
+    np.testing.assert_array_equal(zq[0, :6], [127, 3, -3, 1, -2, -127])
+    assert dz[0, 0] == np.float32(d)
+    assert (zq[0, 32:64] == 0).all() and dz[0, 1] == 0
+    np.testing.assert_array_equal(zq[0, 64:], j)
+    assert dz[0, 2] == np.float32(2.0 ** -20)
+
+
+def test_quantize_rows_f32_invariants_and_agreement_on_bf16():
+    z = np.random.default_rng(71).standard_normal((5, 256)).astype(np.float32) * 3
+    zq, dz = oracle.quantize_rows_f32(z)
+    zb = z.reshape(5, 8, 32).astype(np.float64)
+    amax = np.abs(zb).max(axis=2)
+    assert np.all(np.abs(dz - amax / 127) <= np.spacing(dz).astype(np.float64) / 2)
+    err = np.abs(zb - zq.reshape(5, 8, 32) * dz[..., None].astype(np.float64))
+    assert np.all(err <= dz[..., None] * (0.5 + 127 * 2.0 ** -24))
+    assert np.abs(zq).max() == 127
+    # on bf16-representable input it is the activation quantizer
+    xb = inputs.f32_to_bf16_bits(z)
+    xq, dx = oracle.quantize_act(xb)
+    zq2, dz2 = oracle.quantize_rows_f32(inputs.bf16_bits_to_f32(xb))
+    np.testing.assert_array_equal(zq2, xq)
+    np.testing.assert_array_equal(dz2, dx)

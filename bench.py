@@ -20,7 +20,9 @@ algorithmic bytes (weight values + fp32 scales + activation + output) over
 the timed steps; `roofline` prices the product kernel's own average duration
 (HIP events around each launch, on the launch stream) against 8 TB/s;
 `cpu_baseline` times the CPU oracle on the same workload on this host;
-`by_rows` gives the same measurement at m = 16 and m = 32.
+`by_rows` gives the same measurement at m = 16 and m = 32; `fused_epilogue`
+times the product with bias, residual and quantized output beside the plain
+product, at m = 1 and m = 32.
 """
 import argparse
 import hashlib
@@ -216,6 +218,52 @@ def measure(w, steps, warmup, rotate=True):
     return res
 
 
+def measure_fused(w, steps, warmup, rotate=True):
+    """The product with its full epilogue (bias, residual add, y, and the
+    quantized output for the next projection), against the plain product on
+    the same buffers.  Returns per-launch times and the epilogue's extra bytes."""
+    import ctypes
+    import torch
+    st = Setup(w, rotate=rotate)
+    q8 = st.q8
+    from block_quantized_weight_02_amd import inputs
+    m, K, N = w.m, w.K, w.N
+    Npad = q8.q8_padded_cols(N)
+    bias = torch.from_numpy(inputs.gen_bias(N, seed=w.seed_w + 7)).to("cuda:0")
+    res = torch.from_numpy(inputs.gen_residual(m, Npad, seed=w.seed_w + 8)).to("cuda:0")
+    yq = torch.empty(q8.q8_act_bytes(m, Npad), dtype=torch.uint8, device="cuda:0")
+    ep = q8.make_epilogue(bias=bias, residual=res, y_q8=yq, write_y=True)
+    act = q8.Q8_ACT_BF16 if w.act == "bf16" else q8.Q8_ACT_Q8_0
+    plan = q8.q8_gemv_fused_default_plan(m, K, N, act, ep)
+    fused = q8.lib().q8_gemv_fused
+    epp = ctypes.byref(ep)
+    args = [a[:8] + (epp, a[8]) for a in st._gemv_args]
+
+    def call(i):
+        rc = fused(*args[i % st.copies])
+        if rc:
+            raise RuntimeError(q8.q8_last_error())
+
+    if w.act != "bf16":
+        st.step(0)   # the quantized activation the products read
+    for i in range(warmup):
+        call(i)
+        st.gemv_only(i)
+    plain_ms = time_loop(st.gemv_only, steps)
+    fused_ms = time_loop(call, steps)
+    extra = 4 * N + 4 * m * Npad + m * Npad + 4 * m * (Npad // 32)
+    b = algorithmic_bytes(w)["total"] + extra
+    del st
+    torch.cuda.empty_cache()
+    log(f"[bench] fused {w.name}: {fused_ms * 1e3:.2f} us vs plain {plain_ms * 1e3:.2f} us, "
+        f"plan={plan}")
+    return {"workload": w.name, "epilogue": "bias + residual + y + quantized y",
+            "fused_us": fused_ms * 1e3, "plain_us": plain_ms * 1e3,
+            "fused_bytes": b, "fused_gbs": b / (fused_ms * 1e-3) / 1e9,
+            "plan": {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
+                     "waves": plan.waves, "kslices": plan.kslices}}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU oracle (as it stands) on this host, on the same workload."""
     import oracle
@@ -263,6 +311,7 @@ def main():
     ap.add_argument("--workload", default=None, help="headline workload name (default: the m=1 decode shape)")
     ap.add_argument("--no-rows", action="store_true", help="skip the m=16 and m=32 rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
+    ap.add_argument("--no-fused", action="store_true", help="skip the fused-epilogue lines")
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy (for profiler counter calibration)")
@@ -300,6 +349,13 @@ def main():
             by_rows[f"m{inputs.WORKLOADS[other].m}"] = {
                 k: r[k] for k in ("workload", "us_per_step", "gbs", "pct_hbm_peak", "weights_per_s",
                                   "macs_per_s", "kernel_us_mean", "kernel_gbs", "kernel_pct_hbm_peak", "plan")}
+
+    fused = {}
+    if not args.no_fused:
+        for other in (name, "q8act_m32_k5120_n32000"):
+            r = measure_fused(inputs.WORKLOADS[other], max(200, args.steps // 4),
+                              max(20, args.warmup // 4), rotate=not args.no_rotate)
+            fused[f"m{inputs.WORKLOADS[other].m}"] = r
 
     traffic = traffic_from_profile(w.name)
     achieved = head["kernel_gbs"]
@@ -339,6 +395,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "by_rows": by_rows,
+        "fused_epilogue": fused,
     }
     print(json.dumps(out), flush=True)
 

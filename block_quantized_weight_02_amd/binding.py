@@ -44,6 +44,11 @@ class q8_plan(ctypes.Structure):
                 f"waves={self.waves}, kslices={self.kslices})")
 
 
+class q8_epilogue(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("y_q8", ctypes.c_void_p), ("write_y", ctypes.c_int32)]
+
+
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
 _p = ctypes.c_void_p
@@ -69,6 +74,13 @@ _SIGS = {
                                ctypes.POINTER(q8_plan), _p, _p, _sz]),
     "q8_gemv_block_dots_planned": (_int, [_p, _p, _p, _i64, _i64, _i64,
                                           ctypes.POINTER(q8_plan), _p]),
+    "q8_gemv_fused": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int,
+                             ctypes.POINTER(q8_epilogue), _p]),
+    "q8_gemv_planned_fused": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int,
+                                     ctypes.POINTER(q8_epilogue), ctypes.POINTER(q8_plan),
+                                     _p, _p, _sz]),
+    "q8_gemv_fused_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_epilogue),
+                                          ctypes.POINTER(q8_plan)]),
     "q8_status_string": (ctypes.c_char_p, [_int]),
     "q8_last_error": (ctypes.c_char_p, []),
     "q8_release_workspaces": (_int, []),
@@ -205,6 +217,37 @@ def q8_gemv_block_dots_planned(x_q8, W_q8, dots, m, K, N, plan: q8_plan,
                                stream=None) -> None:
     _check(lib().q8_gemv_block_dots_planned(_addr(x_q8), _addr(W_q8), _addr(dots),
                                             m, K, N, ctypes.byref(plan), _stream(stream)))
+
+
+def make_epilogue(bias=None, residual=None, y_q8=None, write_y=True) -> q8_epilogue:
+    """A ``q8_epilogue`` over device tensors (or raw addresses, or None)."""
+    return q8_epilogue(_addr(bias), _addr(residual), _addr(y_q8), 1 if write_y else 0)
+
+
+def _ep_ref(epilogue):
+    return None if epilogue is None else ctypes.byref(epilogue)
+
+
+def q8_gemv_fused(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, epilogue: q8_epilogue = None,
+                  stream=None) -> None:
+    _check(lib().q8_gemv_fused(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y),
+                               m, K, N, act_fmt, _ep_ref(epilogue), _stream(stream)))
+
+
+def q8_gemv_planned_fused(x, W_q8, W_q8_scale, y, m, K, N, act_fmt,
+                          epilogue: q8_epilogue, plan: q8_plan, stream=None,
+                          workspace=None, ws_bytes=0) -> None:
+    _check(lib().q8_gemv_planned_fused(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y),
+                                       m, K, N, act_fmt, _ep_ref(epilogue),
+                                       ctypes.byref(plan), _stream(stream),
+                                       _addr(workspace), ws_bytes))
+
+
+def q8_gemv_fused_default_plan(m, K, N, act_fmt, epilogue: q8_epilogue = None) -> q8_plan:
+    p = q8_plan()
+    _check(lib().q8_gemv_fused_default_plan(m, K, N, act_fmt, _ep_ref(epilogue),
+                                            ctypes.byref(p)))
+    return p
 
 
 def q8_status_string(status: int) -> str:

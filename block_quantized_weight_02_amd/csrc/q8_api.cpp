@@ -253,11 +253,27 @@ int library_workspace(hipStream_t stream, size_t need, void **out) {
   return Q8_OK;
 }
 
+// The epilogue check: pointers present and aligned, something written.
+int check_epilogue(const q8_epilogue *ep, const float *y) {
+  int st;
+  if (!ep) return check_ptr(y, "y");
+  if (ep->write_y && (st = check_ptr(y, "y"))) return st;
+  if (!ep->write_y && !ep->y_q8)
+    return fail(Q8_ERR_NULL, "epilogue writes neither y nor y_q8");
+  if (ep->bias && (st = check_ptr(ep->bias, "epilogue bias"))) return st;
+  if (ep->residual && (st = check_ptr(ep->residual, "epilogue residual"))) return st;
+  if (ep->y_q8 && (st = check_ptr(ep->y_q8, "epilogue y_q8"))) return st;
+  return Q8_OK;
+}
+
 int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
              float *y, int32_t *dots, int64_t m, int64_t K, int64_t N,
              int act_fmt, const q8_plan &plan, hipStream_t stream,
-             void *workspace, size_t ws_bytes) {
+             void *workspace, size_t ws_bytes, const q8_epilogue *ep = nullptr) {
   const bool write_dots = dots != nullptr;
+  if (ep && ep->y_q8 && plan.kernel == Q8_KERNEL_MFMA_COLS && plan.split_k < 2)
+    return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel quantizes its output in the split-K "
+                "finish: y_q8 needs split_k >= 2 (or the MFMA or VALU kernel)");
   int st = check_plan(&plan, m, K, act_fmt, write_dots);
   if (st) return st;
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
@@ -276,6 +292,18 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   a.act_scale_off = (unsigned)act_scales_offset(m, K);
   if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "activation too large");
+  a.ep.N = (int)N;
+  a.ep.write_y = 1;
+  if (ep) {
+    a.ep.bias = ep->bias;
+    a.ep.residual = ep->residual;
+    a.ep.write_y = ep->write_y != 0;
+    if (ep->y_q8) {
+      a.ep.yq = static_cast<int8_t *>(ep->y_q8);
+      a.ep.yq_scale = reinterpret_cast<float *>(static_cast<char *>(ep->y_q8) +
+                                                act_scales_offset(m, Npad));
+    }
+  }
   if (!write_dots && plan.split_k > 1) {
     const size_t need = plan_ws_bytes(plan, m, N);
     if (!workspace || ws_bytes < need)
@@ -296,7 +324,7 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
 
 int check_gemv_args(const void *x, const int8_t *W_q8, const float *W_q8_scale,
                     const void *out, const char *out_name, int64_t m, int64_t K,
-                    int64_t N, int act_fmt, bool need_scales) {
+                    int64_t N, int act_fmt, bool need_scales, bool need_out = true) {
   int st;
   if ((st = check_m(m))) return st;
   if ((st = check_kn(K, N))) return st;
@@ -304,8 +332,31 @@ int check_gemv_args(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   if ((st = check_ptr(x, "x"))) return st;
   if ((st = check_ptr(W_q8, "W_q8"))) return st;
   if (need_scales && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
-  if ((st = check_ptr(out, out_name))) return st;
+  if (need_out && (st = check_ptr(out, out_name))) return st;
   return Q8_OK;
+}
+
+// q8_gemv's plan, except that an output quantizer needs MFMA_COLS to split K
+// (its quantizer runs in the split-K finish); with one block only, MFMA.
+q8_plan fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
+                           const q8_epilogue *ep) {
+  q8_plan p = default_plan(m, K, N, act_fmt);
+  if (ep && ep->y_q8 && p.kernel == Q8_KERNEL_MFMA_COLS && p.split_k < 2 &&
+      K / Q8_BLOCK >= 2) {
+    p.split_k = 2;
+  } else if (ep && ep->y_q8 && p.kernel == Q8_KERNEL_MFMA_COLS && p.split_k < 2) {
+    p.kernel = Q8_KERNEL_MFMA;
+    p.waves = 16;
+    p.kslices = 1;
+    const int64_t NB = K / Q8_BLOCK;
+    const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
+    int64_t S = 1;
+    while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
+                                        (int)S) > budget)
+      ++S;
+    p.split_k = (int32_t)S;
+  }
+  return p;
 }
 
 }  // namespace
@@ -428,6 +479,42 @@ int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   if ((st = library_workspace(stream, need, &ws))) return st;
   return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, plan,
                   stream, ws, need);
+}
+
+int q8_gemv_fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
+                               const q8_epilogue *epilogue, q8_plan *plan) {
+  int st;
+  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  *plan = fused_default_plan(m, K, N, act_fmt, epilogue);
+  return ok();
+}
+
+int q8_gemv_planned_fused(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                          float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+                          const q8_epilogue *epilogue, const q8_plan *plan,
+                          hipStream_t stream, void *workspace, size_t ws_bytes) {
+  int st = check_gemv_args(x, W_q8, W_q8_scale, y, "y", m, K, N, act_fmt, true, false);
+  if (st) return st;
+  if ((st = check_epilogue(epilogue, y))) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  if (workspace && (st = check_ptr(workspace, "workspace"))) return st;
+  return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, *plan,
+                  stream, workspace, ws_bytes, epilogue);
+}
+
+int q8_gemv_fused(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                  float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+                  const q8_epilogue *epilogue, hipStream_t stream) {
+  int st = check_gemv_args(x, W_q8, W_q8_scale, y, "y", m, K, N, act_fmt, true, false);
+  if (st) return st;
+  if ((st = check_epilogue(epilogue, y))) return st;
+  const q8_plan plan = fused_default_plan(m, K, N, act_fmt, epilogue);
+  const size_t need = plan_ws_bytes(plan, m, N);
+  void *ws = nullptr;
+  if ((st = library_workspace(stream, need, &ws))) return st;
+  return run_gemv(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, plan,
+                  stream, ws, need, epilogue);
 }
 
 int q8_gemv_block_dots_planned(const void *x_q8, const int8_t *W_q8,

@@ -30,6 +30,19 @@ constexpr int kLayoutVersion = 2;
 
 enum Act { kActBf16 = 0, kActQ8 = 1 };
 
+// Fused epilogue of a product (all pointers optional, device memory):
+// z = x.W + bias + residual; y = z when write_y; yq/yq_scale = the quantized
+// form of z per 32 columns (int8 m x Npad, fp32 m x Npad/32).  Pad columns of
+// z are exactly 0.
+struct Epi {
+  const float *bias;
+  const float *residual;
+  int8_t *yq;
+  float *yq_scale;
+  int N;
+  int write_y;
+};
+
 // Everything a product launch needs; pointers are device pointers.
 struct GemvArgs {
   const void *x;          // bf16 m x K, or the quantized activation buffer
@@ -43,6 +56,7 @@ struct GemvArgs {
   int m, K, NB, Npad, T;
   int split_k;
   unsigned act_scale_off; // byte offset of the activation scales (Q8 mode)
+  Epi ep;                 // epilogue (plain product: N set, write_y 1, rest null)
 };
 
 // Launchers (q8_kernels.hip).  Return the launch's hipError_t.

@@ -134,6 +134,16 @@ unpack_kernel(const int8_t *__restrict__ wq, const float *__restrict__ wsc,
 // division (done in fp64, rounded once to fp32); ties round away from zero.
 // ---------------------------------------------------------------------------
 
+// The quantizer of an activation block (also the product's output
+// quantizer): scale from the block's amax, then one code per value.
+__device__ __forceinline__ float q8_scale_of(float amax) { return (float)((double)amax / 127.0); }
+
+__device__ __forceinline__ int8_t q8_code_of(float v, float d) {
+  if (d == 0.0f) return 0;
+  const float rq = roundf((float)((double)v / (double)d));   // ties away from zero
+  return (int8_t)(int)fminf(fmaxf(rq, -127.0f), 127.0f);
+}
+
 // One thread per element of the flattened m x K activation; a 32-lane group
 // is one Q8_0 block (K % 32 == 0 and 256 % 32 == 0).
 __global__ void __launch_bounds__(256)
@@ -145,16 +155,9 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ xq,
   float a = fabsf(v);
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
-  const float d = (float)((double)a / 127.0);
-  int qv = 0;
-  if (d != 0.0f) {
-    const float quot = (float)((double)v / (double)d);
-    float r = roundf(quot);  // half away from zero
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    qv = (int)r;
-  }
+  const float d = q8_scale_of(a);
   if (valid) {
-    xq[idx] = (int8_t)qv;
+    xq[idx] = q8_code_of(v, d);
     if ((idx & 31) == 0) dx[idx >> 5] = d;
   }
 }
@@ -167,6 +170,34 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ xq,
 __device__ __forceinline__ void split_range(int NB, int s, int S, int &b_lo, int &b_hi) {
   b_lo = (int)(((long long)NB * s) / S);
   b_hi = (int)(((long long)NB * (s + 1)) / S);
+}
+
+// z of output element (r, col) from its product value v: bias and residual
+// added in that order; pad columns are exactly 0.
+__device__ __forceinline__ float epi_value(const Epi &ep, int Npad, int r, size_t col, float v) {
+  if ((int)col >= ep.N) return 0.0f;
+  if (ep.bias) v += ep.bias[col];
+  if (ep.residual) v += ep.residual[(size_t)r * Npad + col];
+  return v;
+}
+
+// The final value v of output element (r, col): z = epi_value, y written and
+// z quantized per the epilogue.  The quantizer reduces over 32 consecutive
+// columns, so all 32 lanes of the caller's 32-lane half-wave must call
+// together, for one row and the 32 columns of one 32-column block (in lane
+// order).
+__device__ __forceinline__ void store_out(const Epi &ep, float *__restrict__ y, int Npad, int r,
+                                          size_t col, float v) {
+  v = epi_value(ep, Npad, r, col, v);
+  if (ep.write_y) y[(size_t)r * Npad + col] = v;
+  if (ep.yq) {
+    float a = fabsf(v);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
+    const float d = q8_scale_of(a);
+    ep.yq[(size_t)r * Npad + col] = q8_code_of(v, d);
+    if ((col & 31) == 0) ep.yq_scale[(size_t)r * (Npad / 32) + col / 32] = d;
+  }
 }
 
 // Epilogue of both kernels.  red[w][r][c] holds wave w's fp32 carry of row r,
@@ -183,7 +214,7 @@ template <int MR, int W>
 __device__ __forceinline__ void finish_tile(const float *red, float *__restrict__ y,
                                             float *__restrict__ partial,
                                             unsigned *__restrict__ counters, int m, int Npad,
-                                            int t, int s, int S) {
+                                            int t, int s, int S, const Epi &ep) {
   const size_t col0 = (size_t)t * kTile;
   for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
     const int r = idx >> 6, c = idx & 63;
@@ -192,7 +223,7 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[w * MR * 64 + idx];
       if (S == 1)
-        y[(size_t)r * Npad + col0 + c] = v;
+        store_out(ep, y, Npad, r, col0 + c, v);
       else
         __hip_atomic_store(&partial[((size_t)s * m + r) * Npad + col0 + c], v,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -218,7 +249,7 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
       for (int ss = 1; ss < S; ++ss)
         v += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col0 + c],
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      y[(size_t)r * Npad + col0 + c] = v;
+      store_out(ep, y, Npad, r, col0 + c, v);
     }
   }
   if (threadIdx.x == 0)
@@ -362,7 +393,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
                  float *__restrict__ partial, unsigned *__restrict__ counters,
                  int32_t *__restrict__ dots, int m, int K, int NB, int Npad,
-                 int S, unsigned act_scale_off) {
+                 int S, unsigned act_scale_off, Epi ep) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x / S;
@@ -413,7 +444,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int r = 0; r < MR; ++r) red[(wave * MR + r) * 64 + lane] = acc[r];
   __syncthreads();
-  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S, ep);
 }
 
 // ---------------------------------------------------------------------------
@@ -543,13 +574,141 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
   }
 }
 
-template <int MR, int ACT, bool DOTS, int KW, int P>
+// The epilogue's additions for the column-group kernel's layout, all loads
+// first: v[rg][e][h] is row row0 + 16rg + 4j + e, column col0 + 16h + i of
+// lane (i, j); H column groups (1 or 2).  Pad columns become 0.
+template <int RG, int H>
+__device__ __forceinline__ void epi_add_groups(const Epi &ep, int Npad, int m, int row0,
+                                               size_t col0, int lane, float (&v)[RG][4][H]) {
+  const int li = lane & 15, lj = lane >> 4;
+  float b[H], rv[RG][4][H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const size_t col = col0 + 16 * h + li;
+    b[h] = (ep.bias && (int)col < ep.N) ? ep.bias[col] : 0.0f;
+  }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const int r = row0 + rg * 16 + lj * 4 + e;
+        const size_t col = col0 + 16 * h + li;
+        rv[rg][e][h] = (ep.residual && r < m) ? ep.residual[(size_t)r * Npad + col] : 0.0f;
+      }
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        const size_t col = col0 + 16 * h + li;
+        float z = v[rg][e][h];
+        if (ep.bias) z += b[h];
+        if (ep.residual) z += rv[rg][e][h];
+        v[rg][e][h] = ((int)col < ep.N) ? z : 0.0f;
+      }
+}
+
+// Final values of one 16-column group (column col0 + i of lane (i, j)):
+// epilogue additions, then y.
+template <int RG>
+__device__ __forceinline__ void cols_store_group(const Epi &ep, float *__restrict__ y, int Npad,
+                                                 int m, size_t col0, int lane,
+                                                 float (&v)[RG][4][1]) {
+  const int li = lane & 15, lj = lane >> 4;
+  if (ep.bias || ep.residual || (int)(col0 + 16) > ep.N)
+    epi_add_groups<RG, 1>(ep, Npad, m, 0, col0, lane, v);
+  if (!ep.write_y) return;
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rg * 16 + lj * 4 + e;
+      if (r < m) y[(size_t)r * Npad + col0 + li] = v[rg][e][0];
+    }
+}
+
+// Split-K finish of a column-group pair with the output quantizer (the
+// column-group kernel, S >= 2): the caller has published its partial carries
+// (visible at system scope).  The last of the pair's 2S arrivals sums both
+// groups' partials in split order, applies the epilogue and quantizes the
+// pair's 32 columns: lane (i, j) holds column col0 + 16h + i of rows
+// 16rg + 4j + e, so a row's 32 values are 2 per lane across 16 lanes.
+template <int RG>
+__device__ __forceinline__ void cols_finish_pair(const Epi &ep, float *__restrict__ y,
+                                                 const float *__restrict__ partial,
+                                                 unsigned *__restrict__ counter, int m, int Npad,
+                                                 int S, size_t col0, int lane) {
+  unsigned prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (unsigned)(2 * S - 1)) return;
+  const int li = lane & 15, lj = lane >> 4;
+  // The row stride as an opaque value, so the addresses below are formed
+  // here and not hoisted into registers held across the caller's main loop.
+  asm volatile("" : "+s"(Npad));
+  // One 16-row group at a time (a rolled loop keeps the registers of this
+  // path below the main loop's).  v[0][e][h]: row row0 + 4j + e, column
+  // col0 + 16h + i.  Splits are summed in order 0..S-1, each split's eight
+  // loads issued together.
+#pragma unroll 1
+  for (int rg = 0; rg < RG; ++rg) {
+    const int row0 = rg * 16;
+    if (row0 >= m) break;
+    float v[1][4][2];
+    const float *p = partial + (size_t)(row0 + lj * 4) * Npad + col0 + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        v[0][e][h] = (row0 + lj * 4 + e < m)
+                         ? __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_SYSTEM)
+                         : 0.0f;
+    for (int ss = 1; ss < S; ++ss) {
+      p += (size_t)m * Npad;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (row0 + lj * 4 + e < m)
+            v[0][e][h] += __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    // every bias and residual value is read before any y is written (the
+    // residual may be y itself)
+    epi_add_groups<1, 2>(ep, Npad, m, row0, col0, lane, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + lj * 4 + e;
+      if (r >= m) continue;   // uniform over the 16 lanes of one j
+      const float z[2] = {v[0][e][0], v[0][e][1]};
+      if (ep.write_y) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) y[(size_t)r * Npad + col0 + 16 * h + li] = z[h];
+      }
+      float amax = fmaxf(fabsf(z[0]), fabsf(z[1]));
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+      const float d = q8_scale_of(amax);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ep.yq[(size_t)r * Npad + col0 + 16 * h + li] = q8_code_of(z[h], d);
+      if (li == 0) ep.yq_scale[(size_t)r * (Npad / 32) + col0 / 32] = d;
+    }
+  }
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <int MR, int ACT, bool DOTS, int KW, int P, bool QO>
 __global__ void __launch_bounds__(256 * KW * P)
 gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                       const float *__restrict__ wsc, float *__restrict__ y,
                       float *__restrict__ partial, unsigned *__restrict__ counters,
                       int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
-                      int S, int G, int nblk_max, unsigned act_scale_off) {
+                      int S, int G, int nblk_max, unsigned act_scale_off, Epi ep) {
   constexpr int W = 4 * KW * P;
   constexpr int RG = MR / 16;
   constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;   // one row of one block in LDS
@@ -684,13 +843,12 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
     // same protocol as finish_tile, per 16-column group, inside one wave).
     const size_t col = (size_t)t * kTile + col_in_tile;
     if (S == 1) {
+      float v[RG][4][1];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rg * 16 + lj * 4 + e;
-          if (r < m) y[(size_t)r * Npad + col] = acc[rg][e];
-        }
+        for (int e = 0; e < 4; ++e) v[rg][e][0] = acc[rg][e];
+      cols_store_group<RG>(ep, y, Npad, m, col - li, lane, v);
       continue;
     }
 #pragma unroll
@@ -705,26 +863,39 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (QO) {
+      // Output quantizer: its 32-column blocks span the column-group pair
+      // (g & 2, g | 1), so the pair shares one counter and the last of its 2S
+      // arrivals finishes all 32 columns.
+      cols_finish_pair<RG>(ep, y, partial, counters + (size_t)t * 4 + (g & 2), m, Npad, S,
+                           (size_t)t * kTile + 16 * (g & 2), lane);
+      continue;
+    }
     unsigned prev = 0;
     if (lane == 0)
       prev = __hip_atomic_fetch_add(&counters[(size_t)t * 4 + g], 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_SYSTEM);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != (unsigned)(S - 1)) continue;
+    {
+      float v[RG][4][1];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
+      for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rg * 16 + lj * 4 + e;
-        if (r < m) {
-          float v = __hip_atomic_load(&partial[(size_t)r * Npad + col], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_SYSTEM);
-          for (int ss = 1; ss < S; ++ss)
-            v += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-          y[(size_t)r * Npad + col] = v;
+        for (int e = 0; e < 4; ++e) {
+          const int r = rg * 16 + lj * 4 + e;
+          float a = 0.0f;
+          if (r < m) {
+            a = __hip_atomic_load(&partial[(size_t)r * Npad + col], __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_SYSTEM);
+            for (int ss = 1; ss < S; ++ss)
+              a += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
+          v[rg][e][0] = a;
         }
-      }
+      cols_store_group<RG>(ep, y, Npad, m, col - li, lane, v);
+    }
     if (lane == 0)
       __hip_atomic_store(&counters[(size_t)t * 4 + g], 0u, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
@@ -766,7 +937,8 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
                  float *__restrict__ partial, unsigned *__restrict__ counters,
                  int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
-                 int S, int G, int nblk_max, int red_on_stage, unsigned act_scale_off) {
+                 int S, int G, int nblk_max, int red_on_stage, unsigned act_scale_off,
+                 Epi ep) {
   constexpr int RG = MR / 16;
   constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -898,7 +1070,7 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         for (int e = 0; e < 4; ++e)
           red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
     __syncthreads();
-    finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S);
+    finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S, ep);
     __syncthreads();   // red is free again for the next tile
   }
 }
@@ -929,7 +1101,7 @@ hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.T * a.split_k));
   gemv_valu_kernel<MR, ACT, DOTS, W><<<grid, dim3(64 * W), 0, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB,
-      a.Npad, a.split_k, a.act_scale_off);
+      a.Npad, a.split_k, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
@@ -992,16 +1164,16 @@ hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
-      a.split_k, G, nblk_max, red_on_stage, a.act_scale_off);
+      a.split_k, G, nblk_max, red_on_stage, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
-template <int MR, int ACT, bool DOTS, int KW, int P>
-hipError_t launch_cols(const GemvArgs &a, hipStream_t stream) {
+template <int MR, int ACT, bool DOTS, int KW, int P, bool QO>
+hipError_t launch_cols_k(const GemvArgs &a, hipStream_t stream) {
   constexpr int W = 4 * KW * P;
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t lds = cols_lds_bytes_of(MR, ACT, KW, a.NB, a.split_k);
-  auto kern = gemv_mfma_cols_kernel<MR, ACT, DOTS, KW, P>;
+  auto kern = gemv_mfma_cols_kernel<MR, ACT, DOTS, KW, P, QO>;
   static size_t granted = 64 * 1024;
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
@@ -1013,8 +1185,18 @@ hipError_t launch_cols(const GemvArgs &a, hipStream_t stream) {
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
-      a.split_k, G, nblk_max, a.act_scale_off);
+      a.split_k, G, nblk_max, a.act_scale_off, a.ep);
   return hipGetLastError();
+}
+
+// The column-group kernel is built twice: with the output quantizer in its
+// split-K finish, and without (whose registers it would otherwise share).
+template <int MR, int ACT, bool DOTS, int KW, int P>
+hipError_t launch_cols(const GemvArgs &a, hipStream_t stream) {
+  if constexpr (!DOTS) {
+    if (a.ep.yq) return launch_cols_k<MR, ACT, DOTS, KW, P, true>(a, stream);
+  }
+  return launch_cols_k<MR, ACT, DOTS, KW, P, false>(a, stream);
 }
 
 using Launcher = hipError_t (*)(const GemvArgs &, hipStream_t);

@@ -120,3 +120,46 @@ def random_case(m: int, K: int, N: int, seed: int, q_law: str = "uniform",
                 x_law: str = "normal"):
     """A small seeded case of any shape: ``(x, q, s)``."""
     return gen_x(m, K, seed, x_law), gen_q(K, N, seed, q_law), gen_scales(K, N, seed)
+
+
+def gen_bias(N: int, seed: int) -> np.ndarray:
+    """fp32 bias of N columns, N(0, 1)."""
+    return _rng(seed, 4).standard_normal(N, dtype=np.float32)
+
+
+def gen_residual(m: int, Npad: int, seed: int) -> np.ndarray:
+    """fp32 residual stream, ``m x Npad``, N(0, 8^2) (the order of a
+    projection's output at K = 4096 with the weights above)."""
+    return (_rng(seed, 5).standard_normal((m, Npad), dtype=np.float32) * 8).astype(np.float32)
+
+
+def exact_case(m: int, K: int, N: int, seed: int):
+    """A case whose product, bias and residual are exact in fp32 whatever the
+    summation order, so every rounding-free path gives bit-identical outputs:
+    ``(x, q, s, bias, residual)``.
+
+    * x: integers in [-127, 127], each 32-block holding +-127 (so its int8
+      quantized form is x itself with scale 1), stored as bf16 bits;
+    * q: integers in [-15, 15]; columns 32..63 zero (a zero output block);
+    * s: powers of two 2^-4 .. 2^-1;
+    * bias, residual: multiples of 2^-4 below 2^10 in magnitude, zero on
+      columns 32..63.
+    With K <= 512 every partial sum is a multiple of 2^-4 below 2^20.
+    """
+    if K > 512:
+        raise ValueError("exact_case needs K <= 512")
+    r = _rng(seed, 6)
+    x = r.integers(-126, 127, size=(m, K)).astype(np.float32)
+    pos = r.integers(0, BLOCK, size=(m, K // BLOCK))
+    sign = np.where(r.random((m, K // BLOCK)) < 0.5, -1.0, 1.0)
+    for b in range(K // BLOCK):
+        x[np.arange(m), b * BLOCK + pos[:, b]] = 127.0 * sign[:, b]
+    q = r.integers(-15, 16, size=(K, N)).astype(np.int8)
+    q[:, 32:64] = 0
+    s = np.ldexp(1.0, r.integers(-4, 0, size=(K // BLOCK, N))).astype(np.float32)
+    Npad = (N + 63) // 64 * 64
+    bias = (r.integers(-2 ** 13, 2 ** 13, size=N) / 16.0).astype(np.float32)
+    res = (r.integers(-2 ** 13, 2 ** 13, size=(m, Npad)) / 16.0).astype(np.float32)
+    bias[32:64] = 0
+    res[:, 32:64] = 0
+    return f32_to_bf16_bits(x), q, s, bias, res

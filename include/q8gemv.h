@@ -199,6 +199,56 @@ int q8_gemv_block_dots_planned(const void *x_q8, const int8_t *W_q8,
                                int32_t *dots, int64_t m, int64_t K, int64_t N,
                                const q8_plan *plan, hipStream_t stream);
 
+/* ---- fused epilogues ------------------------------------------------------- */
+
+/*
+ * What a product does with its fp32 carry before it leaves the kernel: the
+ * bias and output-quantize options of codegen_cuda/lane/plan.rs, enum Launch,
+ * variant Gemv (fields `bias`, `quant`), and the residual add that the same
+ * enum folds into a projection's epilogue (its `gemv_norm_epilogue` note).
+ * Per output element (r, n), n < N:
+ *     z[r, n] = (x . W)[r, n] + bias[n] + residual[r, n]
+ * (each term only when its pointer is given, added in that order in fp32);
+ * pad columns N <= n < N_pad get z = 0.  Then
+ *   - y[r, n] = z[r, n] when write_y (else y is not touched and may be NULL);
+ *   - when y_q8 is given, z's quantized form per row and per 32 columns, by
+ *     exactly the q8_quantize_act arithmetic applied to fp32 z, in the
+ *     activation layout of q8_act_bytes(m, N_pad): int8 m x N_pad at y_q8,
+ *     fp32 scales m x N_pad/32 at y_q8 + q8_act_scales_offset(m, N_pad) --
+ *     the input of the next product with act_fmt Q8_ACT_Q8_0 and K = N_pad.
+ * All pointers are device pointers, 16-byte aligned.  bias holds N fp32;
+ * residual is m x N_pad fp32 like y and may be y itself (each element is read
+ * before it is written, by the same thread).  The MFMA_COLS kernel quantizes
+ * its output in the split-K finish (a 32-column block spans two of its
+ * waves): a plan naming it with y_q8 set and split_k < 2 is Q8_ERR_PLAN (the
+ * fused default plan then splits K in two, or with K = 32 takes the MFMA
+ * kernel).
+ */
+typedef struct q8_epilogue {
+  const float *bias;     /* N fp32, or NULL                                   */
+  const float *residual; /* m x N_pad fp32, or NULL; may equal y             */
+  void *y_q8;            /* q8_act_bytes(m, N_pad) bytes, or NULL             */
+  int32_t write_y;       /* nonzero: write y                                  */
+} q8_epilogue;
+
+/* q8_gemv with an epilogue (NULL epilogue: plain q8_gemv).  Library workspace
+ * as q8_gemv.  Q8_ERR_NULL when nothing would be written. */
+int q8_gemv_fused(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                  float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+                  const q8_epilogue *epilogue /* host pointer */, hipStream_t stream);
+
+/* q8_gemv_planned with an epilogue. */
+int q8_gemv_planned_fused(const void *x, const int8_t *W_q8,
+                          const float *W_q8_scale, float *y, int64_t m,
+                          int64_t K, int64_t N, int act_fmt,
+                          const q8_epilogue *epilogue, const q8_plan *plan,
+                          hipStream_t stream, void *workspace, size_t ws_bytes);
+
+/* The plan q8_gemv_fused launches (differs from q8_gemv_default_plan only
+ * when the epilogue quantizes the output). */
+int q8_gemv_fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
+                               const q8_epilogue *epilogue, q8_plan *plan);
+
 /* ---- errors and resources ------------------------------------------------ */
 
 /* Static name of a status code. */

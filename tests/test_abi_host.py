@@ -116,3 +116,43 @@ def test_status_strings():
     assert q8.q8_status_string(0) == "Q8_OK"
     assert q8.q8_status_string(5) == "Q8_ERR_WORKSPACE"
     assert q8.q8_status_string(99) == "Q8_ERR_UNKNOWN"
+
+
+def test_fused_epilogue_validation():
+    ep = q8.make_epilogue(write_y=False)           # writes nothing
+    msg = expect(3, q8.q8_gemv_fused, A, A, A, A, 1, 64, 8, 0, ep, S0)
+    assert "neither" in msg
+    ep = q8.make_epilogue(bias=A + 4)
+    expect(4, q8.q8_gemv_fused, A, A, A, A, 1, 64, 8, 0, ep, S0)
+    ep = q8.make_epilogue(residual=A + 8)
+    expect(4, q8.q8_gemv_fused, A, A, A, A, 1, 64, 8, 0, ep, S0)
+    ep = q8.make_epilogue(y_q8=A + 2, write_y=False)
+    expect(4, q8.q8_gemv_fused, A, A, A, None, 1, 64, 8, 0, ep, S0)
+    expect(3, q8.q8_gemv_fused, A, A, A, None, 1, 64, 8, 0, q8.make_epilogue(), S0)
+    expect(3, q8.q8_gemv_fused, A, A, A, None, 1, 64, 8, 0, None, S0)
+    expect(1, q8.q8_gemv_fused, A, A, A, A, 33, 64, 8, 0, None, S0)
+    # the column-group kernel quantizes its output only in the split-K finish
+    p = q8.q8_plan()
+    p.kernel, p.rows, p.split_k, p.waves, p.kslices = 2, 32, 1, 16, 1
+    ep = q8.make_epilogue(y_q8=A)
+    msg = expect(7, q8.q8_gemv_planned_fused, A, A, A, A, 32, 64, 8, 1, ep, p, S0, None, 0)
+    assert "split_k >= 2" in msg
+
+
+def _t(p):
+    return (p.kernel, p.rows, p.split_k, p.waves, p.kslices)
+
+
+def test_fused_default_plan_for_quantized_output():
+    ep_q = q8.make_epilogue(y_q8=A)
+    for (m, K, N) in ((32, 5120, 32000), (32, 2176, 200), (32, 32, 40), (16, 4096, 64)):
+        plain = q8.q8_gemv_default_plan(m, K, N, 1)
+        fused = q8.q8_gemv_fused_default_plan(m, K, N, 1, ep_q)
+        if plain.kernel != q8.Q8_KERNEL_MFMA_COLS or plain.split_k >= 2:
+            assert _t(fused) == _t(plain)
+        elif K >= 64:
+            assert _t(fused) == _t(plain)[:2] + (2,) + _t(plain)[3:]
+        else:
+            assert fused.kernel == q8.Q8_KERNEL_MFMA
+        same = q8.q8_gemv_fused_default_plan(m, K, N, 1, q8.make_epilogue(bias=A))
+        assert _t(same) == _t(plain)

@@ -44,6 +44,7 @@ def _configure(lib):
     lib.q8o_block_dots.restype = ctypes.c_int
     lib.q8o_gemv_q8.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
     lib.q8o_gemv_q8.restype = ctypes.c_int
+    lib.q8o_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p]
     lib.q8o_view_rows.argtypes = [_i64, _i64]
     lib.q8o_view_rows.restype = _i64
     lib.q8o_fold_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64,
@@ -204,6 +205,46 @@ def gemv_q8(xq: np.ndarray, dx: np.ndarray, q: np.ndarray, s: np.ndarray,
     if rc:
         raise ValueError("bad shape")
     return y, b
+
+
+def swiglu(g: np.ndarray, u: np.ndarray, bg: Optional[np.ndarray] = None,
+           bu: Optional[np.ndarray] = None) -> np.ndarray:
+    """``silu(g + bg) * (u + bu)`` elementwise, fp64 (plan.rs, Launch::GemvGlu)."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    if g.shape != u.shape or g.ndim != 2:
+        raise ValueError("g and u must be equal m x n arrays")
+    m, n = g.shape
+    b1 = None if bg is None else _c(bg, np.float32)
+    b2 = None if bu is None else _c(bu, np.float32)
+    for b in (b1, b2):
+        if b is not None and b.shape != (n,):
+            raise ValueError("bias must have n values")
+    out = np.empty((m, n), np.float64)
+    _load().q8o_swiglu(_ptr(g), _ptr(u), None if b1 is None else _ptr(b1),
+                       None if b2 is None else _ptr(b2), m, n, _ptr(out))
+    return out
+
+
+def gemv_glu_bf16(x_bf16, qg, sg, qu, su, bg=None, bu=None, cols=None):
+    """The gated pair on bf16 activations: ``(out, g, u, bound_g, bound_u)``,
+    fp64 over the listed columns (biases indexed by column)."""
+    g, bnd_g = gemv_bf16(x_bf16, qg, sg, cols)
+    u, bnd_u = gemv_bf16(x_bf16, qu, su, cols)
+    c = slice(None) if cols is None else np.asarray(cols)
+    out = swiglu(g, u, None if bg is None else np.asarray(bg)[c],
+                 None if bu is None else np.asarray(bu)[c])
+    return out, g, u, bnd_g, bnd_u
+
+
+def gemv_glu_q8(xq, dx, qg, sg, qu, su, bg=None, bu=None, cols=None):
+    """The gated pair on int8 activations, as gemv_glu_bf16."""
+    g, bnd_g = gemv_q8(xq, dx, qg, sg, cols)
+    u, bnd_u = gemv_q8(xq, dx, qu, su, cols)
+    c = slice(None) if cols is None else np.asarray(cols)
+    out = swiglu(g, u, None if bg is None else np.asarray(bg)[c],
+                 None if bu is None else np.asarray(bu)[c])
+    return out, g, u, bnd_g, bnd_u
 
 
 def view_rows(m: int, K: int) -> int:

@@ -20,6 +20,9 @@
  *   [LANE] logicaffeine_compile/codegen_cuda/lane/plan.rs
  *          - const QBLOCK / struct Buffer field `quantized`: an activation's
  *            quantized form is int8 values and one scale per 32 values.
+ *          - enum Launch, variant GemvGlu: two projections of one activation
+ *            through a gate, act(x.wg + bg) * (x.wu + bu), SwiGLU (the SiLU
+ *            gate) when no activation is named.
  *
  * Precision: every product below is formed in fp64 (bf16 x int8 x fp32 has
  * 8 + 8 + 24 significant bits <= 53, so each term is exact), integer block
@@ -320,6 +323,23 @@ int q8o_gemv_q8(const int8_t *xq, const float *dx, const int8_t *q,
 /* Rows of the K/32 x 32 view of an m-row activation: K/32 for one row; for a
  * batch, each row's K chunks of 1024 a whole 32-row tile apiece (the tail's
  * unused rows included). */
+/*
+ * [LANE] GemvGlu, SwiGLU form, elementwise over m x n values in fp64:
+ *   out = silu(g + bg) * (u + bu),  silu(v) = v / (1 + exp(-v)) = v * sigmoid(v)
+ * g, u: the two products (fp64, m x n); bg, bu: fp32 biases of n, or NULL.
+ */
+void q8o_swiglu(const double *g, const double *u, const float *bg,
+                const float *bu, int64_t m, int64_t n, double *out) {
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t j = 0; j < n; ++j) {
+      double gv = g[r * n + j] + (bg ? (double)bg[j] : 0.0);
+      double uv = u[r * n + j] + (bu ? (double)bu[j] : 0.0);
+      double sig = 1.0 / (1.0 + exp(-gv));
+      out[r * n + j] = gv * sig * uv;
+    }
+  }
+}
+
 int64_t q8o_view_rows(int64_t m, int64_t K) {
   if (m == 1) return K / Q8O_BLOCK;
   const int64_t chunk = Q8O_BLOCK * Q8O_BLOCK;

@@ -56,6 +56,13 @@ MUTANTS = [
     ("output quantizer scale reads the neighbouring block",
      "float d = (float)(amax / 127.0);\n      dz[r * NB + b] = d;",
      "float d = (float)(amax / 127.0);\n      dz[r * NB + (b + 1) % NB] = d;"),
+    ("SiLU takes sigmoid of +v",
+     "double sig = 1.0 / (1.0 + exp(-gv));", "double sig = 1.0 / (1.0 + exp(gv));"),
+    ("gated pair drops the up factor",
+     "out[r * n + j] = gv * sig * uv;", "out[r * n + j] = gv * sig;"),
+    ("gated pair adds the gate bias to the up product",
+     "double uv = u[r * n + j] + (bu ? (double)bu[j] : 0.0);",
+     "double uv = u[r * n + j] + (bg ? (double)bg[j] : 0.0);"),
     ("view rows drop the K tail",
      "return m * ((K + chunk - 1) / chunk) * Q8O_BLOCK;", "return m * (K / chunk) * Q8O_BLOCK;"),
     ("byte model counts 2-byte scales",

@@ -6,6 +6,7 @@ reduces to a numpy library routine, or brute force on tiny inputs.  The
 oracle's own loops are C (q8_oracle.c); every independent path here is numpy.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -380,3 +381,70 @@ def test_quantize_rows_f32_invariants_and_agreement_on_bf16():
     zq2, dz2 = oracle.quantize_rows_f32(inputs.bf16_bits_to_f32(xb))
     np.testing.assert_array_equal(zq2, xq)
     np.testing.assert_array_equal(dz2, dx)
+
+
+# --------------------------------------------------------------------------
+# plan.rs, enum Launch, variant GemvGlu: silu(x.wg + bg) * (x.wu + bu)
+# --------------------------------------------------------------------------
+
+def _silu_tanh(v):
+    # the same function through sigmoid(v) = (1 + tanh(v / 2)) / 2 for v >= 0
+    # and sigmoid(v) = e^v / (1 + e^v) below (no cancellation there)
+    v = np.asarray(v, np.float64)
+    ev = np.exp(np.minimum(v, 0.0))
+    return np.where(v >= 0, v * (1.0 + np.tanh(v / 2.0)) / 2.0, v * ev / (1.0 + ev))
+
+
+def test_swiglu_closed_forms():
+    g = np.array([[0.0, 1.0, 2.0, -2.0, 10.0, -10.0, 40.0, -40.0, 0.5, -3.25]])
+    u = np.ones_like(g)
+    out = oracle.swiglu(g, u)
+    np.testing.assert_allclose(out, _silu_tanh(g), rtol=4e-15, atol=1e-300)
+    assert out[0, 0] == 0.0
+    # silu(v) - silu(-v) = v
+    gm = -g
+    np.testing.assert_allclose(out - oracle.swiglu(gm, u), g, rtol=1e-14, atol=1e-15)
+    # 2 * sigmoid(2) = 1 + tanh(1)
+    assert abs(out[0, 2] - (1.0 + math.tanh(1.0))) < 1e-15
+
+
+def test_swiglu_linear_in_up_and_biases():
+    rng = np.random.default_rng(80)
+    g = rng.standard_normal((3, 7)) * 4
+    u1 = rng.standard_normal((3, 7))
+    u2 = rng.standard_normal((3, 7))
+    a = oracle.swiglu(g, u1) + oracle.swiglu(g, u2)
+    np.testing.assert_allclose(oracle.swiglu(g, u1 + u2), a, rtol=1e-13, atol=1e-14)
+    assert np.all(oracle.swiglu(g, np.zeros_like(g)) == 0)
+    bg = rng.standard_normal(7).astype(np.float32)
+    bu = rng.standard_normal(7).astype(np.float32)
+    np.testing.assert_array_equal(oracle.swiglu(g, u1, bg, bu),
+                                  oracle.swiglu(g + bg.astype(np.float64),
+                                                u1 + bu.astype(np.float64)))
+    np.testing.assert_allclose(oracle.swiglu(g, u1, bg, None),
+                               _silu_tanh(g + bg.astype(np.float64)) * u1, rtol=1e-13)
+
+
+@pytest.mark.parametrize("m,K,N,seed", [(1, 64, 5, 81), (3, 96, 9, 82)])
+def test_gated_pair_brute_force(m, K, N, seed):
+    x, qg, sg = inputs.random_case(m, K, N, seed=seed)
+    _, qu, su = inputs.random_case(m, K, N, seed=seed + 100)
+    bg = inputs.gen_bias(N, seed)
+    bu = inputs.gen_bias(N, seed + 1)
+    xd = inputs.bf16_bits_to_f32(x).astype(np.float64)
+    g = xd @ dense_w(qg, sg) + bg.astype(np.float64)
+    u = xd @ dense_w(qu, su) + bu.astype(np.float64)
+    out, gg, uu, bnd_g, bnd_u = oracle.gemv_glu_bf16(x, qg, sg, qu, su, bg, bu)
+    np.testing.assert_allclose(out, _silu_tanh(g) * u, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(bnd_g, np.abs(xd) @ np.abs(dense_w(qg, sg)), rtol=1e-13)
+    # int8 form
+    xq, dx = oracle.quantize_act(x)
+    xqd = (xq.reshape(m, K // 32, 32) * dx[..., None].astype(np.float64)).reshape(m, K)
+    out8, _, _, _, _ = oracle.gemv_glu_q8(xq, dx, qg, sg, qu, su, bg, bu)
+    g8 = xqd @ dense_w(qg, sg) + bg.astype(np.float64)
+    u8 = xqd @ dense_w(qu, su) + bu.astype(np.float64)
+    np.testing.assert_allclose(out8, _silu_tanh(g8) * u8, rtol=1e-11, atol=1e-12)
+    # a column subset is the same columns of the whole
+    cols = [N - 1, 0, 2]
+    sub, _, _, _, _ = oracle.gemv_glu_bf16(x, qg, sg, qu, su, bg, bu, cols)
+    np.testing.assert_array_equal(sub, out[:, cols])

@@ -22,7 +22,8 @@ the timed steps; `roofline` prices the product kernel's own average duration
 `cpu_baseline` times the CPU oracle on the same workload on this host;
 `by_rows` gives the same measurement at m = 16 and m = 32; `fused_epilogue`
 times the product with bias, residual and quantized output beside the plain
-product, at m = 1 and m = 32.
+product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
+one launch) beside two plain products, at m = 1 and m = 16.
 """
 import argparse
 import hashlib
@@ -264,6 +265,52 @@ def measure_fused(w, steps, warmup, rotate=True):
                      "waves": plan.waves, "kslices": plan.kslices}}
 
 
+def measure_glu(w, steps, warmup, rotate=True):
+    """The gated pair (gate and up products of one activation through SiLU,
+    one launch) against two plain products of the same weights."""
+    import ctypes
+    import torch
+    st = Setup(w, rotate=rotate)
+    q8 = st.q8
+    m, K, N = w.m, w.K, w.N
+    act = q8.Q8_ACT_BF16 if w.act == "bf16" else q8.Q8_ACT_Q8_0
+    glu = q8.lib().q8_gemv_glu
+    plan = q8.q8_gemv_glu_default_plan(m, K, N, act)
+    xin = st.x.data_ptr() if w.act == "bf16" else st.xq.data_ptr()
+    sp = st.stream.cuda_stream
+    n = st.copies
+    args = [(xin, st.W[i][0].data_ptr(), st.W[i][1].data_ptr(), st.W[(i + 1) % n][0].data_ptr(),
+             st.W[(i + 1) % n][1].data_ptr(), st.y.data_ptr(), m, K, N, act, None, sp)
+            for i in range(n)]
+
+    def call(i):
+        rc = glu(*args[i % n])
+        if rc:
+            raise RuntimeError(q8.q8_last_error())
+
+    def two_products(i):
+        st.gemv_only(i)
+        st.gemv_only(i + 1)
+
+    if w.act != "bf16":
+        st.step(0)
+    for i in range(warmup):
+        call(i)
+        two_products(i)
+    two_ms = time_loop(two_products, steps)
+    glu_ms = time_loop(call, steps)
+    b = algorithmic_bytes(w)
+    pair_bytes = 2 * (b["values"] + b["scales"]) + b["x"] + b["y"]
+    del st
+    torch.cuda.empty_cache()
+    log(f"[bench] gated pair {w.name}: {glu_ms * 1e3:.2f} us vs two products {two_ms * 1e3:.2f} us, "
+        f"plan={plan}")
+    return {"workload": w.name, "glu_us": glu_ms * 1e3, "two_products_us": two_ms * 1e3,
+            "bytes": pair_bytes, "glu_gbs": pair_bytes / (glu_ms * 1e-3) / 1e9,
+            "plan": {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
+                     "waves": plan.waves, "kslices": plan.kslices}}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU oracle (as it stands) on this host, on the same workload."""
     import oracle
@@ -356,6 +403,10 @@ def main():
             r = measure_fused(inputs.WORKLOADS[other], max(200, args.steps // 4),
                               max(20, args.warmup // 4), rotate=not args.no_rotate)
             fused[f"m{inputs.WORKLOADS[other].m}"] = r
+        for other in (name, "batch16_k4096_n14336"):
+            r = measure_glu(inputs.WORKLOADS[other], max(200, args.steps // 4),
+                            max(20, args.warmup // 4), rotate=not args.no_rotate)
+            fused[f"glu_m{inputs.WORKLOADS[other].m}"] = r
 
     traffic = traffic_from_profile(w.name)
     achieved = head["kernel_gbs"]

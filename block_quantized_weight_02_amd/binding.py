@@ -49,6 +49,11 @@ class q8_epilogue(ctypes.Structure):
                 ("y_q8", ctypes.c_void_p), ("write_y", ctypes.c_int32)]
 
 
+class q8_glu_epilogue(ctypes.Structure):
+    _fields_ = [("bias_g", ctypes.c_void_p), ("bias_u", ctypes.c_void_p),
+                ("y_q8", ctypes.c_void_p), ("write_y", ctypes.c_int32)]
+
+
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
 _p = ctypes.c_void_p
@@ -81,6 +86,13 @@ _SIGS = {
                                      _p, _p, _sz]),
     "q8_gemv_fused_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_epilogue),
                                           ctypes.POINTER(q8_plan)]),
+    "q8_gemv_glu": (_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _int,
+                           ctypes.POINTER(q8_glu_epilogue), _p]),
+    "q8_gemv_glu_planned": (_int, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _int,
+                                   ctypes.POINTER(q8_glu_epilogue), ctypes.POINTER(q8_plan),
+                                   _p, _p, _sz]),
+    "q8_gemv_glu_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_plan)]),
+    "q8_glu_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), _i64, _i64, _i64]),
     "q8_status_string": (ctypes.c_char_p, [_int]),
     "q8_last_error": (ctypes.c_char_p, []),
     "q8_release_workspaces": (_int, []),
@@ -248,6 +260,37 @@ def q8_gemv_fused_default_plan(m, K, N, act_fmt, epilogue: q8_epilogue = None) -
     _check(lib().q8_gemv_fused_default_plan(m, K, N, act_fmt, _ep_ref(epilogue),
                                             ctypes.byref(p)))
     return p
+
+
+def make_glu_epilogue(bias_g=None, bias_u=None, y_q8=None, write_y=True) -> q8_glu_epilogue:
+    """A ``q8_glu_epilogue`` over device tensors (or raw addresses, or None)."""
+    return q8_glu_epilogue(_addr(bias_g), _addr(bias_u), _addr(y_q8), 1 if write_y else 0)
+
+
+def q8_gemv_glu(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt,
+                epilogue: q8_glu_epilogue = None, stream=None) -> None:
+    _check(lib().q8_gemv_glu(_addr(x), _addr(Wg_q8), _addr(Wg_q8_scale), _addr(Wu_q8),
+                             _addr(Wu_q8_scale), _addr(y), m, K, N, act_fmt,
+                             _ep_ref(epilogue), _stream(stream)))
+
+
+def q8_gemv_glu_planned(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt,
+                        epilogue: q8_glu_epilogue, plan: q8_plan, stream=None,
+                        workspace=None, ws_bytes=0) -> None:
+    _check(lib().q8_gemv_glu_planned(_addr(x), _addr(Wg_q8), _addr(Wg_q8_scale),
+                                     _addr(Wu_q8), _addr(Wu_q8_scale), _addr(y), m, K, N,
+                                     act_fmt, _ep_ref(epilogue), ctypes.byref(plan),
+                                     _stream(stream), _addr(workspace), ws_bytes))
+
+
+def q8_gemv_glu_default_plan(m, K, N, act_fmt) -> q8_plan:
+    p = q8_plan()
+    _check(lib().q8_gemv_glu_default_plan(m, K, N, act_fmt, ctypes.byref(p)))
+    return p
+
+
+def q8_glu_workspace_bytes(plan: q8_plan, m, K, N) -> int:
+    return int(lib().q8_glu_workspace_bytes(ctypes.byref(plan), m, K, N))
 
 
 def q8_status_string(status: int) -> str:

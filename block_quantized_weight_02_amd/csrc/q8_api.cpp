@@ -205,10 +205,12 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
 // zeroed once stays valid for calls of any shape.
 constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4 * 4;
 
-size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N) {
-  if (p.split_k <= 1) return 0;
+// nw: weights whose carries meet in the workspace (2 for the gated pair,
+// whose two weights' carries always meet there).
+size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N, int nw = 1) {
+  if (p.split_k * nw <= 1) return 0;
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
-  return kCounterBytes + (size_t)round_up((int64_t)p.split_k * m * Npad * 4, 256);
+  return kCounterBytes + (size_t)round_up((int64_t)nw * p.split_k * m * Npad * 4, 256);
 }
 
 // ---- library-owned workspaces, per (device, stream) ---------------------------
@@ -266,12 +268,21 @@ int check_epilogue(const q8_epilogue *ep, const float *y) {
   return Q8_OK;
 }
 
+// The gated pair's second weight and its bias.
+struct PairArgs {
+  const int8_t *wq_u;
+  const float *wsc_u;
+  const float *bias_u;
+};
+
 int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
              float *y, int32_t *dots, int64_t m, int64_t K, int64_t N,
              int act_fmt, const q8_plan &plan, hipStream_t stream,
-             void *workspace, size_t ws_bytes, const q8_epilogue *ep = nullptr) {
+             void *workspace, size_t ws_bytes, const q8_epilogue *ep = nullptr,
+             const PairArgs *pair = nullptr) {
   const bool write_dots = dots != nullptr;
-  if (ep && ep->y_q8 && plan.kernel == Q8_KERNEL_MFMA_COLS && plan.split_k < 2)
+  const int nw = pair ? 2 : 1;
+  if (ep && ep->y_q8 && plan.kernel == Q8_KERNEL_MFMA_COLS && plan.split_k * nw < 2)
     return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel quantizes its output in the split-K "
                 "finish: y_q8 needs split_k >= 2 (or the MFMA or VALU kernel)");
   int st = check_plan(&plan, m, K, act_fmt, write_dots);
@@ -294,6 +305,12 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
     return fail(Q8_ERR_SHAPE, "activation too large");
   a.ep.N = (int)N;
   a.ep.write_y = 1;
+  a.ep.nw = nw;
+  if (pair) {
+    a.ep.wq_u = pair->wq_u;
+    a.ep.wsc_u = pair->wsc_u;
+    a.ep.bias_u = pair->bias_u;
+  }
   if (ep) {
     a.ep.bias = ep->bias;
     a.ep.residual = ep->residual;
@@ -304,8 +321,8 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
                                                 act_scales_offset(m, Npad));
     }
   }
-  if (!write_dots && plan.split_k > 1) {
-    const size_t need = plan_ws_bytes(plan, m, N);
+  if (!write_dots && plan.split_k * nw > 1) {
+    const size_t need = plan_ws_bytes(plan, m, N, nw);
     if (!workspace || ws_bytes < need)
       return fail(Q8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                   workspace ? ws_bytes : (size_t)0, need);
@@ -357,6 +374,58 @@ q8_plan fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
     p.split_k = (int32_t)S;
   }
   return p;
+}
+
+// The gated pair's plan: q8_gemv's for the pair's 2*N_pad columns of work
+// (the VALU split count counts both weights' tiles); its two weights always
+// meet in the workspace, so the column-group kernel's quantizer needs no
+// K split.
+// With the VALU kernel, the pair's twice as many workgroups take 4 waves
+// each once they outnumber the CUs, which keeps the waves streaming at once
+// (and the bytes each wave streams) those of the single product (measured on
+// MI355X, m = 1, K = 4096, N = 14336: 4 waves 23.0 us, 8 waves 24.2 us).
+q8_plan glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
+  q8_plan p = default_plan(m, K, 2 * round_up(N, Q8_TILE_COLS), act_fmt);
+  const int64_t units = 2 * round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
+  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > device_facts().cus) p.waves = 4;
+  return p;
+}
+
+int check_glu_epilogue(const q8_glu_epilogue *ep, const float *y) {
+  int st;
+  if (!ep) return check_ptr(y, "y");
+  if (ep->write_y && (st = check_ptr(y, "y"))) return st;
+  if (!ep->write_y && !ep->y_q8)
+    return fail(Q8_ERR_NULL, "epilogue writes neither y nor y_q8");
+  if (ep->bias_g && (st = check_ptr(ep->bias_g, "epilogue bias_g"))) return st;
+  if (ep->bias_u && (st = check_ptr(ep->bias_u, "epilogue bias_u"))) return st;
+  if (ep->y_q8 && (st = check_ptr(ep->y_q8, "epilogue y_q8"))) return st;
+  return Q8_OK;
+}
+
+int run_glu(const void *x, const int8_t *Wg, const float *Wg_s, const int8_t *Wu,
+            const float *Wu_s, float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+            const q8_glu_epilogue *gep, const q8_plan &plan, hipStream_t stream,
+            void *workspace, size_t ws_bytes) {
+  q8_epilogue ep{};
+  ep.write_y = 1;
+  if (gep) {
+    ep.bias = gep->bias_g;
+    ep.y_q8 = gep->y_q8;
+    ep.write_y = gep->write_y;
+  }
+  const PairArgs pair{Wu, Wu_s, gep ? gep->bias_u : nullptr};
+  return run_gemv(x, Wg, Wg_s, y, nullptr, m, K, N, act_fmt, plan, stream, workspace, ws_bytes,
+                  &ep, &pair);
+}
+
+int check_glu_args(const void *x, const int8_t *Wg, const float *Wg_s, const int8_t *Wu,
+                   const float *Wu_s, const float *y, int64_t m, int64_t K, int64_t N,
+                   int act_fmt, const q8_glu_epilogue *ep) {
+  int st = check_gemv_args(x, Wg, Wg_s, y, "y", m, K, N, act_fmt, true, false);
+  if (st) return st;
+  if ((st = check_ptr(Wu, "Wu_q8")) || (st = check_ptr(Wu_s, "Wu_q8_scale"))) return st;
+  return check_glu_epilogue(ep, y);
 }
 
 }  // namespace
@@ -536,6 +605,47 @@ int q8_gemv_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
   const q8_plan plan = default_plan(m, K, N, Q8_ACT_Q8_0);
   return run_gemv(x_q8, W_q8, nullptr, nullptr, dots, m, K, N, Q8_ACT_Q8_0,
                   plan, stream, nullptr, 0);
+}
+
+size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K, int64_t N) {
+  if (!plan || check_m(m) || check_kn(K, N)) return 0;
+  return plan_ws_bytes(*plan, m, N, 2);
+}
+
+int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, q8_plan *plan) {
+  int st;
+  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  *plan = glu_default_plan(m, K, N, act_fmt);
+  return ok();
+}
+
+int q8_gemv_glu_planned(const void *x, const int8_t *Wg_q8, const float *Wg_q8_scale,
+                        const int8_t *Wu_q8, const float *Wu_q8_scale, float *y, int64_t m,
+                        int64_t K, int64_t N, int act_fmt, const q8_glu_epilogue *epilogue,
+                        const q8_plan *plan, hipStream_t stream, void *workspace,
+                        size_t ws_bytes) {
+  int st = check_glu_args(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt,
+                          epilogue);
+  if (st) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  if (workspace && (st = check_ptr(workspace, "workspace"))) return st;
+  return run_glu(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt, epilogue,
+                 *plan, stream, workspace, ws_bytes);
+}
+
+int q8_gemv_glu(const void *x, const int8_t *Wg_q8, const float *Wg_q8_scale,
+                const int8_t *Wu_q8, const float *Wu_q8_scale, float *y, int64_t m, int64_t K,
+                int64_t N, int act_fmt, const q8_glu_epilogue *epilogue, hipStream_t stream) {
+  int st = check_glu_args(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt,
+                          epilogue);
+  if (st) return st;
+  const q8_plan plan = glu_default_plan(m, K, N, act_fmt);
+  const size_t need = plan_ws_bytes(plan, m, N, 2);
+  void *ws = nullptr;
+  if ((st = library_workspace(stream, need, &ws))) return st;
+  return run_glu(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt, epilogue, plan,
+                 stream, ws, need);
 }
 
 const char *q8_status_string(int status) {

@@ -30,10 +30,12 @@ constexpr int kLayoutVersion = 2;
 
 enum Act { kActBf16 = 0, kActQ8 = 1 };
 
-// Fused epilogue of a product (all pointers optional, device memory):
-// z = x.W + bias + residual; y = z when write_y; yq/yq_scale = the quantized
-// form of z per 32 columns (int8 m x Npad, fp32 m x Npad/32).  Pad columns of
-// z are exactly 0.
+// Fused epilogue of a product (all pointers optional, device memory).
+// nw == 1: z = x.W + bias + residual.
+// nw == 2 (gated pair): z = silu(x.W + bias) * (x.W_u + bias_u), W_u the
+//   second packed weight (wq_u, wsc_u) of the same shape.
+// Then y = z when write_y; yq/yq_scale = the quantized form of z per 32
+// columns (int8 m x Npad, fp32 m x Npad/32).  Pad columns of z are exactly 0.
 struct Epi {
   const float *bias;
   const float *residual;
@@ -41,6 +43,10 @@ struct Epi {
   float *yq_scale;
   int N;
   int write_y;
+  int nw;                // weights: 1, or 2 for the gated pair
+  const int8_t *wq_u;    // the pair's second weight
+  const float *wsc_u;
+  const float *bias_u;
 };
 
 // Everything a product launch needs; pointers are device pointers.
@@ -56,7 +62,9 @@ struct GemvArgs {
   int m, K, NB, Npad, T;
   int split_k;
   unsigned act_scale_off; // byte offset of the activation scales (Q8 mode)
-  Epi ep;                 // epilogue (plain product: N set, write_y 1, rest null)
+  Epi ep;                 // epilogue (plain product: N set, write_y 1, nw 1, rest null)
+  // Output tiles times weights: the launch's units of work.
+  int tiles() const { return T * ep.nw; }
 };
 
 // Launchers (q8_kernels.hip).  Return the launch's hipError_t.

@@ -63,6 +63,25 @@ __device__ __forceinline__ float4 ld_stream16f(const float4 *p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer loads of the weight stream: a wave-uniform resource (base address
+// and byte extent, in scalar registers), a 32-bit lane offset and a uniform
+// block offset -- no per-lane 64-bit addresses, and loads outside the extent
+// return zero.  Cache policy: non-temporal, as above.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr int kBufNT = 2;                 // the nt cache-policy bit
+constexpr int kBufFlags = 0x00020000;     // resource word 3: 32-bit data format
+__device__ __forceinline__ buf_t make_buf(const void *base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kBufFlags);
+}
+__device__ __forceinline__ uint4 buf_ld16(buf_t r, unsigned voff, unsigned soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufNT);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float buf_ld4f(buf_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kBufNT));
+}
+
 // The four signed bytes of a dword as fp32 (exact); byte j is k = 4d + j.
 __device__ __forceinline__ void i8x4_to_f32(uint32_t v, float *f) {
   f[0] = (float)(int8_t)(v);
@@ -172,64 +191,88 @@ __device__ __forceinline__ void split_range(int NB, int s, int S, int &b_lo, int
   b_hi = (int)(((long long)NB * (s + 1)) / S);
 }
 
-// z of output element (r, col) from its product value v: bias and residual
-// added in that order; pad columns are exactly 0.
-__device__ __forceinline__ float epi_value(const Epi &ep, int Npad, int r, size_t col, float v) {
+// SiLU, g * sigmoid(g), in fp32 (the gate of the pages' GemvGlu launch).
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// z of output element (r, col) from its sums over K: vg of the (first) weight
+// and, for the gated pair, vu of the second.  Single weight: bias and
+// residual added in that order; pair: silu(vg + bias) * (vu + bias_u).  Pad
+// columns are exactly 0.
+template <bool PAIR>
+__device__ __forceinline__ float final_value(const Epi &ep, int Npad, int r, size_t col, float vg,
+                                             float vu) {
   if ((int)col >= ep.N) return 0.0f;
-  if (ep.bias) v += ep.bias[col];
-  if (ep.residual) v += ep.residual[(size_t)r * Npad + col];
-  return v;
+  if constexpr (PAIR) {
+    if (ep.bias) vg += ep.bias[col];
+    if (ep.bias_u) vu += ep.bias_u[col];
+    return silu(vg) * vu;
+  }
+  if (ep.bias) vg += ep.bias[col];
+  if (ep.residual) vg += ep.residual[(size_t)r * Npad + col];
+  return vg;
 }
 
-// The final value v of output element (r, col): z = epi_value, y written and
-// z quantized per the epilogue.  The quantizer reduces over 32 consecutive
-// columns, so all 32 lanes of the caller's 32-lane half-wave must call
-// together, for one row and the 32 columns of one 32-column block (in lane
-// order).
-__device__ __forceinline__ void store_out(const Epi &ep, float *__restrict__ y, int Npad, int r,
-                                          size_t col, float v) {
-  v = epi_value(ep, Npad, r, col, v);
-  if (ep.write_y) y[(size_t)r * Npad + col] = v;
+// Stores z of output element (r, col): y when asked, and its quantized form.
+// The quantizer reduces over 32 consecutive columns, so all 32 lanes of the
+// caller's 32-lane half-wave must call together, for one row and the 32
+// columns of one 32-column block (in lane order).
+__device__ __forceinline__ void store_final(const Epi &ep, float *__restrict__ y, int Npad, int r,
+                                            size_t col, float z) {
+  if (ep.write_y) y[(size_t)r * Npad + col] = z;
   if (ep.yq) {
-    float a = fabsf(v);
+    float a = fabsf(z);
 #pragma unroll
     for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
     const float d = q8_scale_of(a);
-    ep.yq[(size_t)r * Npad + col] = q8_code_of(v, d);
+    ep.yq[(size_t)r * Npad + col] = q8_code_of(z, d);
     if ((col & 31) == 0) ep.yq_scale[(size_t)r * (Npad / 32) + col / 32] = d;
   }
 }
 
+// Sum over the S splits of weight `wsel`'s partial carries of (r, col), in
+// split order.  partial holds [wsel][split][row][column] carries.
+__device__ __forceinline__ float sum_partials(const float *__restrict__ partial, int m, int Npad,
+                                              int S, int wsel, int r, size_t col) {
+  const float *p = partial + ((size_t)wsel * S * m + r) * Npad + col;
+  float v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int ss = 1; ss < S; ++ss)
+    v += __hip_atomic_load(p + (size_t)ss * m * Npad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return v;
+}
+
 // Epilogue of both kernels.  red[w][r][c] holds wave w's fp32 carry of row r,
-// tile column c (already written, __syncthreads() done by the caller).  Sums
-// the waves in order; with S == 1 stores y, otherwise publishes the partial
-// and the last workgroup of the tile sums the S partials in split order.
+// tile column c of weight `wsel` (already written, __syncthreads() done by the
+// caller).  Sums the waves in order; when the tile's value is complete here
+// (one split, one weight) stores it, otherwise publishes the partial and the
+// last of the tile's S * nw arrivals sums each weight's S partials in split
+// order and stores the final values.
 //
 // The partial carries are written and read with system-scope relaxed atomic
 // stores and loads, which go through to memory and bypass the per-XCD L2s;
 // their completion is awaited (s_waitcnt 0) before the arrival count is
 // bumped.  So no workgroup needs a device-scope fence, whose L2 write-back and
 // invalidate would cost each workgroup microseconds.
-template <int MR, int W>
+template <int MR, int W, bool PAIR>
 __device__ __forceinline__ void finish_tile(const float *red, float *__restrict__ y,
                                             float *__restrict__ partial,
                                             unsigned *__restrict__ counters, int m, int Npad,
-                                            int t, int s, int S, const Epi &ep) {
+                                            int t, int s, int S, int wsel, const Epi &ep) {
   const size_t col0 = (size_t)t * kTile;
+  const int arrivals = S * (PAIR ? 2 : 1);
   for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
     const int r = idx >> 6, c = idx & 63;
     if (r < m) {
       float v = red[idx];
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[w * MR * 64 + idx];
-      if (S == 1)
-        store_out(ep, y, Npad, r, col0 + c, v);
+      if (arrivals == 1)
+        store_final(ep, y, Npad, r, col0 + c, final_value<PAIR>(ep, Npad, r, col0 + c, v, 0.0f));
       else
-        __hip_atomic_store(&partial[((size_t)s * m + r) * Npad + col0 + c], v,
+        __hip_atomic_store(&partial[(((size_t)wsel * S + s) * m + r) * Npad + col0 + c], v,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
-  if (S == 1) return;
+  if (arrivals == 1) return;
   __shared__ int is_last;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
@@ -237,19 +280,16 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
   __syncthreads();
   if (threadIdx.x == 0)
     is_last = (__hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(S - 1))
+                                      __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(arrivals - 1))
                   ? 1 : 0;
   __syncthreads();
   if (!is_last) return;
   for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
     const int r = idx >> 6, c = idx & 63;
     if (r < m) {
-      float v = __hip_atomic_load(&partial[(size_t)r * Npad + col0 + c], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_SYSTEM);
-      for (int ss = 1; ss < S; ++ss)
-        v += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col0 + c],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      store_out(ep, y, Npad, r, col0 + c, v);
+      const float vg = sum_partials(partial, m, Npad, S, 0, r, col0 + c);
+      const float vu = PAIR ? sum_partials(partial, m, Npad, S, 1, r, col0 + c) : 0.0f;
+      store_final(ep, y, Npad, r, col0 + c, final_value<PAIR>(ep, Npad, r, col0 + c, vg, vu));
     }
   }
   if (threadIdx.x == 0)
@@ -284,20 +324,41 @@ struct ValuStage {
   float dx[kUnroll][ValuX<MR, ACT>::kRows];
 };
 
+// Where a wave's tile comes from: buffer resources (wave-uniform base and
+// extent in scalar registers; a loop with them needs no per-lane 64-bit
+// addresses), or plain pointers where the scalar registers are taken by the
+// prefetched activation (two rows).  lw, ls: the lane's byte offsets.
+template <int MR>
+struct ValuSrc {
+  static constexpr bool kBuf = MR != 2;
+  buf_t wr, sr;
+  const int8_t *wp;
+  const float *sp;
+  unsigned lw, ls;
+};
+
 // Issue the loads of the stage's blocks b0 + u*W; a block past the range
 // reloads the range's last block (in bounds) and is not used.
 template <int MR, int ACT, bool DOTS, int W>
-__device__ __forceinline__ void valu_load(ValuStage<MR, ACT, DOTS> &st, const int8_t *wtile,
-                                          const float *stile, int b0, int b_hi,
-                                          const void *__restrict__ xv, int m, int K, int NB,
-                                          unsigned act_scale_off) {
+__device__ __forceinline__ void valu_load(ValuStage<MR, ACT, DOTS> &st, const ValuSrc<MR> &src,
+                                          int b0, int b_hi, const void *__restrict__ xv, int m,
+                                          int K, int NB, unsigned act_scale_off) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int b = min(b0 + u * W, b_hi - 1);
-    const int8_t *c = wtile + (size_t)b * kChunkBytes;
-    st.wa[u] = ld_stream16(c);
-    st.wb[u] = ld_stream16(c + kHalfBytes);
-    if constexpr (!DOTS) st.sc[u] = ld_stream4f(stile + (size_t)b * kTile);
+    if constexpr (ValuSrc<MR>::kBuf) {
+      const unsigned wb = (unsigned)b * kChunkBytes, sb = (unsigned)b * (kTile * 4);
+      st.wa[u] = buf_ld16(src.wr, src.lw, wb);
+      st.wb[u] = buf_ld16(src.wr, src.lw + kHalfBytes, wb);
+      if constexpr (!DOTS) st.sc[u] = buf_ld4f(src.sr, src.ls, sb);
+    } else {
+      const int8_t *c = src.wp + (size_t)b * kChunkBytes + src.lw;
+      st.wa[u] = ld_stream16(c);
+      st.wb[u] = ld_stream16(c + kHalfBytes);
+      if constexpr (!DOTS)
+        st.sc[u] = ld_stream4f(reinterpret_cast<const float *>(
+            reinterpret_cast<const char *>(src.sp) + (size_t)b * (kTile * 4) + src.ls));
+    }
     if constexpr (ValuX<MR, ACT>::kPrefetch) {
 #pragma unroll
       for (int r = 0; r < MR; ++r) {
@@ -387,7 +448,7 @@ __device__ __forceinline__ void valu_compute(const ValuStage<MR, ACT, DOTS> &st,
   }
 }
 
-template <int MR, int ACT, bool DOTS, int W>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR>
 __global__ void __launch_bounds__(64 * W)
 gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
@@ -396,13 +457,24 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  int S, unsigned act_scale_off, Epi ep) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = blockIdx.x / S;
-  const int s = blockIdx.x - t * S;
+  // unit tv = (tile, weight): a gated pair's two weights are adjacent units
+  const int tv = blockIdx.x / S;
+  const int s = blockIdx.x - tv * S;
+  const int wsel = PAIR ? (tv & 1) : 0;
+  const int t = PAIR ? (tv >> 1) : tv;
   int b_lo, b_hi;
   split_range(NB, s, S, b_lo, b_hi);
 
-  const int8_t *wtile = wq + (size_t)t * NB * kChunkBytes + lane * 16;
-  const float *stile = wsc + (size_t)t * NB * kTile + scale_pos(lane);
+  // the tile's values and scales; each lane adds its own byte offset
+  ValuSrc<MR> src;
+  src.wp = (wsel ? ep.wq_u : wq) + (size_t)t * NB * kChunkBytes;
+  src.sp = (wsel ? ep.wsc_u : wsc) + (size_t)t * NB * kTile;
+  if constexpr (ValuSrc<MR>::kBuf) {
+    src.wr = make_buf(src.wp, (unsigned)NB * kChunkBytes);
+    src.sr = make_buf(src.sp, (unsigned)NB * kTile * 4);
+  }
+  src.lw = (unsigned)lane * 16u;
+  src.ls = (unsigned)scale_pos(lane) * 4u;
 
   float acc[MR];
 #pragma unroll
@@ -416,14 +488,14 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   int b = b_lo + wave;
   if (b < b_hi) {
     ValuStage<MR, ACT, DOTS> A, B;
-    valu_load<MR, ACT, DOTS, W>(A, wtile, stile, b, b_hi, xv, m, K, NB, act_scale_off);
+    valu_load<MR, ACT, DOTS, W>(A, src, b, b_hi, xv, m, K, NB, act_scale_off);
     while (true) {
       if (b + step >= b_hi) {
         valu_compute<MR, ACT, DOTS, W>(A, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
                                        act_scale_off);
         break;
       }
-      valu_load<MR, ACT, DOTS, W>(B, wtile, stile, b + step, b_hi, xv, m, K, NB, act_scale_off);
+      valu_load<MR, ACT, DOTS, W>(B, src, b + step, b_hi, xv, m, K, NB, act_scale_off);
       valu_compute<MR, ACT, DOTS, W>(A, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
                                      act_scale_off);
       b += step;
@@ -432,7 +504,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                                        act_scale_off);
         break;
       }
-      valu_load<MR, ACT, DOTS, W>(A, wtile, stile, b + step, b_hi, xv, m, K, NB, act_scale_off);
+      valu_load<MR, ACT, DOTS, W>(A, src, b + step, b_hi, xv, m, K, NB, act_scale_off);
       valu_compute<MR, ACT, DOTS, W>(B, acc, b, b_hi, xv, dots, m, K, NB, Npad, t, lane,
                                      act_scale_off);
       b += step;
@@ -444,7 +516,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int r = 0; r < MR; ++r) red[(wave * MR + r) * 64 + lane] = acc[r];
   __syncthreads();
-  finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S, ep);
+  finish_tile<MR, W, PAIR>(red, y, partial, counters, m, Npad, t, s, S, wsel, ep);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,18 +646,21 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
   }
 }
 
-// The epilogue's additions for the column-group kernel's layout, all loads
-// first: v[rg][e][h] is row row0 + 16rg + 4j + e, column col0 + 16h + i of
-// lane (i, j); H column groups (1 or 2).  Pad columns become 0.
-template <int RG, int H>
-__device__ __forceinline__ void epi_add_groups(const Epi &ep, int Npad, int m, int row0,
-                                               size_t col0, int lane, float (&v)[RG][4][H]) {
+// The epilogue for the column-group kernel's layout, all loads first:
+// v[rg][e][h] (and vu, the gated pair's second sums) is row
+// row0 + 16rg + 4j + e, column col0 + 16h + i of lane (i, j); H column groups
+// (1 or 2).  On return v holds the final values (final_value's arithmetic).
+template <int RG, int H, bool PAIR>
+__device__ __forceinline__ void epi_final_groups(const Epi &ep, int Npad, int m, int row0,
+                                                 size_t col0, int lane, float (&v)[RG][4][H],
+                                                 const float (&vu)[RG][4][H]) {
   const int li = lane & 15, lj = lane >> 4;
-  float b[H], rv[RG][4][H];
+  float b[H], bu[H], rv[RG][4][H];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const size_t col = col0 + 16 * h + li;
     b[h] = (ep.bias && (int)col < ep.N) ? ep.bias[col] : 0.0f;
+    bu[h] = (PAIR && ep.bias_u && (int)col < ep.N) ? ep.bias_u[col] : 0.0f;
   }
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -595,7 +670,8 @@ __device__ __forceinline__ void epi_add_groups(const Epi &ep, int Npad, int m, i
       for (int h = 0; h < H; ++h) {
         const int r = row0 + rg * 16 + lj * 4 + e;
         const size_t col = col0 + 16 * h + li;
-        rv[rg][e][h] = (ep.residual && r < m) ? ep.residual[(size_t)r * Npad + col] : 0.0f;
+        rv[rg][e][h] = (!PAIR && ep.residual && r < m) ? ep.residual[(size_t)r * Npad + col]
+                                                       : 0.0f;
       }
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -605,21 +681,112 @@ __device__ __forceinline__ void epi_add_groups(const Epi &ep, int Npad, int m, i
       for (int h = 0; h < H; ++h) {
         const size_t col = col0 + 16 * h + li;
         float z = v[rg][e][h];
-        if (ep.bias) z += b[h];
-        if (ep.residual) z += rv[rg][e][h];
+        if constexpr (PAIR) {
+          if (ep.bias) z += b[h];
+          float u = vu[rg][e][h];
+          if (ep.bias_u) u += bu[h];
+          z = silu(z) * u;
+        } else {
+          if (ep.bias) z += b[h];
+          if (ep.residual) z += rv[rg][e][h];
+        }
         v[rg][e][h] = ((int)col < ep.N) ? z : 0.0f;
       }
 }
 
-// Final values of one 16-column group (column col0 + i of lane (i, j)):
-// epilogue additions, then y.
+// Sums over the S splits (in split order) of weight wsel's partial carries
+// for v[0][e][h]'s places (rows row0 + 4j + e, columns col0 + 16h + i); the
+// loads of one split are issued together.
+template <int H>
+__device__ __forceinline__ void cols_sum_partials(const float *__restrict__ partial, int m,
+                                                  int Npad, int S, int wsel, int row0,
+                                                  size_t col0, int lane, float (&v)[1][4][H]) {
+  const int li = lane & 15, lj = lane >> 4;
+  const float *p = partial + ((size_t)wsel * S * m + row0 + lj * 4) * Npad + col0 + li;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+      v[0][e][h] = (row0 + lj * 4 + e < m)
+                       ? __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM)
+                       : 0.0f;
+  for (int ss = 1; ss < S; ++ss) {
+    p += (size_t)m * Npad;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        if (row0 + lj * 4 + e < m)
+          v[0][e][h] += __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+// The last arrival's finish of H adjacent 16-column groups (columns col0 +
+// 16h + i), one 16-row group at a time (a rolled loop keeps the registers of
+// this path below the main loop's): sums of the partials, the epilogue, y,
+// and with QUANT the quantized output (H == 2: a row's 32 values are two per
+// lane across 16 lanes).
+template <int RG, int H, bool QUANT, bool PAIR>
+__device__ __forceinline__ void cols_finish(const Epi &ep, float *__restrict__ y,
+                                            const float *__restrict__ partial, int m, int Npad,
+                                            int S, size_t col0, int lane) {
+  const int li = lane & 15, lj = lane >> 4;
+  // The row stride as an opaque value, so the addresses below are formed
+  // here and not hoisted into registers held across the caller's main loop.
+  asm volatile("" : "+s"(Npad));
+#pragma unroll 1
+  for (int rg = 0; rg < RG; ++rg) {
+    const int row0 = rg * 16;
+    if (row0 >= m) break;
+    float v[1][4][H], vu[1][4][H];
+    cols_sum_partials<H>(partial, m, Npad, S, 0, row0, col0, lane, v);
+    if constexpr (PAIR) {
+      cols_sum_partials<H>(partial, m, Npad, S, 1, row0, col0, lane, vu);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < H; ++h) vu[0][e][h] = 0.0f;
+    }
+    // every bias and residual value is read before any y is written (the
+    // residual may be y itself)
+    epi_final_groups<1, H, PAIR>(ep, Npad, m, row0, col0, lane, v, vu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + lj * 4 + e;
+      if (r >= m) continue;   // uniform over the 16 lanes of one j
+      if (ep.write_y) {
+#pragma unroll
+        for (int h = 0; h < H; ++h) y[(size_t)r * Npad + col0 + 16 * h + li] = v[0][e][h];
+      }
+      if constexpr (QUANT) {
+        static_assert(H == 2, "a quantized block is 32 columns");
+        float amax = fmaxf(fabsf(v[0][e][0]), fabsf(v[0][e][1]));
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+        const float d = q8_scale_of(amax);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ep.yq[(size_t)r * Npad + col0 + 16 * h + li] = q8_code_of(v[0][e][h], d);
+        if (li == 0) ep.yq_scale[(size_t)r * (Npad / 32) + col0 / 32] = d;
+      }
+    }
+  }
+}
+
+// One 16-column group complete in one wave (one split, one weight): the
+// epilogue and y (column col0 + i of lane (i, j)).
 template <int RG>
 __device__ __forceinline__ void cols_store_group(const Epi &ep, float *__restrict__ y, int Npad,
                                                  int m, size_t col0, int lane,
                                                  float (&v)[RG][4][1]) {
   const int li = lane & 15, lj = lane >> 4;
-  if (ep.bias || ep.residual || (int)(col0 + 16) > ep.N)
-    epi_add_groups<RG, 1>(ep, Npad, m, 0, col0, lane, v);
+  if (ep.bias || ep.residual || (int)(col0 + 16) > ep.N) {
+    float vu[RG][4][1] = {};
+    epi_final_groups<RG, 1, false>(ep, Npad, m, 0, col0, lane, v, vu);
+  }
   if (!ep.write_y) return;
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -630,79 +797,7 @@ __device__ __forceinline__ void cols_store_group(const Epi &ep, float *__restric
     }
 }
 
-// Split-K finish of a column-group pair with the output quantizer (the
-// column-group kernel, S >= 2): the caller has published its partial carries
-// (visible at system scope).  The last of the pair's 2S arrivals sums both
-// groups' partials in split order, applies the epilogue and quantizes the
-// pair's 32 columns: lane (i, j) holds column col0 + 16h + i of rows
-// 16rg + 4j + e, so a row's 32 values are 2 per lane across 16 lanes.
-template <int RG>
-__device__ __forceinline__ void cols_finish_pair(const Epi &ep, float *__restrict__ y,
-                                                 const float *__restrict__ partial,
-                                                 unsigned *__restrict__ counter, int m, int Npad,
-                                                 int S, size_t col0, int lane) {
-  unsigned prev = 0;
-  if (lane == 0)
-    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != (unsigned)(2 * S - 1)) return;
-  const int li = lane & 15, lj = lane >> 4;
-  // The row stride as an opaque value, so the addresses below are formed
-  // here and not hoisted into registers held across the caller's main loop.
-  asm volatile("" : "+s"(Npad));
-  // One 16-row group at a time (a rolled loop keeps the registers of this
-  // path below the main loop's).  v[0][e][h]: row row0 + 4j + e, column
-  // col0 + 16h + i.  Splits are summed in order 0..S-1, each split's eight
-  // loads issued together.
-#pragma unroll 1
-  for (int rg = 0; rg < RG; ++rg) {
-    const int row0 = rg * 16;
-    if (row0 >= m) break;
-    float v[1][4][2];
-    const float *p = partial + (size_t)(row0 + lj * 4) * Npad + col0 + li;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        v[0][e][h] = (row0 + lj * 4 + e < m)
-                         ? __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_SYSTEM)
-                         : 0.0f;
-    for (int ss = 1; ss < S; ++ss) {
-      p += (size_t)m * Npad;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          if (row0 + lj * 4 + e < m)
-            v[0][e][h] += __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    // every bias and residual value is read before any y is written (the
-    // residual may be y itself)
-    epi_add_groups<1, 2>(ep, Npad, m, row0, col0, lane, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = row0 + lj * 4 + e;
-      if (r >= m) continue;   // uniform over the 16 lanes of one j
-      const float z[2] = {v[0][e][0], v[0][e][1]};
-      if (ep.write_y) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) y[(size_t)r * Npad + col0 + 16 * h + li] = z[h];
-      }
-      float amax = fmaxf(fabsf(z[0]), fabsf(z[1]));
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-      const float d = q8_scale_of(amax);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) ep.yq[(size_t)r * Npad + col0 + 16 * h + li] = q8_code_of(z[h], d);
-      if (li == 0) ep.yq_scale[(size_t)r * (Npad / 32) + col0 / 32] = d;
-    }
-  }
-  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-template <int MR, int ACT, bool DOTS, int KW, int P, bool QO>
+template <int MR, int ACT, bool DOTS, int KW, int P, bool QO, bool PAIR>
 __global__ void __launch_bounds__(256 * KW * P)
 gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                       const float *__restrict__ wsc, float *__restrict__ y,
@@ -730,21 +825,29 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
   const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + (size_t)col_in_tile * 16 + (lj & 1) * 8;
 
   constexpr int step = KW * kColsUnroll;
-  int t = jwg * P + slot;
+  // Units tv = (tile, weight), T of them: a gated pair's two weights are
+  // adjacent units.
+  constexpr bool pair = PAIR;
+  constexpr int NW = PAIR ? 2 : 1;
+  const int tv0 = jwg * P + slot;
   ColsStage A, B;
   // First stage of the first tile in flight while the activation is staged.
-  if (t < T && b_lo + kw < b_hi)
-    cols_load<DOTS, KW>(A, wq + (size_t)t * NB * kChunkBytes + lane_off,
-                        wsc + (size_t)t * NB * kTile + scale_pos(col_in_tile), b_lo + kw, b_hi);
+  if (tv0 < T && b_lo + kw < b_hi) {
+    const int t0 = pair ? tv0 >> 1 : tv0, w0 = pair ? (tv0 & 1) : 0;
+    cols_load<DOTS, KW>(A, (w0 ? ep.wq_u : wq) + (size_t)t0 * NB * kChunkBytes + lane_off,
+                        (w0 ? ep.wsc_u : wsc) + (size_t)t0 * NB * kTile + scale_pos(col_in_tile),
+                        b_lo + kw, b_hi);
+  }
 
   stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
   __syncthreads();
   const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
   float *red = reinterpret_cast<float *>(lds + mfma_stage_bytes(MR, ACT, nblk_max));
 
-  for (; t < T; t += G * P) {
-    const int8_t *wcol = wq + (size_t)t * NB * kChunkBytes + lane_off;
-    const float *scol = wsc + (size_t)t * NB * kTile + scale_pos(col_in_tile);
+  for (int tv = tv0; tv < T; tv += G * P) {
+    const int t = pair ? tv >> 1 : tv, wsel = pair ? (tv & 1) : 0;
+    const int8_t *wcol = (wsel ? ep.wq_u : wq) + (size_t)t * NB * kChunkBytes + lane_off;
+    const float *scol = (wsel ? ep.wsc_u : wsc) + (size_t)t * NB * kTile + scale_pos(col_in_tile);
     f32x4_t acc[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -796,7 +899,7 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
 
     int b = b_lo + kw;
     if (b < b_hi) {
-      if (t != jwg * P + slot)   // the first tile's first stage is already in flight
+      if (tv != tv0)   // the first tile's first stage is already in flight
         cols_load<DOTS, KW>(A, wcol, scol, b, b_hi);
       // One compute site: the next stage is loaded into B while A is
       // computed, then copied into A (the copy waits for B, which the next
@@ -838,11 +941,13 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
       if (kw != 0) continue;
     }
 
-    // This wave's 16 columns are final for its split: store, or publish the
-    // partial and let the last split to arrive sum them in split order (the
-    // same protocol as finish_tile, per 16-column group, inside one wave).
+    // This wave's 16 columns are final for its split and weight: store, or
+    // publish the partial and let the last arrival sum the partials in split
+    // order (the protocol of finish_tile, per 16-column group, inside one
+    // wave).
     const size_t col = (size_t)t * kTile + col_in_tile;
-    if (S == 1) {
+    const int arrivals = S * NW;
+    if (arrivals == 1) {
       float v[RG][4][1];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -857,27 +962,30 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
       for (int e = 0; e < 4; ++e) {
         const int r = rg * 16 + lj * 4 + e;
         if (r < m)
-          __hip_atomic_store(&partial[((size_t)s * m + r) * Npad + col], acc[rg][e],
+          __hip_atomic_store(&partial[(((size_t)wsel * S + s) * m + r) * Npad + col], acc[rg][e],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if constexpr (QO) {
-      // Output quantizer: its 32-column blocks span the column-group pair
-      // (g & 2, g | 1), so the pair shares one counter and the last of its 2S
-      // arrivals finishes all 32 columns.
-      cols_finish_pair<RG>(ep, y, partial, counters + (size_t)t * 4 + (g & 2), m, Npad, S,
-                           (size_t)t * kTile + 16 * (g & 2), lane);
-      continue;
-    }
+    // The output quantizer's 32-column blocks span the column-group pair
+    // (g & 2, g | 1): then the pair shares one counter and the last of its
+    // arrivals finishes all 32 columns.
+    unsigned *counter = counters + (size_t)t * 4 + (QO ? (g & 2) : g);
+    const unsigned last = (unsigned)(arrivals * (QO ? 2 : 1) - 1);
     unsigned prev = 0;
     if (lane == 0)
-      prev = __hip_atomic_fetch_add(&counters[(size_t)t * 4 + g], 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_SYSTEM);
+      prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != (unsigned)(S - 1)) continue;
-    {
+    if (prev != last) continue;
+    if constexpr (QO) {
+      cols_finish<RG, 2, true, PAIR>(ep, y, partial, m, Npad, S, (size_t)t * kTile + 16 * (g & 2),
+                                     lane);
+    } else if constexpr (PAIR) {
+      cols_finish<RG, 1, false, true>(ep, y, partial, m, Npad, S, col - li, lane);
+    } else {
+      // one weight, no quantizer: the split sums in place (this form keeps
+      // the main loop's register allocation of the plain build)
       float v[RG][4][1];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -896,9 +1004,7 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
         }
       cols_store_group<RG>(ep, y, Npad, m, col - li, lane, v);
     }
-    if (lane == 0)
-      __hip_atomic_store(&counters[(size_t)t * 4 + g], 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
+    if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
@@ -931,7 +1037,7 @@ __device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
   }
 }
 
-template <int MR, int ACT, bool DOTS, int W>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR>
 __global__ void __launch_bounds__(64 * W)
 gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
@@ -954,12 +1060,18 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
   const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
 
+  // Units tv = (tile, weight), T of them: a gated pair's two weights are
+  // adjacent units.
+  constexpr bool pair = PAIR;
   constexpr int step = W * kMfmaUnroll;
   MfmaStage A, B;
-  if (jwg < T && b_lo + wave < b_hi)
-    mfma_load<DOTS, W>(A, wq + (size_t)jwg * NB * kChunkBytes + lane_off,
-                       reinterpret_cast<const float4 *>(wsc + (size_t)jwg * NB * kTile) + li,
+  if (jwg < T && b_lo + wave < b_hi) {
+    const int t0 = pair ? jwg >> 1 : jwg, w0 = pair ? (jwg & 1) : 0;
+    mfma_load<DOTS, W>(A, (w0 ? ep.wq_u : wq) + (size_t)t0 * NB * kChunkBytes + lane_off,
+                       reinterpret_cast<const float4 *>((w0 ? ep.wsc_u : wsc) +
+                                                        (size_t)t0 * NB * kTile) + li,
                        b_lo + wave, b_hi);
+  }
   stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
   __syncthreads();
   const float *dxs = reinterpret_cast<const float *>(lds + (size_t)nblk * MR * kRowBytes);
@@ -968,9 +1080,11 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   float *red = reinterpret_cast<float *>(
       lds + (red_on_stage ? (size_t)0 : mfma_stage_bytes(MR, ACT, nblk_max)));
 
-  for (int t = jwg; t < T; t += G) {
-    const int8_t *wlane = wq + (size_t)t * NB * kChunkBytes + lane_off;
-    const float4 *slane = reinterpret_cast<const float4 *>(wsc + (size_t)t * NB * kTile) + li;
+  for (int tv = jwg; tv < T; tv += G) {
+    const int t = pair ? tv >> 1 : tv, wsel = pair ? (tv & 1) : 0;
+    const int8_t *wlane = (wsel ? ep.wq_u : wq) + (size_t)t * NB * kChunkBytes + lane_off;
+    const float4 *slane =
+        reinterpret_cast<const float4 *>((wsel ? ep.wsc_u : wsc) + (size_t)t * NB * kTile) + li;
     f32x4_t acc[RG][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -1041,7 +1155,7 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 
     int b = b_lo + wave;
     if (b < b_hi) {
-      if (t != jwg) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
+      if (tv != jwg) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
       // One compute site: the next stage is loaded into B while A is
       // computed, then copied into A (the copy waits for B, which the next
       // compute needs anyway).
@@ -1070,7 +1184,7 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         for (int e = 0; e < 4; ++e)
           red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
     __syncthreads();
-    finish_tile<MR, W>(red, y, partial, counters, m, Npad, t, s, S, ep);
+    finish_tile<MR, W, PAIR>(red, y, partial, counters, m, Npad, t, s, S, wsel, ep);
     __syncthreads();   // red is free again for the next tile
   }
 }
@@ -1096,13 +1210,23 @@ size_t cols_lds_bytes_of(int rows, int act, int kslices, int NB, int S) {
   return mfma_stage_bytes(rows, act, nblk) + red;
 }
 
-template <int MR, int ACT, bool DOTS, int W>
-hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.T * a.split_k));
-  gemv_valu_kernel<MR, ACT, DOTS, W><<<grid, dim3(64 * W), 0, stream>>>(
+template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.tiles() * a.split_k));
+  gemv_valu_kernel<MR, ACT, DOTS, W, PAIR><<<grid, dim3(64 * W), 0, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB,
       a.Npad, a.split_k, a.act_scale_off, a.ep);
   return hipGetLastError();
+}
+
+// Each kernel is built for one weight and for the gated pair, so the single
+// product carries none of the pair's code.
+template <int MR, int ACT, bool DOTS, int W>
+hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
+  if constexpr (!DOTS) {
+    if (a.ep.nw == 2) return launch_valu_k<MR, ACT, DOTS, W, true>(a, stream);
+  }
+  return launch_valu_k<MR, ACT, DOTS, W, false>(a, stream);
 }
 
 // Workgroups of a launch that fit on the device at once (per CU, from the
@@ -1121,6 +1245,17 @@ int resident_workgroups(Kern kern, int threads, size_t lds) {
   return per_cu * cus;
 }
 
+// Workgroups of a persistent grid over `units` units of work when at most
+// `fit` are resident: the fewest rounds, then the fewest workgroups that
+// finish in that many rounds, so every workgroup walks the same number of
+// units (448 units on 256 resident: 224 workgroups of 2, not 256 of 1 or 2).
+int balanced_grid(int fit, int units) {
+  if (fit < 1) fit = 1;
+  if (units < 1) return 1;
+  const int rounds = (units + fit - 1) / fit;
+  return (units + rounds - 1) / rounds;
+}
+
 // Grants the dynamic LDS above the default 64 KiB (once per size increase).
 template <typename Kern>
 hipError_t grant_lds(Kern kern, size_t lds, size_t &granted) {
@@ -1131,13 +1266,13 @@ hipError_t grant_lds(Kern kern, size_t lds, size_t &granted) {
   return e;
 }
 
-template <int MR, int ACT, bool DOTS, int W>
-hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
+template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t st = mfma_stage_of(MR, ACT, a.NB, a.split_k), rd = mfma_red_of(MR, W);
   const size_t lds_alias = st > rd ? st : rd;   // carries on top of the stage
   const size_t lds_sep = st + rd;               // carries after the stage
-  auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W>;
+  auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W, PAIR>;
   static size_t granted = 64 * 1024;
   int dev = 0, max_lds = 0;
   (void)hipGetDevice(&dev);
@@ -1149,54 +1284,63 @@ hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
   // once and walks tiles j, j+G, ... (carries apart), if that fits in LDS.
   hipError_t e = grant_lds(kern, lds_alias, granted);
   if (e != hipSuccess) return e;
-  int G = a.T, red_on_stage = 1;
+  int G = a.tiles(), red_on_stage = 1;
   size_t lds = lds_alias;
   const int fit_alias = resident_workgroups(kern, 64 * W, lds_alias) / a.split_k;
-  if (fit_alias < a.T && lds_sep + 1024 <= (size_t)max_lds) {
+  if (fit_alias < a.tiles() && lds_sep + 1024 <= (size_t)max_lds) {
     e = grant_lds(kern, lds_sep, granted);
     if (e != hipSuccess) return e;
-    int g = resident_workgroups(kern, 64 * W, lds_sep) / a.split_k;
-    if (g < 1) g = 1;
-    G = g < a.T ? g : a.T;
+    G = balanced_grid(resident_workgroups(kern, 64 * W, lds_sep) / a.split_k, a.tiles());
     red_on_stage = 0;
     lds = lds_sep;
   }
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
-      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.tiles(),
       a.split_k, G, nblk_max, red_on_stage, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
-template <int MR, int ACT, bool DOTS, int KW, int P, bool QO>
+template <int MR, int ACT, bool DOTS, int W>
+hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
+  if constexpr (!DOTS) {
+    if (a.ep.nw == 2) return launch_mfma_k<MR, ACT, DOTS, W, true>(a, stream);
+  }
+  return launch_mfma_k<MR, ACT, DOTS, W, false>(a, stream);
+}
+
+template <int MR, int ACT, bool DOTS, int KW, int P, bool QO, bool PAIR>
 hipError_t launch_cols_k(const GemvArgs &a, hipStream_t stream) {
   constexpr int W = 4 * KW * P;
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t lds = cols_lds_bytes_of(MR, ACT, KW, a.NB, a.split_k);
-  auto kern = gemv_mfma_cols_kernel<MR, ACT, DOTS, KW, P, QO>;
+  auto kern = gemv_mfma_cols_kernel<MR, ACT, DOTS, KW, P, QO, PAIR>;
   static size_t granted = 64 * 1024;
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
   // G workgroups per K split, each walking tiles j*P + slot, step G*P.
-  const int want = (a.T + P - 1) / P;
-  int G = resident_workgroups(kern, 64 * W, lds) / a.split_k;
-  if (G < 1) G = 1;
-  if (G > want) G = want;
+  const int want = (a.tiles() + P - 1) / P;
+  const int G = balanced_grid(resident_workgroups(kern, 64 * W, lds) / a.split_k, want);
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
-      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.tiles(),
       a.split_k, G, nblk_max, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
-// The column-group kernel is built twice: with the output quantizer in its
-// split-K finish, and without (whose registers it would otherwise share).
+// The column-group kernel is built with and without the output quantizer
+// in its split-K finish, and for one weight or the gated pair: each build
+// keeps only the registers its own finish needs (the main loop runs at the
+// register limit of 16 waves).
 template <int MR, int ACT, bool DOTS, int KW, int P>
 hipError_t launch_cols(const GemvArgs &a, hipStream_t stream) {
   if constexpr (!DOTS) {
-    if (a.ep.yq) return launch_cols_k<MR, ACT, DOTS, KW, P, true>(a, stream);
+    const bool qo = a.ep.yq != nullptr, pair = a.ep.nw == 2;
+    if (qo && pair) return launch_cols_k<MR, ACT, DOTS, KW, P, true, true>(a, stream);
+    if (qo) return launch_cols_k<MR, ACT, DOTS, KW, P, true, false>(a, stream);
+    if (pair) return launch_cols_k<MR, ACT, DOTS, KW, P, false, true>(a, stream);
   }
-  return launch_cols_k<MR, ACT, DOTS, KW, P, false>(a, stream);
+  return launch_cols_k<MR, ACT, DOTS, KW, P, false, false>(a, stream);
 }
 
 using Launcher = hipError_t (*)(const GemvArgs &, hipStream_t);

@@ -163,3 +163,13 @@ def exact_case(m: int, K: int, N: int, seed: int):
     bias[32:64] = 0
     res[:, 32:64] = 0
     return f32_to_bf16_bits(x), q, s, bias, res
+
+
+def generate_pair(w: Workload, n_cols: Optional[int] = None):
+    """``(x, qg, sg, qu, su)``: a workload's activation and two weights of its
+    shape (a gate and an up projection), the up weight from seed_w + 500000."""
+    x, qg, sg = generate(w, n_cols)
+    N = w.N if n_cols is None else n_cols
+    qu = gen_q(w.K, N, w.seed_w + 500000, w.q_law)
+    su = gen_scales(w.K, N, w.seed_w + 500000)
+    return x, qg, sg, qu, su

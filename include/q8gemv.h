@@ -249,6 +249,49 @@ int q8_gemv_planned_fused(const void *x, const int8_t *W_q8,
 int q8_gemv_fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
                                const q8_epilogue *epilogue, q8_plan *plan);
 
+/* ---- the gated pair --------------------------------------------------------- */
+
+/*
+ * Two products of one activation through a gate, in one launch: the pages'
+ * codegen_cuda/lane/plan.rs, enum Launch, variant GemvGlu, whose output is
+ * act(x.Wg + bg) * (x.Wu + bu), SwiGLU when no activation is named.  This
+ * library computes the SwiGLU form, per output element (r, n), n < N:
+ *     g = (x . Wg)[r, n] + bias_g[n],  u = (x . Wu)[r, n] + bias_u[n]
+ *     z = silu(g) * u,  silu(g) = g / (1 + exp(-g))
+ * in fp32 (each bias only when given); pad columns get z = 0.  y and y_q8 as
+ * in q8_epilogue.  Wg and Wu are packed weights of the same K x N shape (one
+ * q8_repack each); x and act_fmt as in q8_gemv.  The two weights' carries
+ * always meet through the workspace (q8_glu_workspace_bytes).
+ */
+typedef struct q8_glu_epilogue {
+  const float *bias_g;   /* N fp32, or NULL                                   */
+  const float *bias_u;   /* N fp32, or NULL                                   */
+  void *y_q8;            /* q8_act_bytes(m, N_pad) bytes, or NULL             */
+  int32_t write_y;       /* nonzero: write y                                  */
+} q8_glu_epilogue;
+
+/* The pair with the library's workspace (as q8_gemv).  NULL epilogue: y
+ * only, no biases. */
+int q8_gemv_glu(const void *x, const int8_t *Wg_q8, const float *Wg_q8_scale,
+                const int8_t *Wu_q8, const float *Wu_q8_scale, float *y, int64_t m,
+                int64_t K, int64_t N, int act_fmt,
+                const q8_glu_epilogue *epilogue /* host pointer */, hipStream_t stream);
+
+/* The pair with an explicit plan and the caller's workspace (zeroed once,
+ * as in q8_gemv_ws). */
+int q8_gemv_glu_planned(const void *x, const int8_t *Wg_q8,
+                        const float *Wg_q8_scale, const int8_t *Wu_q8,
+                        const float *Wu_q8_scale, float *y, int64_t m, int64_t K,
+                        int64_t N, int act_fmt, const q8_glu_epilogue *epilogue,
+                        const q8_plan *plan, hipStream_t stream, void *workspace,
+                        size_t ws_bytes);
+
+/* The plan q8_gemv_glu launches, and the workspace a plan needs for it. */
+int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
+                             q8_plan *plan);
+size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K,
+                              int64_t N);
+
 /* ---- errors and resources ------------------------------------------------ */
 
 /* Static name of a status code. */

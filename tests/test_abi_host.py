@@ -156,3 +156,35 @@ def test_fused_default_plan_for_quantized_output():
             assert fused.kernel == q8.Q8_KERNEL_MFMA
         same = q8.q8_gemv_fused_default_plan(m, K, N, 1, q8.make_epilogue(bias=A))
         assert _t(same) == _t(plain)
+
+
+def test_gated_pair_validation():
+    expect(3, q8.q8_gemv_glu, A, A, A, None, A, A, 1, 64, 8, 0, None, S0)
+    expect(4, q8.q8_gemv_glu, A, A, A, A, A + 4, A, 1, 64, 8, 0, None, S0)
+    expect(1, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 48, 8, 0, None, S0)
+    expect(2, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, 3, None, S0)
+    ep = q8.make_glu_epilogue(write_y=False)
+    expect(3, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, 0, ep, S0)
+    ep = q8.make_glu_epilogue(bias_u=A + 8)
+    expect(4, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, 0, ep, S0)
+    p = q8.q8_gemv_glu_default_plan(1, 64, 8, 0)
+    # the two weights' carries always meet in the workspace
+    need = q8.q8_glu_workspace_bytes(p, 1, 64, 8)
+    assert need >= 4 * 2 ** 20 + 2 * p.split_k * 64 * 4
+    expect(5, q8.q8_gemv_glu_planned, A, A, A, A, A, A, 1, 64, 8, 0, None, p, S0, None, 0)
+    expect(5, q8.q8_gemv_glu_planned, A, A, A, A, A, A, 1, 64, 8, 0, None, p, S0, A, need - 16)
+
+
+def test_gated_pair_plan_counts_both_weights():
+    # the pair's work is 2 * N_pad columns: its split count is that of a
+    # product twice as wide; VALU workgroups beyond one per CU take 4 waves
+    for (m, K, N, act) in ((1, 4096, 14336, 0), (1, 4096, 1024, 0), (4, 2048, 200, 1),
+                           (16, 4096, 14336, 0)):
+        pair = q8.q8_gemv_glu_default_plan(m, K, N, act)
+        wide = q8.q8_gemv_default_plan(m, K, 2 * q8.q8_padded_cols(N), act)
+        assert (pair.kernel, pair.rows, pair.split_k, pair.kslices) == \
+            (wide.kernel, wide.rows, wide.split_k, wide.kslices)
+        if pair.kernel == q8.Q8_KERNEL_VALU:
+            assert pair.waves in (4, wide.waves)
+        else:
+            assert pair.waves == wide.waves

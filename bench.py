@@ -64,6 +64,17 @@ def algorithmic_bytes(w) -> dict:
             "total": values + scales + x + y}
 
 
+def kernel_name(plan: dict, w) -> str:
+    """The kernel a plan launches for a single product, as rocprofv3 names it."""
+    act = 0 if w.act == "bf16" else 1
+    r, wv, ks = plan["rows"], plan["waves"], plan.get("kslices", 1)
+    if plan["kernel"] == 0:
+        return f"gemv_valu_kernel<{r}, {act}, false, {wv}, false>"
+    if plan["kernel"] == 1:
+        return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false>"
+    return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
+
+
 def csrc_hash() -> str:
     h = hashlib.sha256()
     d = os.path.join(ROOT, "block_quantized_weight_02_amd", "csrc")
@@ -207,7 +218,7 @@ def measure(w, steps, warmup, rotate=True):
         "event_pair_us_p90": float(np.percentile(each, 90) * 1e3),
         "bytes": b, "copies": st.copies, "wall_s": wall,
         "plan": {"kernel": st.plan.kernel, "rows": st.plan.rows,
-                 "split_k": st.plan.split_k, "waves": st.plan.waves},
+                 "split_k": st.plan.split_k, "waves": st.plan.waves, "kslices": st.plan.kslices},
     }
     # the product kernel moves every algorithmic byte (its x is the quantized
     # buffer in Q8_0 mode); the quantize launch is counted in the step only
@@ -412,7 +423,7 @@ def main():
     achieved = head["kernel_gbs"]
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": ("gemv_valu_kernel" if head["plan"]["kernel"] == 0 else "gemv_mfma_kernel"),
+            "kernel": kernel_name(head["plan"], w),
             "kernel_us_mean": head["kernel_us_mean"], "loop_us_per_step": head["us_per_step"],
             "bytes_per_launch": head["bytes"]["total"]}
 

@@ -23,7 +23,8 @@ the timed steps; `roofline` prices the product kernel's own average duration
 `by_rows` gives the same measurement at m = 16 and m = 32; `fused_epilogue`
 times the product with bias, residual and quantized output beside the plain
 product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
-one launch) beside two plain products, at m = 1 and m = 16.
+one launch) beside two plain products, at m = 1 and m = 16; `context` gives
+the headline with one weight copy reused and a 1 GiB device copy's rate.
 """
 import argparse
 import hashlib
@@ -343,10 +344,48 @@ def cpu_baseline(w, budget_s=12.0):
             break
     per = el / reps
     b = algorithmic_bytes(w)["total"]
-    return {"value": b / per / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+    cores = oracle.threads()
+    # the same on one thread (a few products: about 2 s)
+    oracle.set_threads(1)
+    try:
+        t1 = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            run()
+            t1.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(0)
+    per1 = sorted(t1)[1]
+    return {"value": b / per / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full {w.name} products (m={w.m} K={w.K} N={w.N}), "
                       f"{per * 1e3:.1f} ms each, fp64 C oracle, OpenMP",
-            "ms_per_step": per * 1e3, "weights_per_s": w.K * w.N / per}
+            "ms_per_step": per * 1e3, "weights_per_s": w.K * w.N / per,
+            "one_thread": {"value": b / per1 / 1e9, "ms_per_step": per1 * 1e3,
+                           "sample": "median of 3 full products on 1 thread"}}
+
+
+def bandwidth_context(torch, w, steps):
+    """What surrounds the headline number: the same product with one weight
+    copy reused (the 256 MB cache may then hold it: 'MALL-hot'), and a plain
+    1 GiB device-to-device copy (reads and writes 1 GiB)."""
+    st = Setup(w, rotate=False)
+    for i in range(50):
+        st.gemv_only(i)
+    hot_ms = time_loop(st.gemv_only, steps)
+    b = algorithmic_bytes(w)["total"]
+    del st
+    torch.cuda.empty_cache()
+    nbytes = 2 ** 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    cms = time_loop(lambda i: dst.copy_(src), 20)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mall_hot_us": hot_ms * 1e3, "mall_hot_gbs": b / (hot_ms * 1e-3) / 1e9,
+            "copy_1gib_us": cms * 1e3,
+            "copy_1gib_gbs_read_plus_write": 2 * nbytes / (cms * 1e-3) / 1e9}
 
 
 def copy_calibration(torch, nbytes=256 * 2 ** 20, reps=20):
@@ -419,6 +458,12 @@ def main():
                             max(20, args.warmup // 4), rotate=not args.no_rotate)
             fused[f"glu_m{inputs.WORKLOADS[other].m}"] = r
 
+    context = None
+    if not args.no_rows:
+        context = bandwidth_context(torch, w, args.steps)
+        log(f"[bench] context: one weight copy {context['mall_hot_us']:.2f} us; 1 GiB copy "
+            f"{context['copy_1gib_gbs_read_plus_write']:.0f} GB/s read+write")
+
     traffic = traffic_from_profile(w.name)
     achieved = head["kernel_gbs"]
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -458,6 +503,7 @@ def main():
         "cpu_baseline": cpu,
         "by_rows": by_rows,
         "fused_epilogue": fused,
+        "context": context,
     }
     print(json.dumps(out), flush=True)
 

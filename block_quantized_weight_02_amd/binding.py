@@ -22,6 +22,8 @@ Q8_ACT_Q8_0 = 1
 Q8_KERNEL_VALU = 0
 Q8_KERNEL_MFMA = 1
 Q8_KERNEL_MFMA_COLS = 2
+Q8_MAX_ROWS = 32
+Q8_MAX_GEMM_ROWS = 8192
 
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_SHAPE", 2: "Q8_ERR_ACT_FMT", 3: "Q8_ERR_NULL",
           4: "Q8_ERR_ALIGN", 5: "Q8_ERR_WORKSPACE", 6: "Q8_ERR_HIP", 7: "Q8_ERR_PLAN"}
@@ -93,6 +95,8 @@ _SIGS = {
                                    _p, _p, _sz]),
     "q8_gemv_glu_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_plan)]),
     "q8_glu_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), _i64, _i64, _i64]),
+    "q8_gemm": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
+    "q8_gemm_block_dots": (_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
     "q8_status_string": (ctypes.c_char_p, [_int]),
     "q8_last_error": (ctypes.c_char_p, []),
     "q8_release_workspaces": (_int, []),
@@ -291,6 +295,16 @@ def q8_gemv_glu_default_plan(m, K, N, act_fmt) -> q8_plan:
 
 def q8_glu_workspace_bytes(plan: q8_plan, m, K, N) -> int:
     return int(lib().q8_glu_workspace_bytes(ctypes.byref(plan), m, K, N))
+
+
+def q8_gemm(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream=None) -> None:
+    _check(lib().q8_gemm(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y), m, K, N,
+                         act_fmt, _stream(stream)))
+
+
+def q8_gemm_block_dots(x_q8, W_q8, dots, m, K, N, stream=None) -> None:
+    _check(lib().q8_gemm_block_dots(_addr(x_q8), _addr(W_q8), _addr(dots), m, K, N,
+                                    _stream(stream)))
 
 
 def q8_status_string(status: int) -> str:

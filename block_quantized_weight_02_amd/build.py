@@ -9,12 +9,14 @@ disabled for every device compile (-Xclang -target-feature -Xclang
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq8gemv.so")
-SOURCES = ["q8_kernels.hip", "q8_api.cpp"]
+SOURCES = ["q8_kernels.hip", "q8_gemm.hip", "q8_api.cpp"]
 ARCH = os.environ.get("Q8_OFFLOAD_ARCH", "gfx950")
 
 
@@ -25,13 +27,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
-    tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-command-line-argument",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp, *extra]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +38,25 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
+    """Compiles every source to an object (in parallel), then links the
+    shared library; returns its path."""
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Wall", "-Wno-unused-command-line-argument",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra]
+    with tempfile.TemporaryDirectory(prefix="q8build") as d:
+        objs = [os.path.join(d, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = out + ".tmp"
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, out)
     return out
 
 

@@ -63,10 +63,10 @@ int check_kn(int64_t K, int64_t N) {
   return Q8_OK;
 }
 
-int check_m(int64_t m) {
-  if (m < 1 || m > Q8_MAX_ROWS)
-    return fail(Q8_ERR_SHAPE, "m = %lld out of range: need 1 <= m <= %d",
-                (long long)m, Q8_MAX_ROWS);
+int check_m(int64_t m, int64_t max_rows = Q8_MAX_ROWS) {
+  if (m < 1 || m > max_rows)
+    return fail(Q8_ERR_SHAPE, "m = %lld out of range: need 1 <= m <= %lld",
+                (long long)m, (long long)max_rows);
   return Q8_OK;
 }
 
@@ -491,8 +491,11 @@ int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K, int64_t N,
 int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
                     hipStream_t stream) {
   int st;
-  if ((st = check_m(m))) return st;
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS))) return st;
   if ((st = check_kn(K, 1))) return st;
+  if (act_scales_offset(m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
+                (long long)(m * K));
   if ((st = check_ptr(x_bf16, "x_bf16")) || (st = check_ptr(x_q8, "x_q8"))) return st;
   (void)hipGetLastError();
   hipError_t e = q8::launch_quantize_act(x_bf16, x_q8, (int)m, (int)K,
@@ -646,6 +649,53 @@ int q8_gemv_glu(const void *x, const int8_t *Wg_q8, const float *Wg_q8_scale,
   if ((st = library_workspace(stream, need, &ws))) return st;
   return run_glu(x, Wg_q8, Wg_q8_scale, Wu_q8, Wu_q8_scale, y, m, K, N, act_fmt, epilogue, plan,
                  stream, ws, need);
+}
+
+namespace {
+
+int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *y,
+             int32_t *dots, int64_t m, int64_t K, int64_t N, int act_fmt, hipStream_t stream) {
+  int st;
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, N)) || (st = check_act(act_fmt)))
+    return st;
+  if ((st = check_ptr(x, "x")) || (st = check_ptr(W_q8, "W_q8"))) return st;
+  if (!dots && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
+  if (dots ? (st = check_ptr(dots, "dots")) : (st = check_ptr(y, "y"))) return st;
+  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
+                (long long)(m * K));
+  const int64_t Npad = round_up(N, Q8_TILE_COLS);
+  q8::GemmArgs a{};
+  a.x = x;
+  a.wq = W_q8;
+  a.wsc = W_q8_scale;
+  a.y = y;
+  a.dots = dots;
+  a.m = (int)m;
+  a.K = (int)K;
+  a.NB = (int)(K / Q8_BLOCK);
+  a.Npad = (int)Npad;
+  a.T = (int)(Npad / Q8_TILE_COLS);
+  a.act_scale_off = (unsigned)act_scales_offset(m, K);
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_gemm(act_fmt, dots != nullptr, q8::gemm_rows_per_block(m), a, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_fail(e, "gemm launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+int q8_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *y, int64_t m,
+            int64_t K, int64_t N, int act_fmt, hipStream_t stream) {
+  return run_gemm(x, W_q8, W_q8_scale, y, nullptr, m, K, N, act_fmt, stream);
+}
+
+int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots, int64_t m, int64_t K,
+                       int64_t N, hipStream_t stream) {
+  return run_gemm(x_q8, W_q8, nullptr, nullptr, dots, m, K, N, Q8_ACT_Q8_0, stream);
 }
 
 const char *q8_status_string(int status) {

@@ -1,0 +1,328 @@
+// q8_gemm.hip -- the Q8_0 weight product for many activation rows (a prefill
+// chunk): a matrix-core GEMM over the packed weight.
+//
+// What it computes is the product of q8_kernels.hip for any m:
+//   y[r,n] = sum_b s[b,n] * D[r,b,n],  D[r,b,n] = sum_i x[r,32b+i] * q[32b+i,n]
+// (int8 activations: x = dx[r,b] * xq), carried in fp32.  The pages' CUDA
+// planner takes the product to its tensor-core GEMM above the GEMV's rows,
+// with the activation quantized and the Q8_0 scale arrays read beside the
+// values (codegen_cuda/lane/plan.rs, Launch::on_tensor_cores and
+// gemm_blk_rows).
+//
+// gfx950 design:
+//   * a workgroup of 4 waves owns a BM x BN output tile (BM = 64: 1 x 4 waves,
+//     BN = 256; BM = 128: 2 x 2 waves, BN = 128); each wave a 64 x 64 piece:
+//     4 row groups x 4 column groups of 16 = 16 MFMAs per Q8_0 block;
+//   * one 16x16x32 MFMA is exactly one Q8_0 block (K = 32), so every D is a
+//     single block's dot and takes its own scale on the vector ALU:
+//     acc += s[b,n] * D (int8: (dx[r,b] * s[b,n]) * D);
+//   * the activation rows and the weight chunks of kGemmCB blocks are staged
+//     in LDS by the whole workgroup (16-byte pieces, coalesced), double
+//     buffered: the next stage's global loads are in flight while the current
+//     stage is computed.  The weight's packed chunks are copied as they are:
+//     their byte order already is the MFMA B-operand order;
+//   * workgroups are numbered so that each XCD walks a contiguous range of
+//     (row block, column block) pairs with the row block fastest: the row
+//     blocks that read one weight tile run together on one XCD, and its L2
+//     serves the weight to all of them.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q8_device.h"
+#include "q8_internal.h"
+
+namespace q8 {
+namespace {
+
+using namespace dev;
+
+constexpr int kGemmCB = 2;        // Q8_0 blocks per LDS stage
+constexpr int kGemmThreads = 256;
+
+template <int ACT, int BM>
+struct GemmShape {
+  static constexpr int WM = BM / 64;            // waves along M
+  static constexpr int WN = 4 / WM;             // waves along N, one 64-column tile each
+  static constexpr int BN = 64 * WN;
+  static constexpr int kRowB = ACT == kActBf16 ? 64 : 32;   // activation bytes, one row x block
+  static constexpr int kA = kGemmCB * BM * kRowB;           // activation bytes per stage
+  static constexpr int kDx = ACT == kActBf16 ? 0 : kGemmCB * BM * 4;   // int8 row scales
+  static constexpr int kW = WN * kGemmCB * kChunkBytes;     // weight values per stage
+  static constexpr int kS = WN * kGemmCB * kTile * 4;       // weight scales per stage
+  static constexpr int kStage = kA + kDx + kW + kS;
+  static constexpr int kPieces = (kA + kW + kS) / 16;       // 16-byte staging pieces
+  static constexpr int kPer = (kPieces + kGemmThreads - 1) / kGemmThreads;
+  static constexpr int kDxPer = (kGemmCB * BM + kGemmThreads - 1) / kGemmThreads;
+  static_assert(kA % (16 * 64) == 0 && kW % (16 * 64) == 0 && kS % (16 * 64) == 0,
+                "each wave's staging pieces fall in one region");
+};
+
+// Registers holding one stage between its global loads and its LDS write.
+template <int ACT, int BM>
+struct GemmStaging {
+  uint4 v[GemmShape<ACT, BM>::kPer];
+  float dx[GemmShape<ACT, BM>::kDxPer];
+};
+
+// Issue the global loads of stage (blocks b0 .. b0 + kGemmCB - 1) of the
+// workgroup's row block (rows row0 ..) and column tiles (t0 ..).  Pieces
+// outside the activation's rows, the weight's tiles or K are loaded from a
+// clamped, valid address and zeroed at the LDS write.
+template <int ACT, int BM, bool DOTS>
+__device__ __forceinline__ void gemm_load(GemmStaging<ACT, BM> &st, const void *__restrict__ xv,
+                                          const int8_t *__restrict__ wq,
+                                          const float *__restrict__ wsc, int m, int K, int NB,
+                                          int T, int row0, int t0, int b0,
+                                          unsigned act_scale_off) {
+  using S = GemmShape<ACT, BM>;
+  constexpr int kPPB = S::kRowB / 16;   // pieces per row and block
+#pragma unroll
+  for (int k = 0; k < S::kPer; ++k) {
+    const int p = k * kGemmThreads + (int)threadIdx.x;
+    const char *src;
+    if (p < S::kA / 16) {
+      // activation: p = (r * CB + cb) * kPPB + q  (a row's stage is contiguous)
+      const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
+      const int row = min(row0 + r, m - 1), b = min(b0 + cb, NB - 1);
+      src = static_cast<const char *>(xv) +
+            ((size_t)row * K + (size_t)b * kBlock) * (ACT == kActBf16 ? 2 : 1) + q * 16;
+    } else if (p < (S::kA + S::kW) / 16) {
+      // weight values: p' = (wn * CB + cb) * 128 + q, chunk (t0 + wn, b)
+      const int pp = p - S::kA / 16;
+      const int q = pp % 128, cb = (pp / 128) % kGemmCB, wn = pp / (128 * kGemmCB);
+      const int t = min(t0 + wn, T - 1), b = min(b0 + cb, NB - 1);
+      src = reinterpret_cast<const char *>(wq) + ((size_t)t * NB + b) * kChunkBytes + q * 16;
+    } else {
+      // weight scales: p' = (wn * CB + cb) * 16 + q, the chunk's 256-byte row
+      // (the block-dot form has no scales: nothing is read)
+      if constexpr (DOTS) {
+        st.v[k] = make_uint4(0u, 0u, 0u, 0u);
+        continue;
+      }
+      const int pp = min(p - (S::kA + S::kW) / 16, S::kS / 16 - 1);
+      const int q = pp % 16, cb = (pp / 16) % kGemmCB, wn = pp / (16 * kGemmCB);
+      const int t = min(t0 + wn, T - 1), b = min(b0 + cb, NB - 1);
+      src = reinterpret_cast<const char *>(wsc) + (((size_t)t * NB + b) * kTile) * 4 + q * 16;
+    }
+    st.v[k] = *reinterpret_cast<const uint4 *>(src);
+  }
+  if constexpr (ACT == kActQ8) {
+    const float *dxp = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
+                                                       act_scale_off);
+#pragma unroll
+    for (int k = 0; k < S::kDxPer; ++k) {
+      const int p = min(k * kGemmThreads + (int)threadIdx.x, kGemmCB * BM - 1);
+      const int cb = p / BM, r = p % BM;   // LDS order [cb][r]
+      st.dx[k] = dxp[(size_t)min(row0 + r, m - 1) * NB + min(b0 + cb, NB - 1)];
+    }
+  }
+}
+
+// Write a loaded stage into LDS buffer `buf`, zeroing what lies outside.
+template <int ACT, int BM>
+__device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st, char *buf, int m,
+                                           int NB, int T, int row0, int t0, int b0) {
+  using S = GemmShape<ACT, BM>;
+  constexpr int kPPB = S::kRowB / 16;
+#pragma unroll
+  for (int k = 0; k < S::kPer; ++k) {
+    const int p = k * kGemmThreads + (int)threadIdx.x;
+    if (p >= S::kPieces) break;
+    uint4 v = st.v[k];
+    int dst;
+    bool ok;
+    if (p < S::kA / 16) {
+      const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
+      ok = row0 + r < m && b0 + cb < NB;
+      dst = (cb * BM + r) * S::kRowB + q * 16;
+    } else if (p < (S::kA + S::kW) / 16) {
+      const int pp = p - S::kA / 16;
+      const int q = pp % 128, cb = (pp / 128) % kGemmCB, wn = pp / (128 * kGemmCB);
+      ok = t0 + wn < T && b0 + cb < NB;
+      dst = S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes + q * 16;
+    } else {
+      const int pp = p - (S::kA + S::kW) / 16;
+      const int q = pp % 16, cb = (pp / 16) % kGemmCB, wn = pp / (16 * kGemmCB);
+      ok = t0 + wn < T && b0 + cb < NB;
+      dst = S::kA + S::kDx + S::kW + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
+    }
+    if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4 *>(buf + dst) = v;
+  }
+  if constexpr (ACT == kActQ8) {
+    float *dxs = reinterpret_cast<float *>(buf + S::kA);
+#pragma unroll
+    for (int k = 0; k < S::kDxPer; ++k) {
+      const int p = k * kGemmThreads + (int)threadIdx.x;
+      if (p >= kGemmCB * BM) break;
+      const int cb = p / BM, r = p % BM;
+      dxs[p] = (row0 + r < m && b0 + cb < NB) ? st.dx[k] : 0.0f;
+    }
+  }
+}
+
+template <int ACT, int BM, bool DOTS>
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
+            const float *__restrict__ wsc, float *__restrict__ y, int32_t *__restrict__ dots,
+            int m, int K, int NB, int Npad, int T, int MB, int NBN, unsigned act_scale_off) {
+  using S = GemmShape<ACT, BM>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+
+  // XCD-aware numbering: workgroups are dealt round-robin over the 8 XCDs,
+  // so (when the grid divides) give XCD x the logical range x*G/8 ...
+  const int G = MB * NBN;
+  const int bid = (int)blockIdx.x;
+  const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int mb = logical % MB, nb = logical / MB;
+  const int row0 = mb * BM, t0 = nb * S::WN;
+
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lj = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int wm = wave / S::WN, wn = wave % S::WN;
+  const int t = t0 + wn;   // this wave's 64-column tile
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[rt][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int NC = (NB + kGemmCB - 1) / kGemmCB;
+  GemmStaging<ACT, BM> st;
+  gemm_load<ACT, BM, DOTS>(st, xv, wq, wsc, m, K, NB, T, row0, t0, 0, act_scale_off);
+  gemm_store<ACT, BM>(st, lds, m, NB, T, row0, t0, 0);
+  __syncthreads();
+
+  // lane's bytes of a chunk: half j/2, column 16g + i, k offset 8 * (j % 2)
+  const int w_lane = (lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
+  for (int c = 0; c < NC; ++c) {
+    const int b0 = c * kGemmCB;
+    if (c + 1 < NC)
+      gemm_load<ACT, BM, DOTS>(st, xv, wq, wsc, m, K, NB, T, row0, t0, b0 + kGemmCB,
+                               act_scale_off);
+    const char *buf = lds + (c & 1) * S::kStage;
+#pragma unroll
+    for (int cb = 0; cb < kGemmCB; ++cb) {
+      const int b = b0 + cb;
+      if (b >= NB) break;
+      const char *As = buf + cb * BM * S::kRowB;
+      const char *Ws = buf + S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes;
+      uint2 bw[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bw[g] = *reinterpret_cast<const uint2 *>(Ws + w_lane + g * 256);
+      float4 sc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if constexpr (!DOTS)
+        sc = *reinterpret_cast<const float4 *>(buf + S::kA + S::kDx + S::kW +
+                                               ((wn * kGemmCB + cb) * kTile + 4 * li) * 4);
+      const float scs[4] = {sc.x, sc.y, sc.z, sc.w};
+      if constexpr (ACT == kActBf16) {
+        bf16x8_t bb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bb[g] = i8x8_to_bf16(bw[g]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+              As + (wm * 64 + rt * 16 + li) * S::kRowB + lj * 16);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, bb[g], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rt][g][e] = fmaf(scs[g], d[e], acc[rt][g][e]);
+          }
+        }
+      } else {
+        const float *dxs = reinterpret_cast<const float *>(buf + S::kA) + cb * BM;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const long a = *reinterpret_cast<const long *>(
+              As + (wm * 64 + rt * 16 + li) * S::kRowB + lj * 8);
+          float dxv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (!DOTS) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(dxs + wm * 64 + rt * 16 + lj * 4);
+            dxv[0] = d4.x; dxv[1] = d4.y; dxv[2] = d4.z; dxv[3] = d4.w;
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                a, __builtin_bit_cast(long, bw[g]), i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+            if constexpr (DOTS) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = row0 + wm * 64 + rt * 16 + lj * 4 + e;
+                if (r < m && t < T)
+                  dots[((size_t)r * NB + b) * Npad + (size_t)t * kTile + g * 16 + li] = d[e];
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[rt][g][e] = fmaf(dxv[e] * scs[g], (float)d[e], acc[rt][g][e]);
+            }
+          }
+        }
+      }
+    }
+    if (c + 1 < NC)
+      gemm_store<ACT, BM>(st, lds + ((c + 1) & 1) * S::kStage, m, NB, T, row0, t0,
+                          b0 + kGemmCB);
+    __syncthreads();
+  }
+  if constexpr (DOTS) return;
+
+  if (t >= T) return;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = row0 + wm * 64 + rt * 16 + lj * 4 + e;
+      if (r < m) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          y[(size_t)r * Npad + (size_t)t * kTile + g * 16 + li] = acc[rt][g][e];
+      }
+    }
+}
+
+template <int ACT, int BM, bool DOTS>
+hipError_t launch_gemm_k(const GemmArgs &a, hipStream_t stream) {
+  using S = GemmShape<ACT, BM>;
+  const int MB = (a.m + BM - 1) / BM;
+  const int NBN = (a.T + S::WN - 1) / S::WN;
+  const size_t lds = 2 * (size_t)S::kStage;
+  auto kern = gemm_kernel<ACT, BM, DOTS>;
+  static bool granted = false;
+  if (!granted && lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    granted = true;
+  }
+  (void)hipGetLastError();
+  kern<<<dim3((unsigned)(MB * NBN)), dim3(kGemmThreads), lds, stream>>>(
+      a.x, a.wq, a.wsc, a.y, a.dots, a.m, a.K, a.NB, a.Npad, a.T, MB, NBN, a.act_scale_off);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_rows_per_block(int64_t m) { return m > 64 ? 128 : 64; }
+
+hipError_t launch_gemm(int act, bool write_dots, int bm, const GemmArgs &a, hipStream_t stream) {
+  if (act == kActBf16 && !write_dots) {
+    if (bm == 64) return launch_gemm_k<kActBf16, 64, false>(a, stream);
+    if (bm == 128) return launch_gemm_k<kActBf16, 128, false>(a, stream);
+  }
+  if (act == kActQ8) {
+    if (bm == 64)
+      return write_dots ? launch_gemm_k<kActQ8, 64, true>(a, stream)
+                        : launch_gemm_k<kActQ8, 64, false>(a, stream);
+    if (bm == 128)
+      return write_dots ? launch_gemm_k<kActQ8, 128, true>(a, stream)
+                        : launch_gemm_k<kActQ8, 128, false>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q8

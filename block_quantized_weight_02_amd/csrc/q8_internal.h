@@ -85,4 +85,18 @@ bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves
 size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int NB,
                       int split_k);
 
+// The many-row product (q8_gemm.hip): no split, no workspace.
+struct GemmArgs {
+  const void *x;
+  const int8_t *wq;
+  const float *wsc;
+  float *y;
+  int32_t *dots;           // non-null: write the int32 block dots instead of y
+  int m, K, NB, Npad, T;
+  unsigned act_scale_off;
+};
+// Output rows per workgroup the GEMM takes for m rows (64 or 128).
+int gemm_rows_per_block(int64_t m);
+hipError_t launch_gemm(int act, bool write_dots, int bm, const GemmArgs &a, hipStream_t stream);
+
 }  // namespace q8

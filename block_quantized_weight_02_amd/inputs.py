@@ -55,6 +55,12 @@ WORKLOADS: Dict[str, Workload] = {
                                        note="m=32 Q8_0 activations, vocabulary-wide N"),
     "decode_k4096_n14336": Workload("decode_k4096_n14336", 1, 4096, 14336, "bf16", 1006, 1006,
                                     note="m=1 decode gate/up projection, the headline shape"),
+    "prefill_m512_k4096_n14336": Workload("prefill_m512_k4096_n14336", 512, 4096, 14336, "bf16",
+                                          1007, 1007,
+                                          note="m=512 prefill chunk through the gate/up projection"),
+    "prefill_q8act_m512_k4096_n14336": Workload("prefill_q8act_m512_k4096_n14336", 512, 4096, 14336,
+                                                "q8_0", 1008, 1008,
+                                                note="the same chunk with Q8_0 activations"),
 }
 
 HEADLINE = "decode_k4096_n14336"

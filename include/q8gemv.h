@@ -120,8 +120,8 @@ int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K,
  * The pages do not give the formula; this library computes
  *     amax = max|x|,  d = fp32(amax / 127)  (amax == 0: d = 0, xq = 0),
  *     xq   = clamp(round_half_away_from_zero(fp32(x / d)), -127, 127)
- * with correctly rounded divisions.  Requires 1 <= m <= 32, K > 0,
- * K % 32 == 0.  x_q8 receives q8_act_bytes(m, K) bytes.
+ * with correctly rounded divisions.  Requires 1 <= m <= Q8_MAX_GEMM_ROWS,
+ * K > 0, K % 32 == 0.  x_q8 receives q8_act_bytes(m, K) bytes.
  */
 int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
                     hipStream_t stream);
@@ -291,6 +291,32 @@ int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
                              q8_plan *plan);
 size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K,
                               int64_t N);
+
+/* ---- many rows: the prefill product ----------------------------------------- */
+
+/* Rows the many-row product accepts. */
+#define Q8_MAX_GEMM_ROWS 8192
+
+/*
+ * q8_gemm: y = x . W for 1 <= m <= Q8_MAX_GEMM_ROWS activation rows (a prefill
+ * chunk), over the same packed weight as q8_gemv, with the same arithmetic
+ * (per-block dots scaled once per block, fp32 carry) and the same layouts: x
+ * m x K bf16 or the q8_quantize_act buffer of m rows, y m x N_pad fp32 (pad
+ * columns 0).  The pages' CUDA planner runs the product as a tensor-core GEMM
+ * above its GEMV's rows (codegen_cuda/lane/plan.rs, Launch::on_tensor_cores,
+ * gemm_blk_rows); this is its matrix-core form on gfx950.  No workspace; the
+ * call allocates nothing.  Requires K > 0, K % 32 == 0, N >= 1.
+ */
+int q8_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+            float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+            hipStream_t stream);
+
+/*
+ * q8_gemm_block_dots: test hook of q8_gemm's int8 path: the exact per-block
+ * int32 dots, m x K/32 x N_pad, as q8_gemv_block_dots writes them.
+ */
+int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
+                       int64_t m, int64_t K, int64_t N, hipStream_t stream);
 
 /* ---- errors and resources ------------------------------------------------ */
 

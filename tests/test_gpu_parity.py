@@ -230,7 +230,7 @@ def _sample_cols(N, n=384, seed=0):
     return np.array(sorted(c for c in fixed | pick if 0 <= c < N), np.int64)
 
 
-@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+@pytest.mark.parametrize("name", [n for n, w in inputs.WORKLOADS.items() if w.m <= q8.Q8_MAX_ROWS])
 def test_workload_full_size(name):
     w = inputs.WORKLOADS[name]
     x, q, s = inputs.generate(w)

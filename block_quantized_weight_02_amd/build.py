@@ -17,6 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq8gemv.so")
 SOURCES = ["q8_kernels.hip", "q8_gemm.hip", "q8_api.cpp"]
+# Per-source device flags.  The GEMM writes its MFMA results to VGPRs (by
+# default the compiler routes them through one AGPR quad and serialises the
+# matrix core behind its reads).
+SOURCE_FLAGS = {"q8_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("Q8_OFFLOAD_ARCH", "gfx950")
 
 
@@ -49,7 +53,7 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
              "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra]
     with tempfile.TemporaryDirectory(prefix="q8build") as d:
         objs = [os.path.join(d, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-        cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o]
+        cmds = [[hipcc(), *flags, *SOURCE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
                 for s, o in zip(SOURCES, objs)]
         with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -57,112 +57,178 @@ struct GemmShape {
                 "each wave's staging pieces fall in one region");
 };
 
-// Registers holding one stage between its global loads and its LDS write.
+// Byte offset, within one row's staged activation, of 16-byte part q of row
+// r: the parts of a row are permuted by (r / 4) % 4 (bf16) or 8-byte units
+// by 2 * ((r / 8) % 2) (int8), so the 16 rows an MFMA operand read touches
+// land in distinct LDS banks.
+template <int ACT>
+__device__ __forceinline__ int a_part(int r, int unit) {
+  if constexpr (ACT == kActBf16) return (unit ^ ((r >> 2) & 3)) * 16;   // unit: 16-byte part
+  else return (unit ^ (((r >> 3) & 1) << 1)) * 8;                      // unit: 8-byte part
+}
+
+// One thread's share of a stage: which 16-byte pieces it copies, from where
+// (an offset from the stage's wave-uniform region base) and to where in LDS.
+// Computed once per workgroup; a stage only moves the region bases:
+//   activation: row0's row at the stage's first block;
+//   weight values / scales: tile t0's chunk / scale row of that block.
+// Thread tid copies activation pieces tid + 256k (k < kNA), weight pieces
+// tid + 256k (k < kNW) and, when tid < kNS, scale piece tid.  Rows past m and
+// tiles past T are clamped to valid ones: their LDS rows and columns feed
+// only outputs that are never stored.
 template <int ACT, int BM>
-struct GemmStaging {
-  uint4 v[GemmShape<ACT, BM>::kPer];
-  float dx[GemmShape<ACT, BM>::kDxPer];
+struct GemmPlan {
+  using S = GemmShape<ACT, BM>;
+  static constexpr int kNA = S::kA / 16 / kGemmThreads;
+  static constexpr int kNW = S::kW / 16 / kGemmThreads;
+  static constexpr int kNS = S::kS / 16;   // pieces; threads below it copy one
+  static_assert(S::kA % (16 * kGemmThreads) == 0 && S::kW % (16 * kGemmThreads) == 0 &&
+                kNS <= kGemmThreads && kNS % 64 == 0, "whole pieces per thread, whole waves");
+  unsigned asrc[kNA], wsrc[kNW], ssrc;   // byte offsets from the region bases
+  int adst[kNA], adst2[kNA], wdst[kNW], sdst;
+  int acb[kNA], wcb[kNW], scb;           // the piece's block within the stage
+  unsigned dxsrc[S::kDxPer];
+  int dxcb[S::kDxPer];
 };
 
-// Issue the global loads of stage (blocks b0 .. b0 + kGemmCB - 1) of the
-// workgroup's row block (rows row0 ..) and column tiles (t0 ..).  Pieces
-// outside the activation's rows, the weight's tiles or K are loaded from a
-// clamped, valid address and zeroed at the LDS write.
-template <int ACT, int BM, bool DOTS>
-__device__ __forceinline__ void gemm_load(GemmStaging<ACT, BM> &st, const void *__restrict__ xv,
-                                          const int8_t *__restrict__ wq,
-                                          const float *__restrict__ wsc, int m, int K, int NB,
-                                          int T, int row0, int t0, int b0,
-                                          unsigned act_scale_off) {
+template <int ACT, int BM>
+__device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, int NB, int T,
+                                          int row0, int t0) {
   using S = GemmShape<ACT, BM>;
-  constexpr int kPPB = S::kRowB / 16;   // pieces per row and block
+  using P = GemmPlan<ACT, BM>;
+  constexpr int kPPB = S::kRowB / 16;
+  constexpr int kElt = ACT == kActBf16 ? 2 : 1;
+  const int tid = (int)threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < S::kPer; ++k) {
-    const int p = k * kGemmThreads + (int)threadIdx.x;
-    const char *src;
-    if (p < S::kA / 16) {
-      // activation: p = (r * CB + cb) * kPPB + q  (a row's stage is contiguous)
-      const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
-      const int row = min(row0 + r, m - 1), b = min(b0 + cb, NB - 1);
-      src = static_cast<const char *>(xv) +
-            ((size_t)row * K + (size_t)b * kBlock) * (ACT == kActBf16 ? 2 : 1) + q * 16;
-    } else if (p < (S::kA + S::kW) / 16) {
-      // weight values: p' = (wn * CB + cb) * 128 + q, chunk (t0 + wn, b)
-      const int pp = p - S::kA / 16;
-      const int q = pp % 128, cb = (pp / 128) % kGemmCB, wn = pp / (128 * kGemmCB);
-      const int t = min(t0 + wn, T - 1), b = min(b0 + cb, NB - 1);
-      src = reinterpret_cast<const char *>(wq) + ((size_t)t * NB + b) * kChunkBytes + q * 16;
+  for (int k = 0; k < P::kNA; ++k) {
+    const int p = k * kGemmThreads + tid;
+    const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
+    const int rc = min(row0 + r, m - 1) - row0;
+    pl.asrc[k] = (unsigned)rc * (unsigned)K * kElt + cb * kBlock * kElt + q * 16;
+    pl.acb[k] = cb;
+    if constexpr (ACT == kActBf16) {
+      pl.adst[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, q);
+      pl.adst2[k] = 0;
     } else {
-      // weight scales: p' = (wn * CB + cb) * 16 + q, the chunk's 256-byte row
-      // (the block-dot form has no scales: nothing is read)
-      if constexpr (DOTS) {
-        st.v[k] = make_uint4(0u, 0u, 0u, 0u);
-        continue;
-      }
-      const int pp = min(p - (S::kA + S::kW) / 16, S::kS / 16 - 1);
-      const int q = pp % 16, cb = (pp / 16) % kGemmCB, wn = pp / (16 * kGemmCB);
-      const int t = min(t0 + wn, T - 1), b = min(b0 + cb, NB - 1);
-      src = reinterpret_cast<const char *>(wsc) + (((size_t)t * NB + b) * kTile) * 4 + q * 16;
+      pl.adst[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, 2 * q);
+      pl.adst2[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, 2 * q + 1);
     }
-    st.v[k] = *reinterpret_cast<const uint4 *>(src);
+  }
+#pragma unroll
+  for (int k = 0; k < P::kNW; ++k) {
+    const int p = k * kGemmThreads + tid;
+    const int q = p % 128, cb = (p / 128) % kGemmCB, wn = p / (128 * kGemmCB);
+    const int tc = min(t0 + wn, T - 1) - t0;
+    pl.wsrc[k] = ((unsigned)tc * NB + cb) * kChunkBytes + q * 16;
+    pl.wcb[k] = cb;
+    pl.wdst[k] = S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes + q * 16;
+  }
+  {
+    const int p = min(tid, P::kNS - 1);
+    const int q = p % 16, cb = (p / 16) % kGemmCB, wn = p / (16 * kGemmCB);
+    const int tc = min(t0 + wn, T - 1) - t0;
+    pl.ssrc = ((unsigned)tc * NB + cb) * (kTile * 4) + q * 16;
+    pl.scb = cb;
+    pl.sdst = S::kA + S::kDx + S::kW + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
   }
   if constexpr (ACT == kActQ8) {
-    const float *dxp = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
-                                                       act_scale_off);
 #pragma unroll
     for (int k = 0; k < S::kDxPer; ++k) {
-      const int p = min(k * kGemmThreads + (int)threadIdx.x, kGemmCB * BM - 1);
+      const int p = min(k * kGemmThreads + tid, kGemmCB * BM - 1);
       const int cb = p / BM, r = p % BM;   // LDS order [cb][r]
-      st.dx[k] = dxp[(size_t)min(row0 + r, m - 1) * NB + min(b0 + cb, NB - 1)];
+      pl.dxsrc[k] = (unsigned)(min(row0 + r, m - 1) - row0) * NB + cb;
+      pl.dxcb[k] = cb;
     }
   }
 }
 
-// Write a loaded stage into LDS buffer `buf`, zeroing what lies outside.
+// Registers holding one stage between its global loads and its LDS write.
 template <int ACT, int BM>
-__device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st, char *buf, int m,
-                                           int NB, int T, int row0, int t0, int b0) {
-  using S = GemmShape<ACT, BM>;
-  constexpr int kPPB = S::kRowB / 16;
+struct GemmStaging {
+  using P = GemmPlan<ACT, BM>;
+  u32x4_t va[P::kNA], vw[P::kNW], vs;   // native vectors (a uint4 struct copy becomes a
+                                        // memcpy that keeps the array in scratch memory)
+  float dx[GemmShape<ACT, BM>::kDxPer];
+};
+
+// Issue the global loads of a stage.  nvalid: the stage's blocks inside K.
+// Pieces of later blocks (the last stage only) reload the stage's last block
+// in K instead -- in bounds, and those LDS blocks are never computed.  Loads
+// and stores are unconditional (a staging array written under divergent
+// conditions would be kept in scratch memory).
+template <int ACT, int BM, bool DOTS>
+__device__ __forceinline__ void gemm_load(GemmStaging<ACT, BM> &st, const GemmPlan<ACT, BM> &pl,
+                                          const char *abase, const char *wbase,
+                                          const char *sbase, const float *dxbase, int nvalid) {
+  using P = GemmPlan<ACT, BM>;
+  constexpr unsigned kAStride = kBlock * (ACT == kActBf16 ? 2 : 1);   // one block of a row
+  if (nvalid >= kGemmCB) {
 #pragma unroll
-  for (int k = 0; k < S::kPer; ++k) {
-    const int p = k * kGemmThreads + (int)threadIdx.x;
-    if (p >= S::kPieces) break;
-    uint4 v = st.v[k];
-    int dst;
-    bool ok;
-    if (p < S::kA / 16) {
-      const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
-      ok = row0 + r < m && b0 + cb < NB;
-      dst = (cb * BM + r) * S::kRowB + q * 16;
-    } else if (p < (S::kA + S::kW) / 16) {
-      const int pp = p - S::kA / 16;
-      const int q = pp % 128, cb = (pp / 128) % kGemmCB, wn = pp / (128 * kGemmCB);
-      ok = t0 + wn < T && b0 + cb < NB;
-      dst = S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes + q * 16;
-    } else {
-      const int pp = p - (S::kA + S::kW) / 16;
-      const int q = pp % 16, cb = (pp / 16) % kGemmCB, wn = pp / (16 * kGemmCB);
-      ok = t0 + wn < T && b0 + cb < NB;
-      dst = S::kA + S::kDx + S::kW + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
+    for (int k = 0; k < P::kNA; ++k) st.va[k] = *reinterpret_cast<const u32x4_t *>(abase + pl.asrc[k]);
+#pragma unroll
+    for (int k = 0; k < P::kNW; ++k) st.vw[k] = *reinterpret_cast<const u32x4_t *>(wbase + pl.wsrc[k]);
+    if (!DOTS && (int)threadIdx.x < P::kNS)
+      st.vs = *reinterpret_cast<const u32x4_t *>(sbase + pl.ssrc);
+    if constexpr (ACT == kActQ8 && !DOTS) {
+#pragma unroll
+      for (int k = 0; k < GemmShape<ACT, BM>::kDxPer; ++k) st.dx[k] = dxbase[pl.dxsrc[k]];
     }
-    if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4 *>(buf + dst) = v;
+  } else {
+    // back off by the blocks past K
+#pragma unroll
+    for (int k = 0; k < P::kNA; ++k) {
+      const unsigned back = (unsigned)max(pl.acb[k] - nvalid + 1, 0);
+      st.va[k] = *reinterpret_cast<const u32x4_t *>(abase + pl.asrc[k] - back * kAStride);
+    }
+#pragma unroll
+    for (int k = 0; k < P::kNW; ++k) {
+      const unsigned back = (unsigned)max(pl.wcb[k] - nvalid + 1, 0);
+      st.vw[k] = *reinterpret_cast<const u32x4_t *>(wbase + pl.wsrc[k] - back * kChunkBytes);
+    }
+    if (!DOTS && (int)threadIdx.x < P::kNS) {
+      const unsigned back = (unsigned)max(pl.scb - nvalid + 1, 0);
+      st.vs = *reinterpret_cast<const u32x4_t *>(sbase + pl.ssrc - back * (kTile * 4));
+    }
+    if constexpr (ACT == kActQ8 && !DOTS) {
+#pragma unroll
+      for (int k = 0; k < GemmShape<ACT, BM>::kDxPer; ++k)
+        st.dx[k] = dxbase[pl.dxsrc[k] - (unsigned)max(pl.dxcb[k] - nvalid + 1, 0)];
+    }
   }
-  if constexpr (ACT == kActQ8) {
+}
+
+// Write a loaded stage into LDS buffer `buf`.
+template <int ACT, int BM, bool DOTS>
+__device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st,
+                                           const GemmPlan<ACT, BM> &pl, char *buf) {
+  using S = GemmShape<ACT, BM>;
+  using P = GemmPlan<ACT, BM>;
+#pragma unroll
+  for (int k = 0; k < P::kNA; ++k) {
+    if constexpr (ACT == kActQ8) {
+      *reinterpret_cast<u32x2_t *>(buf + pl.adst[k]) = u32x2_t{st.va[k].x, st.va[k].y};
+      *reinterpret_cast<u32x2_t *>(buf + pl.adst2[k]) = u32x2_t{st.va[k].z, st.va[k].w};
+    } else {
+      *reinterpret_cast<u32x4_t *>(buf + pl.adst[k]) = st.va[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < P::kNW; ++k) *reinterpret_cast<u32x4_t *>(buf + pl.wdst[k]) = st.vw[k];
+  if (!DOTS && (int)threadIdx.x < P::kNS) *reinterpret_cast<u32x4_t *>(buf + pl.sdst) = st.vs;
+  if constexpr (ACT == kActQ8 && !DOTS) {
     float *dxs = reinterpret_cast<float *>(buf + S::kA);
 #pragma unroll
     for (int k = 0; k < S::kDxPer; ++k) {
       const int p = k * kGemmThreads + (int)threadIdx.x;
-      if (p >= kGemmCB * BM) break;
-      const int cb = p / BM, r = p % BM;
-      dxs[p] = (row0 + r < m && b0 + cb < NB) ? st.dx[k] : 0.0f;
+      if (p < kGemmCB * BM) dxs[p] = st.dx[k];
     }
   }
 }
 
+// Two workgroups per CU (8 waves): the register budget is then 256 per lane,
+// which the accumulators, the in-flight stage and its descriptors need.
 template <int ACT, int BM, bool DOTS>
-__global__ void __launch_bounds__(kGemmThreads)
+__global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
             const float *__restrict__ wsc, float *__restrict__ y, int32_t *__restrict__ dots,
             int m, int K, int NB, int Npad, int T, int MB, int NBN, unsigned act_scale_off) {
@@ -190,18 +256,31 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     for (int g = 0; g < 4; ++g) acc[rt][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int NC = (NB + kGemmCB - 1) / kGemmCB;
+  constexpr int kElt = ACT == kActBf16 ? 2 : 1;
+  GemmPlan<ACT, BM> pl;
+  gemm_plan<ACT, BM>(pl, m, K, NB, T, row0, t0);
+  // the regions' bases at stage 0; each stage advances them by kGemmCB blocks
+  const char *abase = static_cast<const char *>(xv) + (size_t)row0 * K * kElt;
+  const char *wbase = reinterpret_cast<const char *>(wq) + (size_t)t0 * NB * kChunkBytes;
+  const char *sbase = reinterpret_cast<const char *>(wsc) + (size_t)t0 * NB * kTile * 4;
+  const float *dxbase = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
+                                                        act_scale_off) + (size_t)row0 * NB;
   GemmStaging<ACT, BM> st;
-  gemm_load<ACT, BM, DOTS>(st, xv, wq, wsc, m, K, NB, T, row0, t0, 0, act_scale_off);
-  gemm_store<ACT, BM>(st, lds, m, NB, T, row0, t0, 0);
+  gemm_load<ACT, BM, DOTS>(st, pl, abase, wbase, sbase, dxbase, min(NB, kGemmCB));
+  gemm_store<ACT, BM, DOTS>(st, pl, lds);
   __syncthreads();
 
   // lane's bytes of a chunk: half j/2, column 16g + i, k offset 8 * (j % 2)
   const int w_lane = (lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
+  // lane's activation bytes within a row (rows 16rt + i: the swizzle depends on i)
+  const int a_lane = ACT == kActBf16 ? a_part<ACT>(li, lj) : a_part<ACT>(li, lj);
   for (int c = 0; c < NC; ++c) {
     const int b0 = c * kGemmCB;
     if (c + 1 < NC)
-      gemm_load<ACT, BM, DOTS>(st, xv, wq, wsc, m, K, NB, T, row0, t0, b0 + kGemmCB,
-                               act_scale_off);
+      gemm_load<ACT, BM, DOTS>(st, pl, abase + (size_t)(b0 + kGemmCB) * kBlock * kElt,
+                               wbase + (size_t)(b0 + kGemmCB) * kChunkBytes,
+                               sbase + (size_t)(b0 + kGemmCB) * kTile * 4,
+                               dxbase + b0 + kGemmCB, min(NB - b0 - kGemmCB, kGemmCB));
     const char *buf = lds + (c & 1) * S::kStage;
 #pragma unroll
     for (int cb = 0; cb < kGemmCB; ++cb) {
@@ -221,24 +300,28 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         bf16x8_t bb[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) bb[g] = i8x8_to_bf16(bw[g]);
+        // Per row group: the four MFMAs first (independent, so the matrix
+        // core pipelines them), then their sixteen scale FMAs.
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-              As + (wm * 64 + rt * 16 + li) * S::kRowB + lj * 16);
+              As + (wm * 64 + rt * 16 + li) * S::kRowB + a_lane);
+          f32x4_t d[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, bb[g], f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          for (int g = 0; g < 4; ++g)
+            d[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb[g],
+                                                           f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rt][g][e] = fmaf(scs[g], d[e], acc[rt][g][e]);
-          }
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rt][g][e] = fmaf(scs[g], d[g][e], acc[rt][g][e]);
         }
       } else {
         const float *dxs = reinterpret_cast<const float *>(buf + S::kA) + cb * BM;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const long a = *reinterpret_cast<const long *>(
-              As + (wm * 64 + rt * 16 + li) * S::kRowB + lj * 8);
+              As + (wm * 64 + rt * 16 + li) * S::kRowB + a_lane);
           float dxv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if constexpr (!DOTS) {
             const float4 d4 = *reinterpret_cast<const float4 *>(dxs + wm * 64 + rt * 16 + lj * 4);
@@ -265,8 +348,7 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       }
     }
     if (c + 1 < NC)
-      gemm_store<ACT, BM>(st, lds + ((c + 1) & 1) * S::kStage, m, NB, T, row0, t0,
-                          b0 + kGemmCB);
+      gemm_store<ACT, BM, DOTS>(st, pl, lds + ((c + 1) & 1) * S::kStage);
     __syncthreads();
   }
   if constexpr (DOTS) return;

@@ -24,7 +24,8 @@ the timed steps; `roofline` prices the product kernel's own average duration
 times the product with bias, residual and quantized output beside the plain
 product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
 one launch) beside two plain products, at m = 1 and m = 16; `context` gives
-the headline with one weight copy reused and a 1 GiB device copy's rate.
+the headline with one weight copy reused and a 1 GiB device copy's rate;
+`prefill` times the many-row product (m = 512) against the MFMA peak.
 """
 import argparse
 import hashlib
@@ -140,7 +141,7 @@ class Setup:
         self._gemv_args = [(xin, Wq.data_ptr(), Ws.data_ptr(), self.y.data_ptr(), m, K, N, act, sp)
                            for (Wq, Ws) in self.W]
         self._quant_args = (self.x.data_ptr(), self.xq.data_ptr(), m, K, sp)
-        self.plan = q8.q8_gemv_default_plan(m, K, N, act)
+        self.plan = q8.q8_gemv_default_plan(m, K, N, act) if m <= q8.Q8_MAX_ROWS else None
 
     def step(self, i):
         if self.w.act != "bf16":
@@ -323,6 +324,53 @@ def measure_glu(w, steps, warmup, rotate=True):
                      "waves": plan.waves, "kslices": plan.kslices}}
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "q8_0": 5000.0}   # MI355X dense, published
+
+
+def measure_gemm(w, steps, warmup, rotate=True):
+    """The many-row product (prefill chunk): q8_gemm per step; with Q8_0
+    activations the step also quantizes them (reported apart too)."""
+    import torch
+    st = Setup(w, rotate=rotate)
+    q8 = st.q8
+    m, K, N = w.m, w.K, w.N
+    act = q8.Q8_ACT_BF16 if w.act == "bf16" else q8.Q8_ACT_Q8_0
+    gemm = q8.lib().q8_gemm
+    xin = st.x.data_ptr() if w.act == "bf16" else st.xq.data_ptr()
+    sp = st.stream.cuda_stream
+    args = [(xin, Wq.data_ptr(), Ws.data_ptr(), st.y.data_ptr(), m, K, N, act, sp)
+            for (Wq, Ws) in st.W]
+
+    def product(i):
+        rc = gemm(*args[i % st.copies])
+        if rc:
+            raise RuntimeError(q8.q8_last_error())
+
+    def step(i):
+        if w.act != "bf16":
+            rc = st._quant(*st._quant_args)
+            if rc:
+                raise RuntimeError(q8.q8_last_error())
+        product(i)
+
+    for i in range(warmup):
+        step(i)
+    step_ms = time_loop(step, steps)
+    gemm_ms = time_loop(product, steps)
+    flops = 2.0 * m * K * N
+    b = algorithmic_bytes(w)
+    peak = MFMA_PEAK_TFLOPS[w.act]
+    del st
+    torch.cuda.empty_cache()
+    tf = flops / (gemm_ms * 1e-3) / 1e12
+    log(f"[bench] gemm {w.name}: {gemm_ms * 1e3:.2f} us/launch ({tf:.0f} TFLOP/s, "
+        f"{100 * tf / peak:.1f}% of {peak:.0f}), step {step_ms * 1e3:.2f} us")
+    return {"workload": w.name, "m": m, "K": K, "N": N, "act": w.act,
+            "us_per_step": step_ms * 1e3, "kernel_us_mean": gemm_ms * 1e3,
+            "tflops": tf, "peak_tflops": peak, "frac_of_mfma_peak": tf / peak,
+            "gbs_algorithmic": b["total"] / (gemm_ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU oracle (as it stands) on this host, on the same workload."""
     import oracle
@@ -409,6 +457,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the m=16 and m=32 rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-epilogue lines")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the many-row (prefill) lines")
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy (for profiler counter calibration)")
@@ -458,6 +507,13 @@ def main():
                             max(20, args.warmup // 4), rotate=not args.no_rotate)
             fused[f"glu_m{inputs.WORKLOADS[other].m}"] = r
 
+    prefill = {}
+    if not args.no_prefill:
+        for other in ("prefill_m512_k4096_n14336", "prefill_q8act_m512_k4096_n14336"):
+            prefill[inputs.WORKLOADS[other].act] = measure_gemm(
+                inputs.WORKLOADS[other], max(100, args.steps // 10), max(10, args.warmup // 10),
+                rotate=not args.no_rotate)
+
     context = None
     if not args.no_rows:
         context = bandwidth_context(torch, w, args.steps)
@@ -504,6 +560,7 @@ def main():
         "by_rows": by_rows,
         "fused_epilogue": fused,
         "context": context,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 

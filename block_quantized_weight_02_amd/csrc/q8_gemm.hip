@@ -47,9 +47,12 @@ struct GemmShape {
   static constexpr int kRowB = ACT == kActBf16 ? 64 : 32;   // activation bytes, one row x block
   static constexpr int kA = kGemmCB * BM * kRowB;           // activation bytes per stage
   static constexpr int kDx = ACT == kActBf16 ? 0 : kGemmCB * BM * 4;   // int8 row scales
-  static constexpr int kW = WN * kGemmCB * kChunkBytes;     // weight values per stage
+  static constexpr int kW = WN * kGemmCB * kChunkBytes;     // weight values per stage (global)
+  // in LDS the bf16 form holds the values as bf16 (converted once, at staging)
+  static constexpr int kWElt = ACT == kActBf16 ? 2 : 1;
+  static constexpr int kWL = kW * kWElt;                    // weight values per stage (LDS)
   static constexpr int kS = WN * kGemmCB * kTile * 4;       // weight scales per stage
-  static constexpr int kStage = kA + kDx + kW + kS;
+  static constexpr int kStage = kA + kDx + kWL + kS;
   static constexpr int kPieces = (kA + kW + kS) / 16;       // 16-byte staging pieces
   static constexpr int kPer = (kPieces + kGemmThreads - 1) / kGemmThreads;
   static constexpr int kDxPer = (kGemmCB * BM + kGemmThreads - 1) / kGemmThreads;
@@ -57,15 +60,26 @@ struct GemmShape {
                 "each wave's staging pieces fall in one region");
 };
 
-// Byte offset, within one row's staged activation, of 16-byte part q of row
-// r: the parts of a row are permuted by (r / 4) % 4 (bf16) or 8-byte units
-// by 2 * ((r / 8) % 2) (int8), so the 16 rows an MFMA operand read touches
-// land in distinct LDS banks.
+// Byte offset, within one row's staged activation, of 16-byte part `unit`
+// of row r (bf16), or of 8-byte unit `unit` (int8).  The parts of a row are
+// permuted by a function of r % 16 chosen so that an MFMA operand read (16
+// rows, one part each) hits distinct LDS banks whether the LDS serves 16
+// lanes from 64 banks or 8 lanes from 32 banks per cycle: with
+// r % 16 = 8a + 4b + 2c + d, bf16 parts are XORed with 2(a ^ c) + b, which
+// is a bijection over (a, b) for fixed (c, d) and over (b, c) for fixed
+// (a, d).
 template <int ACT>
 __device__ __forceinline__ int a_part(int r, int unit) {
-  if constexpr (ACT == kActBf16) return (unit ^ ((r >> 2) & 3)) * 16;   // unit: 16-byte part
-  else return (unit ^ (((r >> 3) & 1) << 1)) * 8;                      // unit: 8-byte part
+  if constexpr (ACT == kActBf16) {
+    const int f = ((((r >> 3) ^ (r >> 1)) & 1) << 1) | ((r >> 2) & 1);
+    return (unit ^ f) * 16;
+  } else {
+    return (unit ^ (((r >> 3) & 1) << 1)) * 8;
+  }
 }
+
+// The bf16 weight's 16-byte part swizzle for column c (see gemm_store).
+__device__ __forceinline__ int w_part_swizzle(int c) { return ((c >> 2) ^ (c >> 3)) & 1; }
 
 // One thread's share of a stage: which 16-byte pieces it copies, from where
 // (an offset from the stage's wave-uniform region base) and to where in LDS.
@@ -99,10 +113,12 @@ __device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, i
   constexpr int kPPB = S::kRowB / 16;
   constexpr int kElt = ACT == kActBf16 ? 2 : 1;
   const int tid = (int)threadIdx.x;
+  // activation pieces: consecutive threads take the parts of consecutive
+  // rows of one block (so a store's 16 lanes write 4 rows: distinct banks)
 #pragma unroll
   for (int k = 0; k < P::kNA; ++k) {
     const int p = k * kGemmThreads + tid;
-    const int q = p % kPPB, cb = (p / kPPB) % kGemmCB, r = p / (kPPB * kGemmCB);
+    const int q = p % kPPB, r = (p / kPPB) % BM, cb = p / (kPPB * BM);
     const int rc = min(row0 + r, m - 1) - row0;
     pl.asrc[k] = (unsigned)rc * (unsigned)K * kElt + cb * kBlock * kElt + q * 16;
     pl.acb[k] = cb;
@@ -121,7 +137,9 @@ __device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, i
     const int tc = min(t0 + wn, T - 1) - t0;
     pl.wsrc[k] = ((unsigned)tc * NB + cb) * kChunkBytes + q * 16;
     pl.wcb[k] = cb;
-    pl.wdst[k] = S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes + q * 16;
+    // int8 form: the chunk as it is.  bf16 form: column c's 16 values of half h
+    // at h * 2048 + c * 32, in two 16-byte parts (swizzled at the store)
+    pl.wdst[k] = S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes * S::kWElt + q * 16 * S::kWElt;
   }
   {
     const int p = min(tid, P::kNS - 1);
@@ -129,7 +147,7 @@ __device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, i
     const int tc = min(t0 + wn, T - 1) - t0;
     pl.ssrc = ((unsigned)tc * NB + cb) * (kTile * 4) + q * 16;
     pl.scb = cb;
-    pl.sdst = S::kA + S::kDx + S::kW + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
+    pl.sdst = S::kA + S::kDx + S::kWL + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
   }
   if constexpr (ACT == kActQ8) {
 #pragma unroll
@@ -213,7 +231,22 @@ __device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st,
     }
   }
 #pragma unroll
-  for (int k = 0; k < P::kNW; ++k) *reinterpret_cast<u32x4_t *>(buf + pl.wdst[k]) = st.vw[k];
+  for (int k = 0; k < P::kNW; ++k) {
+    if constexpr (ACT == kActBf16) {
+      // 16 int8 values of column c (piece q = h * 64 + c) -> two 8-value bf16
+      // parts; part p sits at (p ^ w_part_swizzle(c)) * 16 so that the
+      // operand reads of adjacent columns hit distinct banks (both LDS bank
+      // models, as for the activation)
+      const int c = (k * kGemmThreads + (int)threadIdx.x) & 63;
+      const int sw = w_part_swizzle(c);
+      const bf16x8_t lo = i8x8_to_bf16(make_uint2(st.vw[k].x, st.vw[k].y));
+      const bf16x8_t hi = i8x8_to_bf16(make_uint2(st.vw[k].z, st.vw[k].w));
+      *reinterpret_cast<bf16x8_t *>(buf + pl.wdst[k] + sw * 16) = lo;
+      *reinterpret_cast<bf16x8_t *>(buf + pl.wdst[k] + (sw ^ 1) * 16) = hi;
+    } else {
+      *reinterpret_cast<u32x4_t *>(buf + pl.wdst[k]) = st.vw[k];
+    }
+  }
   if (!DOTS && (int)threadIdx.x < P::kNS) *reinterpret_cast<u32x4_t *>(buf + pl.sdst) = st.vs;
   if constexpr (ACT == kActQ8 && !DOTS) {
     float *dxs = reinterpret_cast<float *>(buf + S::kA);
@@ -265,41 +298,31 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const char *sbase = reinterpret_cast<const char *>(wsc) + (size_t)t0 * NB * kTile * 4;
   const float *dxbase = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
                                                         act_scale_off) + (size_t)row0 * NB;
-  GemmStaging<ACT, BM> st;
-  gemm_load<ACT, BM, DOTS>(st, pl, abase, wbase, sbase, dxbase, min(NB, kGemmCB));
-  gemm_store<ACT, BM, DOTS>(st, pl, lds);
-  __syncthreads();
-
   // lane's bytes of a chunk: half j/2, column 16g + i, k offset 8 * (j % 2)
   const int w_lane = (lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
+  // bf16 form: half j/2 at 2048 * (j/2), column 16g + i at 32 * (16g + i), the
+  // lane's 8 values (part j % 2) at the swizzled 16-byte offset
+  const int wb_lane = (lj >> 1) * 2 * kHalfBytes + li * 32 + (((lj & 1) ^ w_part_swizzle(li)) * 16);
   // lane's activation bytes within a row (rows 16rt + i: the swizzle depends on i)
-  const int a_lane = ACT == kActBf16 ? a_part<ACT>(li, lj) : a_part<ACT>(li, lj);
-  for (int c = 0; c < NC; ++c) {
-    const int b0 = c * kGemmCB;
-    if (c + 1 < NC)
-      gemm_load<ACT, BM, DOTS>(st, pl, abase + (size_t)(b0 + kGemmCB) * kBlock * kElt,
-                               wbase + (size_t)(b0 + kGemmCB) * kChunkBytes,
-                               sbase + (size_t)(b0 + kGemmCB) * kTile * 4,
-                               dxbase + b0 + kGemmCB, min(NB - b0 - kGemmCB, kGemmCB));
-    const char *buf = lds + (c & 1) * S::kStage;
+  const int a_lane = a_part<ACT>(li, lj);
+
+  // One stage (blocks b0 .. b0 + kGemmCB - 1) from LDS buffer `buf`.
+  auto compute = [&](const char *buf, int b0) {
 #pragma unroll
     for (int cb = 0; cb < kGemmCB; ++cb) {
       const int b = b0 + cb;
       if (b >= NB) break;
       const char *As = buf + cb * BM * S::kRowB;
-      const char *Ws = buf + S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes;
-      uint2 bw[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) bw[g] = *reinterpret_cast<const uint2 *>(Ws + w_lane + g * 256);
+      const char *Ws = buf + S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes * S::kWElt;
       float4 sc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if constexpr (!DOTS)
-        sc = *reinterpret_cast<const float4 *>(buf + S::kA + S::kDx + S::kW +
+        sc = *reinterpret_cast<const float4 *>(buf + S::kA + S::kDx + S::kWL +
                                                ((wn * kGemmCB + cb) * kTile + 4 * li) * 4);
       const float scs[4] = {sc.x, sc.y, sc.z, sc.w};
       if constexpr (ACT == kActBf16) {
         bf16x8_t bb[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) bb[g] = i8x8_to_bf16(bw[g]);
+        for (int g = 0; g < 4; ++g) bb[g] = *reinterpret_cast<const bf16x8_t *>(Ws + wb_lane + g * 512);
         // Per row group: the four MFMAs first (independent, so the matrix
         // core pipelines them), then their sixteen scale FMAs.
 #pragma unroll
@@ -317,6 +340,9 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
             for (int e = 0; e < 4; ++e) acc[rt][g][e] = fmaf(scs[g], d[g][e], acc[rt][g][e]);
         }
       } else {
+        uint2 bw[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bw[g] = *reinterpret_cast<const uint2 *>(Ws + w_lane + g * 256);
         const float *dxs = reinterpret_cast<const float *>(buf + S::kA) + cb * BM;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -347,9 +373,38 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         }
       }
     }
-    if (c + 1 < NC)
-      gemm_store<ACT, BM, DOTS>(st, pl, lds + ((c + 1) & 1) * S::kStage);
+  };
+  // The global loads of stage c (its region bases moved by c stages).
+  auto load = [&](GemmStaging<ACT, BM> &st, int c) {
+    const int b0 = c * kGemmCB;
+    gemm_load<ACT, BM, DOTS>(st, pl, abase + (size_t)b0 * kBlock * kElt,
+                             wbase + (size_t)b0 * kChunkBytes,
+                             sbase + (size_t)b0 * kTile * 4, dxbase + b0,
+                             min(NB - b0, kGemmCB));
+  };
+
+  // Pipeline: LDS double-buffered, and the global loads of each stage issued
+  // two stages ahead of its compute (into the register set freed when the
+  // stage before it went to LDS), so a load has two stages' compute to land.
+  GemmStaging<ACT, BM> r0, r1;
+  char *buf0 = lds, *buf1 = lds + S::kStage;
+  load(r0, 0);
+  gemm_store<ACT, BM, DOTS>(r0, pl, buf0);
+  if (NC > 1) load(r1, 1);
+  __syncthreads();
+  for (int c = 0;;) {
+    // buf0 holds stage c, r1 stage c + 1 (in flight)
+    if (c + 2 < NC) load(r0, c + 2);
+    compute(buf0, c * kGemmCB);
+    if (c + 1 < NC) gemm_store<ACT, BM, DOTS>(r1, pl, buf1);
     __syncthreads();
+    if (++c >= NC) break;
+    // buf1 holds stage c, r0 stage c + 1
+    if (c + 2 < NC) load(r1, c + 2);
+    compute(buf1, c * kGemmCB);
+    if (c + 1 < NC) gemm_store<ACT, BM, DOTS>(r0, pl, buf0);
+    __syncthreads();
+    if (++c >= NC) break;
   }
   if constexpr (DOTS) return;
 

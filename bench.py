@@ -355,8 +355,8 @@ def measure_gemm(w, steps, warmup, rotate=True):
 
     for i in range(warmup):
         step(i)
-    step_ms = time_loop(step, steps)
     gemm_ms = time_loop(product, steps)
+    step_ms = time_loop(step, steps) if w.act != "bf16" else gemm_ms
     flops = 2.0 * m * K * N
     b = algorithmic_bytes(w)
     peak = MFMA_PEAK_TFLOPS[w.act]
@@ -516,7 +516,7 @@ def main():
 
     context = None
     if not args.no_rows:
-        context = bandwidth_context(torch, w, args.steps)
+        context = bandwidth_context(torch, w, 200)
         log(f"[bench] context: one weight copy {context['mall_hot_us']:.2f} us; 1 GiB copy "
             f"{context['copy_1gib_gbs_read_plus_write']:.0f} GB/s read+write")
 

@@ -23,7 +23,9 @@ the timed steps; `roofline` prices the product kernel's own average duration
 `by_rows` gives the same measurement at m = 16 and m = 32; `fused_epilogue`
 times the product with bias, residual and quantized output beside the plain
 product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
-one launch) beside two plain products, at m = 1 and m = 16; `context` gives
+one launch) beside two plain products, at m = 1 and m = 16, and the product
+in parts (query, key and value projections of one activation in one launch)
+beside the same products one by one, at m = 1 and m = 16; `context` gives
 the headline with one weight copy reused and a 1 GiB device copy's rate;
 `prefill` times the many-row product (m = 512) against the MFMA peak.
 """
@@ -71,9 +73,9 @@ def kernel_name(plan: dict, w) -> str:
     act = 0 if w.act == "bf16" else 1
     r, wv, ks = plan["rows"], plan["waves"], plan.get("kslices", 1)
     if plan["kernel"] == 0:
-        return f"gemv_valu_kernel<{r}, {act}, false, {wv}, false>"
+        return f"gemv_valu_kernel<{r}, {act}, false, {wv}, false, false>"
     if plan["kernel"] == 1:
-        return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false>"
+        return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false, false>"
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
 
 
@@ -324,6 +326,75 @@ def measure_glu(w, steps, warmup, rotate=True):
                      "waves": plan.waves, "kslices": plan.kslices}}
 
 
+def measure_parts(pw, steps, warmup, rotate=True):
+    """The product in parts (several projections of one activation, one
+    launch) against the same products launched one by one."""
+    import torch
+    import block_quantized_weight_02_amd as q8
+    from block_quantized_weight_02_amd import inputs
+    dev = "cuda:0"
+    m, K, Ns = pw.m, pw.K, pw.Ns
+    act = q8.Q8_ACT_BF16 if pw.act == "bf16" else q8.Q8_ACT_Q8_0
+    x, ws = inputs.generate_parts(pw)
+    per_copy = sum(q8.q8_packed_values_bytes(K, N) + q8.q8_packed_scales_bytes(K, N) for N in Ns)
+    copies = max(2, math.ceil(ROTATE_BYTES / per_copy)) if rotate else 1
+    Wd = []
+    for (q, s), N in zip(ws, Ns):
+        qd, sd = torch.from_numpy(q).to(dev), torch.from_numpy(s).to(dev)
+        one = []
+        for _ in range(copies):
+            Wq = torch.empty(q8.q8_packed_values_bytes(K, N), dtype=torch.uint8, device=dev)
+            Ws = torch.empty(q8.q8_packed_scales_bytes(K, N) // 4, dtype=torch.float32, device=dev)
+            q8.q8_repack(qd, sd, K, N, Wq, Ws)
+            one.append((Wq, Ws))
+        Wd.append(one)
+        del qd, sd
+    xb = torch.from_numpy(x.view(np.int16)).to(dev)
+    xq = torch.empty(max(16, q8.q8_act_bytes(m, K)), dtype=torch.uint8, device=dev)
+    if act == q8.Q8_ACT_Q8_0:
+        q8.q8_quantize_act(xb, xq, m, K)
+    xin = xb.data_ptr() if act == q8.Q8_ACT_BF16 else xq.data_ptr()
+    ys = [torch.empty((m, q8.q8_padded_cols(N)), dtype=torch.float32, device=dev) for N in Ns]
+    sp = torch.cuda.current_stream().cuda_stream
+    lib = q8.lib()
+    arrs = []
+    for c in range(copies):
+        parts = [q8.make_part(Wd[i][c][0], Wd[i][c][1], ys[i], N) for i, N in enumerate(Ns)]
+        arrs.append((q8.q8_part * len(parts))(*parts))
+    singles = [[(xin, Wd[i][c][0].data_ptr(), Wd[i][c][1].data_ptr(), ys[i].data_ptr(), m, K, N,
+                 act, sp) for i, N in enumerate(Ns)] for c in range(copies)]
+    plan = q8.q8_gemv_parts_default_plan(list(arrs[0]), m, K, act)
+    torch.cuda.synchronize()
+
+    def call(i):
+        rc = lib.q8_gemv_parts(xin, arrs[i % copies], len(Ns), m, K, act, sp)
+        if rc:
+            raise RuntimeError(q8.q8_last_error())
+
+    def one_by_one(i):
+        for a in singles[i % copies]:
+            rc = lib.q8_gemv(*a)
+            if rc:
+                raise RuntimeError(q8.q8_last_error())
+
+    for i in range(warmup):
+        call(i)
+        one_by_one(i)
+    sep_ms = time_loop(one_by_one, steps)
+    parts_ms = time_loop(call, steps)
+    xbytes = 2 * m * K if act == q8.Q8_ACT_BF16 else m * K + 4 * m * (K // 32)
+    nbytes = per_copy + xbytes + sum(4 * m * q8.q8_padded_cols(N) for N in Ns)
+    del Wd, arrs, singles
+    torch.cuda.empty_cache()
+    log(f"[bench] parts {pw.name}: {parts_ms * 1e3:.2f} us vs one by one {sep_ms * 1e3:.2f} us, "
+        f"plan={plan}")
+    return {"workload": pw.name, "Ns": list(Ns), "parts_us": parts_ms * 1e3,
+            "one_by_one_us": sep_ms * 1e3, "bytes": nbytes,
+            "parts_gbs": nbytes / (parts_ms * 1e-3) / 1e9,
+            "plan": {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
+                     "waves": plan.waves, "kslices": plan.kslices}}
+
+
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "q8_0": 5000.0}   # MI355X dense, published
 
 
@@ -506,6 +577,10 @@ def main():
             r = measure_glu(inputs.WORKLOADS[other], max(200, args.steps // 4),
                             max(20, args.warmup // 4), rotate=not args.no_rotate)
             fused[f"glu_m{inputs.WORKLOADS[other].m}"] = r
+        for other in ("qkv_decode_k4096", "qkv_batch16_k4096"):
+            r = measure_parts(inputs.PARTS_WORKLOADS[other], max(200, args.steps // 4),
+                              max(20, args.warmup // 4), rotate=not args.no_rotate)
+            fused[f"parts_m{inputs.PARTS_WORKLOADS[other].m}"] = r
 
     prefill = {}
     if not args.no_prefill:

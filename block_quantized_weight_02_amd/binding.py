@@ -24,6 +24,7 @@ Q8_KERNEL_MFMA = 1
 Q8_KERNEL_MFMA_COLS = 2
 Q8_MAX_ROWS = 32
 Q8_MAX_GEMM_ROWS = 8192
+Q8_MAX_PARTS = 4
 
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_SHAPE", 2: "Q8_ERR_ACT_FMT", 3: "Q8_ERR_NULL",
           4: "Q8_ERR_ALIGN", 5: "Q8_ERR_WORKSPACE", 6: "Q8_ERR_HIP", 7: "Q8_ERR_PLAN"}
@@ -54,6 +55,11 @@ class q8_epilogue(ctypes.Structure):
 class q8_glu_epilogue(ctypes.Structure):
     _fields_ = [("bias_g", ctypes.c_void_p), ("bias_u", ctypes.c_void_p),
                 ("y_q8", ctypes.c_void_p), ("write_y", ctypes.c_int32)]
+
+
+class q8_part(ctypes.Structure):
+    _fields_ = [("W_q8", ctypes.c_void_p), ("W_q8_scale", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("y", ctypes.c_void_p), ("N", ctypes.c_int64)]
 
 
 _i64 = ctypes.c_int64
@@ -95,6 +101,13 @@ _SIGS = {
                                    _p, _p, _sz]),
     "q8_gemv_glu_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_plan)]),
     "q8_glu_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), _i64, _i64, _i64]),
+    "q8_gemv_parts": (_int, [_p, ctypes.POINTER(q8_part), _int, _i64, _i64, _int, _p]),
+    "q8_gemv_parts_planned": (_int, [_p, ctypes.POINTER(q8_part), _int, _i64, _i64, _int,
+                                     ctypes.POINTER(q8_plan), _p, _p, _sz]),
+    "q8_gemv_parts_default_plan": (_int, [ctypes.POINTER(q8_part), _int, _i64, _i64, _int,
+                                          ctypes.POINTER(q8_plan)]),
+    "q8_parts_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), ctypes.POINTER(q8_part), _int,
+                                       _i64, _i64]),
     "q8_gemm": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
     "q8_gemm_block_dots": (_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
     "q8_status_string": (ctypes.c_char_p, [_int]),
@@ -295,6 +308,43 @@ def q8_gemv_glu_default_plan(m, K, N, act_fmt) -> q8_plan:
 
 def q8_glu_workspace_bytes(plan: q8_plan, m, K, N) -> int:
     return int(lib().q8_glu_workspace_bytes(ctypes.byref(plan), m, K, N))
+
+
+def make_part(W_q8, W_q8_scale, y, N, bias=None) -> q8_part:
+    """A ``q8_part`` over device tensors (or raw addresses, or None)."""
+    return q8_part(_addr(W_q8), _addr(W_q8_scale), _addr(bias), _addr(y), N)
+
+
+def _parts_ref(parts):
+    """(host array, count) of a sequence of ``q8_part``; None passes NULL."""
+    if parts is None:
+        return None, 0
+    parts = list(parts)
+    return (q8_part * max(1, len(parts)))(*parts), len(parts)
+
+
+def q8_gemv_parts(x, parts, m, K, act_fmt, stream=None) -> None:
+    arr, n = _parts_ref(parts)
+    _check(lib().q8_gemv_parts(_addr(x), arr, n, m, K, act_fmt, _stream(stream)))
+
+
+def q8_gemv_parts_planned(x, parts, m, K, act_fmt, plan: q8_plan, stream=None,
+                          workspace=None, ws_bytes=0) -> None:
+    arr, n = _parts_ref(parts)
+    _check(lib().q8_gemv_parts_planned(_addr(x), arr, n, m, K, act_fmt, ctypes.byref(plan),
+                                       _stream(stream), _addr(workspace), ws_bytes))
+
+
+def q8_gemv_parts_default_plan(parts, m, K, act_fmt) -> q8_plan:
+    arr, n = _parts_ref(parts)
+    p = q8_plan()
+    _check(lib().q8_gemv_parts_default_plan(arr, n, m, K, act_fmt, ctypes.byref(p)))
+    return p
+
+
+def q8_parts_workspace_bytes(plan: q8_plan, parts, m, K) -> int:
+    arr, n = _parts_ref(parts)
+    return int(lib().q8_parts_workspace_bytes(ctypes.byref(plan), arr, n, m, K))
 
 
 def q8_gemm(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream=None) -> None:

@@ -428,6 +428,128 @@ int check_glu_args(const void *x, const int8_t *Wg, const float *Wg_s, const int
   return check_glu_epilogue(ep, y);
 }
 
+// ---- projections in parts -------------------------------------------------------
+
+static_assert(Q8_MAX_PARTS == q8::kMaxParts, "parts limit of the ABI and the kernels");
+
+// Checks the parts and returns their padded widths summed: the launch's
+// output columns side by side.
+int check_parts(const q8_part *parts, int n_parts, int64_t *cols_out) {
+  if (!parts) return fail(Q8_ERR_NULL, "parts is NULL");
+  if (n_parts < 1 || n_parts > Q8_MAX_PARTS)
+    return fail(Q8_ERR_SHAPE, "n_parts = %d out of range: need 1 <= n_parts <= %d", n_parts,
+                Q8_MAX_PARTS);
+  int64_t cols = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    const int64_t N = parts[i].N;
+    if (N < 1 || N > kMaxN)
+      return fail(Q8_ERR_SHAPE, "part %d: N = %lld out of range: need 1 <= N <= %lld", i,
+                  (long long)N, (long long)kMaxN);
+    cols += round_up(N, Q8_TILE_COLS);
+  }
+  if (cols > kMaxN)
+    return fail(Q8_ERR_SHAPE, "the parts' padded widths sum to %lld, more than %lld",
+                (long long)cols, (long long)kMaxN);
+  *cols_out = cols;
+  return Q8_OK;
+}
+
+int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
+                     int act_fmt, int64_t *cols) {
+  int st;
+  if ((st = check_parts(parts, n_parts, cols))) return st;
+  if ((st = check_m(m)) || (st = check_kn(K, *cols)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_ptr(x, "x"))) return st;
+  for (int i = 0; i < n_parts; ++i) {
+    const q8_part &pt = parts[i];
+    if ((st = check_ptr(pt.W_q8, "W_q8")) || (st = check_ptr(pt.W_q8_scale, "W_q8_scale")) ||
+        (st = check_ptr(pt.y, "y")) || (pt.bias && (st = check_ptr(pt.bias, "bias")))) {
+      const std::string what = g_last_error;
+      return fail(st, "part %d: %s", i, what.c_str());
+    }
+  }
+  return Q8_OK;
+}
+
+// The product's plan over the parts' columns side by side, on a kernel that
+// walks units of any part (VALU or block-interleaved MFMA); the VALU kernel
+// takes 4 waves a workgroup once the workgroups outnumber the CUs, as the
+// gated pair does.
+q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
+  q8_plan p = default_plan(m, K, cols, act_fmt);
+  const int64_t NB = K / Q8_BLOCK;
+  if (p.kernel == Q8_KERNEL_MFMA_COLS) {
+    p.kernel = Q8_KERNEL_MFMA;
+    p.waves = 16;
+    p.kslices = 1;
+    const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
+    int64_t S = 1;
+    while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
+                                        (int)S) > budget)
+      ++S;
+    p.split_k = (int32_t)S;
+  }
+  if (p.kernel == Q8_KERNEL_VALU && cols / Q8_TILE_COLS * p.split_k > device_facts().cus)
+    p.waves = 4;
+  return p;
+}
+
+int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
+              int64_t cols, int act_fmt, const q8_plan &plan, hipStream_t stream,
+              void *workspace, size_t ws_bytes) {
+  if (plan.kernel == Q8_KERNEL_MFMA_COLS)
+    return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel does not run parts: "
+                "use the VALU or MFMA kernel");
+  int st = check_plan(&plan, m, K, act_fmt, false);
+  if (st) return st;
+  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "activation too large");
+  q8::GemvArgs a{};
+  a.x = x;
+  a.wq = parts[0].W_q8;
+  a.wsc = parts[0].W_q8_scale;
+  a.y = parts[0].y;
+  a.m = (int)m;
+  a.K = (int)K;
+  a.NB = (int)(K / Q8_BLOCK);
+  a.Npad = (int)cols;
+  a.T = (int)(cols / Q8_TILE_COLS);
+  a.split_k = plan.split_k;
+  a.act_scale_off = (unsigned)act_scales_offset(m, K);
+  a.ep.N = (int)parts[0].N;
+  a.ep.write_y = 1;
+  a.ep.nw = 1;
+  q8::Parts &pp = a.ep.parts;
+  pp.n = n_parts;
+  pp.cum[0] = 0;
+  for (int i = 0; i < q8::kMaxParts; ++i) {
+    const bool on = i < n_parts;
+    pp.wq[i] = on ? parts[i].W_q8 : nullptr;
+    pp.wsc[i] = on ? parts[i].W_q8_scale : nullptr;
+    pp.y[i] = on ? parts[i].y : nullptr;
+    pp.bias[i] = on ? parts[i].bias : nullptr;
+    pp.N[i] = on ? (int)parts[i].N : 0;
+    pp.cum[i + 1] =
+        pp.cum[i] + (on ? (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS) : 0);
+  }
+  if (plan.split_k > 1) {
+    const size_t need = plan_ws_bytes(plan, m, cols);
+    if (!workspace || ws_bytes < need)
+      return fail(Q8_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? ws_bytes : (size_t)0, need);
+    a.counters = static_cast<unsigned *>(workspace);
+    a.partial = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+  }
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_gemv(plan.kernel, plan.rows, act_fmt, false, plan.waves,
+                                 plan.kslices, a, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_fail(e, "gemv parts launch");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -736,5 +858,47 @@ int q8_release_workspaces(void) {
 }
 
 int q8_layout_version(void) { return q8::kLayoutVersion; }
+
+
+int q8_gemv_parts_default_plan(const q8_part *parts, int n_parts, int64_t m, int64_t K,
+                               int act_fmt, q8_plan *plan) {
+  int st;
+  int64_t cols = 0;
+  if ((st = check_parts(parts, n_parts, &cols))) return st;
+  if ((st = check_m(m)) || (st = check_kn(K, cols)) || (st = check_act(act_fmt))) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  *plan = parts_default_plan(m, K, cols, act_fmt);
+  return ok();
+}
+
+size_t q8_parts_workspace_bytes(const q8_plan *plan, const q8_part *parts, int n_parts,
+                                int64_t m, int64_t K) {
+  int64_t cols = 0;
+  if (!plan || check_parts(parts, n_parts, &cols) || check_m(m) || check_kn(K, cols)) return 0;
+  return plan_ws_bytes(*plan, m, cols);
+}
+
+int q8_gemv_parts_planned(const void *x, const q8_part *parts, int n_parts, int64_t m,
+                          int64_t K, int act_fmt, const q8_plan *plan, hipStream_t stream,
+                          void *workspace, size_t ws_bytes) {
+  int64_t cols = 0;
+  int st = check_parts_args(x, parts, n_parts, m, K, act_fmt, &cols);
+  if (st) return st;
+  if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
+  if (workspace && (st = check_ptr(workspace, "workspace"))) return st;
+  return run_parts(x, parts, n_parts, m, K, cols, act_fmt, *plan, stream, workspace, ws_bytes);
+}
+
+int q8_gemv_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
+                  int act_fmt, hipStream_t stream) {
+  int64_t cols = 0;
+  int st = check_parts_args(x, parts, n_parts, m, K, act_fmt, &cols);
+  if (st) return st;
+  const q8_plan plan = parts_default_plan(m, K, cols, act_fmt);
+  const size_t need = plan_ws_bytes(plan, m, cols);
+  void *ws = nullptr;
+  if ((st = library_workspace(stream, need, &ws))) return st;
+  return run_parts(x, parts, n_parts, m, K, cols, act_fmt, plan, stream, ws, need);
+}
 
 }  // extern "C"

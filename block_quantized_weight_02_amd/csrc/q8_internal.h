@@ -30,6 +30,21 @@ constexpr int kLayoutVersion = 2;
 
 enum Act { kActBf16 = 0, kActQ8 = 1 };
 
+// Several products of one activation in one launch (the GEMV in parts): part
+// p multiplies by its own packed weight (wq[p], wsc[p], N[p] columns) into
+// its own output y[p] (m x N_pad(p)), plus its optional bias.  Units (the
+// launch's 64-column tiles) cum[p] .. cum[p+1]-1 are part p's tiles.
+constexpr int kMaxParts = 4;
+struct Parts {
+  int n;                          // parts; 0: not a parts launch
+  int cum[kMaxParts + 1];
+  const int8_t *wq[kMaxParts];
+  const float *wsc[kMaxParts];
+  float *y[kMaxParts];
+  const float *bias[kMaxParts];
+  int N[kMaxParts];
+};
+
 // Fused epilogue of a product (all pointers optional, device memory).
 // nw == 1: z = x.W + bias + residual.
 // nw == 2 (gated pair): z = silu(x.W + bias) * (x.W_u + bias_u), W_u the
@@ -47,6 +62,7 @@ struct Epi {
   const int8_t *wq_u;    // the pair's second weight
   const float *wsc_u;
   const float *bias_u;
+  Parts parts;           // the GEMV in parts (parts.n > 0): units are its parts' tiles
 };
 
 // Everything a product launch needs; pointers are device pointers.

@@ -168,6 +168,52 @@ __device__ __forceinline__ float sum_partials(const float *__restrict__ partial,
   return v;
 }
 
+// Where a unit's finished tile goes: its product's output y (row stride
+// Npad) at columns col0 .., its partial carries' columns pcol0 .. in rows of
+// pstride, and its arrival counter.
+struct TileOut {
+  float *y;
+  int Npad;
+  size_t col0;
+  size_t pcol0;
+  int pstride;
+  unsigned cidx;
+};
+
+// The part that unit tv of a parts launch belongs to.
+__device__ __forceinline__ int part_of(const Parts &pt, int tv) {
+  int p = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxParts; ++i)
+    if (i < pt.n && tv >= pt.cum[i]) p = i;
+  return p;
+}
+
+// Unit tv of a parts launch (units in all): its weight, where its tile goes,
+// its epilogue (the part's bias and width), and its tile within the part.
+struct PartUnit {
+  const int8_t *wq;
+  const float *wsc;
+  TileOut out;
+  Epi ep;
+  int t;
+};
+__device__ __forceinline__ PartUnit part_unit(const Epi &ep, int tv, int units) {
+  const Parts &pt = ep.parts;
+  const int p = part_of(pt, tv);
+  PartUnit u;
+  u.t = tv - pt.cum[p];
+  u.wq = pt.wq[p];
+  u.wsc = pt.wsc[p];
+  const int np = (pt.N[p] + kTile - 1) / kTile * kTile;
+  u.out = TileOut{pt.y[p], np, (size_t)u.t * kTile, (size_t)tv * kTile, units * kTile,
+                  (unsigned)tv};
+  u.ep = ep;
+  u.ep.bias = pt.bias[p];
+  u.ep.N = pt.N[p];
+  return u;
+}
+
 // Epilogue of both kernels.  red[w][r][c] holds wave w's fp32 carry of row r,
 // tile column c of weight `wsel` (already written, __syncthreads() done by the
 // caller).  Sums the waves in order; when the tile's value is complete here
@@ -181,11 +227,10 @@ __device__ __forceinline__ float sum_partials(const float *__restrict__ partial,
 // bumped.  So no workgroup needs a device-scope fence, whose L2 write-back and
 // invalidate would cost each workgroup microseconds.
 template <int MR, int W, bool PAIR>
-__device__ __forceinline__ void finish_tile(const float *red, float *__restrict__ y,
+__device__ __forceinline__ void finish_tile(const float *red, const TileOut &o,
                                             float *__restrict__ partial,
-                                            unsigned *__restrict__ counters, int m, int Npad,
-                                            int t, int s, int S, int wsel, const Epi &ep) {
-  const size_t col0 = (size_t)t * kTile;
+                                            unsigned *__restrict__ counters, int m, int s, int S,
+                                            int wsel, const Epi &ep) {
   const int arrivals = S * (PAIR ? 2 : 1);
   for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
     const int r = idx >> 6, c = idx & 63;
@@ -194,10 +239,11 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
 #pragma unroll
       for (int w = 1; w < W; ++w) v += red[w * MR * 64 + idx];
       if (arrivals == 1)
-        store_final(ep, y, Npad, r, col0 + c, final_value<PAIR>(ep, Npad, r, col0 + c, v, 0.0f));
+        store_final(ep, o.y, o.Npad, r, o.col0 + c,
+                    final_value<PAIR>(ep, o.Npad, r, o.col0 + c, v, 0.0f));
       else
-        __hip_atomic_store(&partial[(((size_t)wsel * S + s) * m + r) * Npad + col0 + c], v,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&partial[(((size_t)wsel * S + s) * m + r) * o.pstride + o.pcol0 + c],
+                           v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
   if (arrivals == 1) return;
@@ -207,7 +253,7 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0)
-    is_last = (__hip_atomic_fetch_add(&counters[t], 1u, __ATOMIC_RELAXED,
+    is_last = (__hip_atomic_fetch_add(&counters[o.cidx], 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(arrivals - 1))
                   ? 1 : 0;
   __syncthreads();
@@ -215,13 +261,14 @@ __device__ __forceinline__ void finish_tile(const float *red, float *__restrict_
   for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
     const int r = idx >> 6, c = idx & 63;
     if (r < m) {
-      const float vg = sum_partials(partial, m, Npad, S, 0, r, col0 + c);
-      const float vu = PAIR ? sum_partials(partial, m, Npad, S, 1, r, col0 + c) : 0.0f;
-      store_final(ep, y, Npad, r, col0 + c, final_value<PAIR>(ep, Npad, r, col0 + c, vg, vu));
+      const float vg = sum_partials(partial, m, o.pstride, S, 0, r, o.pcol0 + c);
+      const float vu = PAIR ? sum_partials(partial, m, o.pstride, S, 1, r, o.pcol0 + c) : 0.0f;
+      store_final(ep, o.y, o.Npad, r, o.col0 + c,
+                  final_value<PAIR>(ep, o.Npad, r, o.col0 + c, vg, vu));
     }
   }
   if (threadIdx.x == 0)
-    __hip_atomic_store(&counters[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&counters[o.cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,7 +423,7 @@ __device__ __forceinline__ void valu_compute(const ValuStage<MR, ACT, DOTS> &st,
   }
 }
 
-template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR, bool PARTS>
 __global__ void __launch_bounds__(64 * W)
 gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
@@ -385,18 +432,31 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  int S, unsigned act_scale_off, Epi ep) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // unit tv = (tile, weight): a gated pair's two weights are adjacent units
+  // unit tv: a tile of the product, of a gated pair's weight (the pair's two
+  // weights are adjacent units), or of one part of a parts launch
   const int tv = blockIdx.x / S;
   const int s = blockIdx.x - tv * S;
   const int wsel = PAIR ? (tv & 1) : 0;
-  const int t = PAIR ? (tv >> 1) : tv;
+  int t = PAIR ? (tv >> 1) : tv;
+  const int8_t *wbase = wsel ? ep.wq_u : wq;
+  const float *sbase = wsel ? ep.wsc_u : wsc;
+  TileOut out{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t};
+  Epi uep = ep;
+  if constexpr (PARTS) {
+    const PartUnit u = part_unit(ep, tv, (int)(gridDim.x / S));
+    t = u.t;
+    wbase = u.wq;
+    sbase = u.wsc;
+    out = u.out;
+    uep = u.ep;
+  }
   int b_lo, b_hi;
   split_range(NB, s, S, b_lo, b_hi);
 
   // the tile's values and scales; each lane adds its own byte offset
   ValuSrc<MR> src;
-  src.wp = (wsel ? ep.wq_u : wq) + (size_t)t * NB * kChunkBytes;
-  src.sp = (wsel ? ep.wsc_u : wsc) + (size_t)t * NB * kTile;
+  src.wp = wbase + (size_t)t * NB * kChunkBytes;
+  src.sp = sbase + (size_t)t * NB * kTile;
   if constexpr (ValuSrc<MR>::kBuf) {
     src.wr = make_buf(src.wp, (unsigned)NB * kChunkBytes);
     src.sr = make_buf(src.sp, (unsigned)NB * kTile * 4);
@@ -444,7 +504,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int r = 0; r < MR; ++r) red[(wave * MR + r) * 64 + lane] = acc[r];
   __syncthreads();
-  finish_tile<MR, W, PAIR>(red, y, partial, counters, m, Npad, t, s, S, wsel, ep);
+  finish_tile<MR, W, PAIR>(red, out, partial, counters, m, s, S, wsel, uep);
 }
 
 // ---------------------------------------------------------------------------
@@ -948,7 +1008,7 @@ __device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
   }
 }
 
-template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR, bool PARTS>
 __global__ void __launch_bounds__(64 * W)
 gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
@@ -976,11 +1036,27 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   constexpr bool pair = PAIR;
   constexpr int step = W * kMfmaUnroll;
   MfmaStage A, B;
+  // unit tv's weight and scales, and its tile within its product
+  auto unit_src = [&](int tv, const int8_t *&wb, const float *&sb, int &tt) {
+    if constexpr (PARTS) {
+      const int p = part_of(ep.parts, tv);
+      tt = tv - ep.parts.cum[p];
+      wb = ep.parts.wq[p];
+      sb = ep.parts.wsc[p];
+    } else {
+      tt = pair ? tv >> 1 : tv;
+      const int w0 = pair ? (tv & 1) : 0;
+      wb = w0 ? ep.wq_u : wq;
+      sb = w0 ? ep.wsc_u : wsc;
+    }
+  };
   if (jwg < T && b_lo + wave < b_hi) {
-    const int t0 = pair ? jwg >> 1 : jwg, w0 = pair ? (jwg & 1) : 0;
-    mfma_load<DOTS, W>(A, (w0 ? ep.wq_u : wq) + (size_t)t0 * NB * kChunkBytes + lane_off,
-                       reinterpret_cast<const float4 *>((w0 ? ep.wsc_u : wsc) +
-                                                        (size_t)t0 * NB * kTile) + li,
+    const int8_t *wb;
+    const float *sb;
+    int t0;
+    unit_src(jwg, wb, sb, t0);
+    mfma_load<DOTS, W>(A, wb + (size_t)t0 * NB * kChunkBytes + lane_off,
+                       reinterpret_cast<const float4 *>(sb + (size_t)t0 * NB * kTile) + li,
                        b_lo + wave, b_hi);
   }
   stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
@@ -992,10 +1068,13 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       lds + (red_on_stage ? (size_t)0 : mfma_stage_bytes(MR, ACT, nblk_max)));
 
   for (int tv = jwg; tv < T; tv += G) {
-    const int t = pair ? tv >> 1 : tv, wsel = pair ? (tv & 1) : 0;
-    const int8_t *wlane = (wsel ? ep.wq_u : wq) + (size_t)t * NB * kChunkBytes + lane_off;
-    const float4 *slane =
-        reinterpret_cast<const float4 *>((wsel ? ep.wsc_u : wsc) + (size_t)t * NB * kTile) + li;
+    const int wsel = pair ? (tv & 1) : 0;
+    const int8_t *wb;
+    const float *sb;
+    int t;
+    unit_src(tv, wb, sb, t);
+    const int8_t *wlane = wb + (size_t)t * NB * kChunkBytes + lane_off;
+    const float4 *slane = reinterpret_cast<const float4 *>(sb + (size_t)t * NB * kTile) + li;
     f32x4_t acc[RG][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -1095,7 +1174,14 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         for (int e = 0; e < 4; ++e)
           red[(wave * MR + rg * 16 + lj * 4 + e) * 64 + g * 16 + li] = acc[rg][g][e];
     __syncthreads();
-    finish_tile<MR, W, PAIR>(red, y, partial, counters, m, Npad, t, s, S, wsel, ep);
+    if constexpr (PARTS) {
+      const PartUnit u = part_unit(ep, tv, T);
+      finish_tile<MR, W, false>(red, u.out, partial, counters, m, s, S, 0, u.ep);
+    } else {
+      finish_tile<MR, W, PAIR>(red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad,
+                                            (unsigned)t},
+                               partial, counters, m, s, S, wsel, ep);
+    }
     __syncthreads();   // red is free again for the next tile
   }
 }
@@ -1121,10 +1207,10 @@ size_t cols_lds_bytes_of(int rows, int act, int kslices, int NB, int S) {
   return mfma_stage_bytes(rows, act, nblk) + red;
 }
 
-template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR, bool PARTS>
 hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.tiles() * a.split_k));
-  gemv_valu_kernel<MR, ACT, DOTS, W, PAIR><<<grid, dim3(64 * W), 0, stream>>>(
+  gemv_valu_kernel<MR, ACT, DOTS, W, PAIR, PARTS><<<grid, dim3(64 * W), 0, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB,
       a.Npad, a.split_k, a.act_scale_off, a.ep);
   return hipGetLastError();
@@ -1135,9 +1221,10 @@ hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
   if constexpr (!DOTS) {
-    if (a.ep.nw == 2) return launch_valu_k<MR, ACT, DOTS, W, true>(a, stream);
+    if (a.ep.nw == 2) return launch_valu_k<MR, ACT, DOTS, W, true, false>(a, stream);
+    if (a.ep.parts.n > 0) return launch_valu_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }
-  return launch_valu_k<MR, ACT, DOTS, W, false>(a, stream);
+  return launch_valu_k<MR, ACT, DOTS, W, false, false>(a, stream);
 }
 
 // Workgroups of a launch that fit on the device at once (per CU, from the
@@ -1177,13 +1264,13 @@ hipError_t grant_lds(Kern kern, size_t lds, size_t &granted) {
   return e;
 }
 
-template <int MR, int ACT, bool DOTS, int W, bool PAIR>
+template <int MR, int ACT, bool DOTS, int W, bool PAIR, bool PARTS>
 hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t st = mfma_stage_of(MR, ACT, a.NB, a.split_k), rd = mfma_red_of(MR, W);
   const size_t lds_alias = st > rd ? st : rd;   // carries on top of the stage
   const size_t lds_sep = st + rd;               // carries after the stage
-  auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W, PAIR>;
+  auto kern = gemv_mfma_kernel<MR, ACT, DOTS, W, PAIR, PARTS>;
   static size_t granted = 64 * 1024;
   int dev = 0, max_lds = 0;
   (void)hipGetDevice(&dev);
@@ -1215,9 +1302,10 @@ hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
   if constexpr (!DOTS) {
-    if (a.ep.nw == 2) return launch_mfma_k<MR, ACT, DOTS, W, true>(a, stream);
+    if (a.ep.nw == 2) return launch_mfma_k<MR, ACT, DOTS, W, true, false>(a, stream);
+    if (a.ep.parts.n > 0) return launch_mfma_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }
-  return launch_mfma_k<MR, ACT, DOTS, W, false>(a, stream);
+  return launch_mfma_k<MR, ACT, DOTS, W, false, false>(a, stream);
 }
 
 template <int MR, int ACT, bool DOTS, int KW, int P, bool QO, bool PAIR>

@@ -66,6 +66,32 @@ WORKLOADS: Dict[str, Workload] = {
 HEADLINE = "decode_k4096_n14336"
 
 
+@dataclass(frozen=True)
+class PartsWorkload:
+    """Several projections of one activation (one launch in parts)."""
+    name: str
+    m: int
+    K: int
+    Ns: tuple
+    act: str
+    seed_x: int
+    seed_w: int
+    note: str = field(default="", compare=False)
+
+
+# The attention's query, key and value projections of the same decoder
+# (hidden 4096, 32 query heads and 8 key/value heads of 128).
+PARTS_WORKLOADS: Dict[str, PartsWorkload] = {
+    "qkv_decode_k4096": PartsWorkload("qkv_decode_k4096", 1, 4096, (4096, 1024, 1024), "bf16",
+                                      1009, 1009, note="m=1 decode q/k/v projections"),
+    "qkv_batch16_k4096": PartsWorkload("qkv_batch16_k4096", 16, 4096, (4096, 1024, 1024), "bf16",
+                                       1010, 1010, note="m=16 batched decode q/k/v projections"),
+    "qkv_q8act_m32_k4096": PartsWorkload("qkv_q8act_m32_k4096", 32, 4096, (4096, 1024, 1024),
+                                         "q8_0", 1011, 1011,
+                                         note="m=32 Q8_0 activations, q/k/v projections"),
+}
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even (inputs are finite)."""
     u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
@@ -179,3 +205,12 @@ def generate_pair(w: Workload, n_cols: Optional[int] = None):
     qu = gen_q(w.K, N, w.seed_w + 500000, w.q_law)
     su = gen_scales(w.K, N, w.seed_w + 500000)
     return x, qg, sg, qu, su
+
+
+def generate_parts(w: PartsWorkload):
+    """``(x, [(q_i, s_i), ...])``: a parts workload's activation and one weight
+    per part, part i's from seed_w + 100000 * i."""
+    x = gen_x(w.m, w.K, w.seed_x, "normal")
+    ws = [(gen_q(w.K, N, w.seed_w + 100000 * i, "uniform"),
+           gen_scales(w.K, N, w.seed_w + 100000 * i)) for i, N in enumerate(w.Ns)]
+    return x, ws

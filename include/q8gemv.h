@@ -292,6 +292,50 @@ int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
 size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K,
                               int64_t N);
 
+/* ---- projections in parts ----------------------------------------------------- */
+
+/* Most parts one launch takes. */
+#define Q8_MAX_PARTS 4
+
+/*
+ * Several products of one activation in one launch: the pages'
+ * codegen_cuda/lane/plan.rs, enum Launch, variant GemmParts, and its part,
+ * struct GemmPart (a matrix, an optional bias, a destination and its output
+ * width), which run as the GEMV in parts at the GEMV's rows.  Part i computes
+ *     y_i[r, n] = (x . W_i)[r, n] + bias_i[n]        n < N_i (pad columns 0)
+ * with q8_gemv's arithmetic and layouts: every W_i is a packed K x N_i weight
+ * (its own q8_repack) over the same K, y_i is m x q8_padded_cols(N_i) fp32.
+ * The parts' column tiles are the launch's units side by side, so the
+ * workgroups stream all the weights at once.
+ */
+typedef struct q8_part {
+  const int8_t *W_q8;        /* q8_packed_values_bytes(K, N) bytes            */
+  const float *W_q8_scale;   /* q8_packed_scales_bytes(K, N) bytes            */
+  const float *bias;         /* N fp32, or NULL                               */
+  float *y;                  /* m x N_pad fp32, written whole                 */
+  int64_t N;                 /* output columns, 1 <= N                        */
+} q8_part;
+
+/* 1 <= n_parts <= Q8_MAX_PARTS parts (a host array of them), the padded
+ * widths summing to at most 2^24; m, K, x, act_fmt as in q8_gemv.  Uses the
+ * library's workspace (as q8_gemv).  Q8_ERR_SHAPE for a bad count or width,
+ * Q8_ERR_NULL / Q8_ERR_ALIGN naming the part whose pointer is wrong. */
+int q8_gemv_parts(const void *x, const q8_part *parts, int n_parts, int64_t m,
+                  int64_t K, int act_fmt, hipStream_t stream);
+
+/* With an explicit plan (the VALU or MFMA kernel; MFMA_COLS is Q8_ERR_PLAN)
+ * and the caller's workspace (zeroed once, as in q8_gemv_ws). */
+int q8_gemv_parts_planned(const void *x, const q8_part *parts, int n_parts,
+                          int64_t m, int64_t K, int act_fmt, const q8_plan *plan,
+                          hipStream_t stream, void *workspace, size_t ws_bytes);
+
+/* The plan q8_gemv_parts launches, and the workspace a plan needs for it
+ * (0 on invalid arguments). */
+int q8_gemv_parts_default_plan(const q8_part *parts, int n_parts, int64_t m,
+                               int64_t K, int act_fmt, q8_plan *plan);
+size_t q8_parts_workspace_bytes(const q8_plan *plan, const q8_part *parts,
+                                int n_parts, int64_t m, int64_t K);
+
 /* ---- many rows: the prefill product ----------------------------------------- */
 
 /* Rows the many-row product accepts. */

@@ -188,3 +188,50 @@ def test_gated_pair_plan_counts_both_weights():
             assert pair.waves in (4, wide.waves)
         else:
             assert pair.waves == wide.waves
+
+
+def _part(N, w=A, s=A, y=A, bias=None):
+    return q8.make_part(w, s, y, N, bias=bias)
+
+
+def test_parts_validation():
+    three = [_part(4096), _part(1024), _part(1024)]
+    expect(3, q8.q8_gemv_parts, A, None, 1, 4096, 0, S0)
+    expect(1, q8.q8_gemv_parts, A, [], 1, 4096, 0, S0)
+    expect(1, q8.q8_gemv_parts, A, [_part(64)] * 5, 1, 4096, 0, S0)
+    expect(1, q8.q8_gemv_parts, A, [_part(64), _part(0)], 1, 4096, 0, S0)
+    expect(1, q8.q8_gemv_parts, A, three, 33, 4096, 0, S0)
+    expect(1, q8.q8_gemv_parts, A, three, 1, 48, 0, S0)
+    expect(2, q8.q8_gemv_parts, A, three, 1, 4096, 2, S0)
+    expect(3, q8.q8_gemv_parts, None, three, 1, 4096, 0, S0)
+    expect(3, q8.q8_gemv_parts, A, [_part(64), _part(64, y=None)], 1, 4096, 0, S0)
+    assert "part 1" in q8.q8_last_error()
+    expect(4, q8.q8_gemv_parts, A, [_part(64), _part(64, s=A + 4)], 1, 4096, 0, S0)
+    expect(4, q8.q8_gemv_parts, A, [_part(64, bias=A + 8)], 1, 4096, 0, S0)
+    # the padded widths together stay within 2^24 columns
+    expect(1, q8.q8_gemv_parts, A, [_part(1 << 24), _part(1)], 1, 64, 0, S0)
+    p = q8.q8_gemv_parts_default_plan(three, 1, 4096, 0)
+    need = q8.q8_parts_workspace_bytes(p, three, 1, 4096)
+    assert need == (4 * 2 ** 20 + p.split_k * 6144 * 4 if p.split_k > 1 else 0)
+    if need:
+        expect(5, q8.q8_gemv_parts_planned, A, three, 1, 4096, 0, p, S0, None, 0)
+        expect(5, q8.q8_gemv_parts_planned, A, three, 1, 4096, 0, p, S0, A, need - 16)
+    cols = q8.q8_gemv_default_plan(32, 4096, 6144, 1)
+    assert cols.kernel == q8.Q8_KERNEL_MFMA_COLS
+    expect(7, q8.q8_gemv_parts_planned, A, three, 32, 4096, 1, cols, S0, A, 1 << 30)
+    assert q8.q8_parts_workspace_bytes(p, [], 1, 4096) == 0
+
+
+def test_parts_plan_is_the_side_by_side_product():
+    # the parts' columns side by side are one product's work; the column-group
+    # kernel (which does not walk parts) is replaced by the MFMA kernel
+    for (m, K, Ns, act) in ((1, 4096, (4096, 1024, 1024), 0), (8, 4096, (4096, 1024, 1024), 1),
+                            (16, 4096, (4096, 1024, 1024), 0), (32, 4096, (100, 30), 1),
+                            (4, 2048, (200,), 1)):
+        parts = [_part(N) for N in Ns]
+        got = q8.q8_gemv_parts_default_plan(parts, m, K, act)
+        wide = q8.q8_gemv_default_plan(m, K, sum(q8.q8_padded_cols(N) for N in Ns), act)
+        if wide.kernel == q8.Q8_KERNEL_MFMA_COLS:
+            assert got.kernel == q8.Q8_KERNEL_MFMA and got.waves == 16
+        else:
+            assert (got.kernel, got.rows, got.split_k) == (wide.kernel, wide.rows, wide.split_k)

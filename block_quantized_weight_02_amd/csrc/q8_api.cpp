@@ -474,23 +474,33 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
 // The product's plan over the parts' columns side by side, on a kernel that
 // walks units of any part (VALU or block-interleaved MFMA); the VALU kernel
 // takes 4 waves a workgroup once the workgroups outnumber the CUs, as the
-// gated pair does.
+// gated pair does.  The MFMA kernel splits K further while the splits still
+// fit one workgroup per CU: the parts of one attention block are narrower
+// than the products the single-product plan was settled on (measured on
+// MI355X, m = 16, K = 4096, N = 4096 + 1024 + 1024: one split 14.7 us, two
+// 12.1 us, three 16.0 us).
 q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
   q8_plan p = default_plan(m, K, cols, act_fmt);
   const int64_t NB = K / Q8_BLOCK;
+  const int64_t units = cols / Q8_TILE_COLS;
+  const DeviceFacts dev = device_facts();
   if (p.kernel == Q8_KERNEL_MFMA_COLS) {
     p.kernel = Q8_KERNEL_MFMA;
     p.waves = 16;
     p.kslices = 1;
-    const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
+    const size_t budget = (size_t)dev.lds_per_block - kStaticLdsReserve;
     int64_t S = 1;
     while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
                                         (int)S) > budget)
       ++S;
     p.split_k = (int32_t)S;
   }
-  if (p.kernel == Q8_KERNEL_VALU && cols / Q8_TILE_COLS * p.split_k > device_facts().cus)
-    p.waves = 4;
+  if (p.kernel == Q8_KERNEL_MFMA) {
+    int64_t S = p.split_k;
+    while (S < NB && units * (S + 1) <= dev.cus) ++S;
+    p.split_k = (int32_t)S;
+  }
+  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > dev.cus) p.waves = 4;
   return p;
 }
 

@@ -231,7 +231,14 @@ def test_parts_plan_is_the_side_by_side_product():
         parts = [_part(N) for N in Ns]
         got = q8.q8_gemv_parts_default_plan(parts, m, K, act)
         wide = q8.q8_gemv_default_plan(m, K, sum(q8.q8_padded_cols(N) for N in Ns), act)
-        if wide.kernel == q8.Q8_KERNEL_MFMA_COLS:
-            assert got.kernel == q8.Q8_KERNEL_MFMA and got.waves == 16
-        else:
+        units = sum(q8.q8_padded_cols(N) for N in Ns) // 64
+        if wide.kernel == q8.Q8_KERNEL_VALU:
             assert (got.kernel, got.rows, got.split_k) == (wide.kernel, wide.rows, wide.split_k)
+        else:
+            # MFMA: at least the splits the LDS needs, more while one
+            # workgroup per CU still holds them all (256 CUs on the host)
+            assert got.kernel == q8.Q8_KERNEL_MFMA and got.waves == 16 and got.rows == wide.rows
+            if wide.kernel == q8.Q8_KERNEL_MFMA:
+                assert got.split_k >= wide.split_k
+            assert got.split_k == K // 32 or units * (got.split_k + 1) > 256 or \
+                got.split_k == wide.split_k and units * got.split_k > 256

@@ -359,3 +359,33 @@ def test_library_workspace_reused_across_shapes():
         y = run_bf16(x, q, s)
         ref, bnd = oracle.gemv_bf16(x, q, s)
         assert_close(y[:, :N], ref, bnd, f"shape {i}")
+
+
+def test_row_split_halves():
+    """The product split along K (at a block boundary), as a row split across
+    devices would run it (int8_model.rs, the row-split projections): each half's
+    block dots are the full call's, bit for bit, its quantized activation is
+    the full one's blocks, and the halves' outputs sum to the full product
+    within the two halves' tolerances."""
+    m, K, N, K1 = 3, 2176, 200, 1056
+    x, q, s = inputs.random_case(m, K, N, seed=95)
+    halves = [(0, K1), (K1, K)]
+    xbuf = g.quantize(x)
+    xq, dx = g.act_host(xbuf, m, K)
+    Wq, _ = g.pack(q, s)
+    dots = g.block_dots(xbuf, Wq, m, K, N)
+    ysum = np.zeros((m, N))
+    for lo, hi in halves:
+        xh = np.ascontiguousarray(x[:, lo:hi])
+        bh = g.quantize(xh)
+        xqh, dxh = g.act_host(bh, m, hi - lo)
+        np.testing.assert_array_equal(xqh, xq[:, lo:hi])
+        np.testing.assert_array_equal(dxh.view(np.uint32), dx[:, lo // 32:hi // 32].view(np.uint32))
+        Wh, Wsh = g.pack(np.ascontiguousarray(q[lo:hi]), np.ascontiguousarray(s[lo // 32:hi // 32]))
+        dh = g.block_dots(bh, Wh, m, hi - lo, N)
+        np.testing.assert_array_equal(dh, dots[:, lo // 32:hi // 32, :])
+        yh = g.gemv(xdev(xh), Wh, Wsh, m, hi - lo, N, BF16)
+        ysum += yh[:, :N].astype(np.float64)
+    yref, bnd = oracle.gemv_bf16(x, q, s)
+    err = np.abs(ysum - yref)
+    assert np.all(err <= REL * bnd + 2 * ABS), np.max(err / (REL * bnd + 2 * ABS))

@@ -44,6 +44,10 @@ def _configure(lib):
     lib.q8o_block_dots.restype = ctypes.c_int
     lib.q8o_gemv_q8.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
     lib.q8o_gemv_q8.restype = ctypes.c_int
+    lib.q8o_quantize_act_two_words.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    lib.q8o_gemv_q8_two_words.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _p, _i64,
+                                          _p, _p]
+    lib.q8o_gemv_q8_two_words.restype = ctypes.c_int
     lib.q8o_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p]
     lib.q8o_view_rows.argtypes = [_i64, _i64]
     lib.q8o_view_rows.restype = _i64
@@ -202,6 +206,46 @@ def gemv_q8(xq: np.ndarray, dx: np.ndarray, q: np.ndarray, s: np.ndarray,
     b = np.empty((m, nc), np.float64)
     rc = _load().q8o_gemv_q8(_ptr(xq), _ptr(dx), _ptr(q), _ptr(s), m, K, N,
                              None if c is None else _ptr(c), nc, _ptr(y), _ptr(b))
+    if rc:
+        raise ValueError("bad shape")
+    return y, b
+
+
+def quantize_act_two_words(x_bf16: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The two-word form of a bf16 activation: ``(hi, lo, dx)``, two ``m x K``
+    int8 words and one fp32 scale per 32, standing for
+    ``dx * (hi + lo / 128)`` (reading in q8_oracle.c)."""
+    x = _c(x_bf16, np.uint16)
+    m, K = x.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    hi = np.empty((m, K), np.int8)
+    lo = np.empty((m, K), np.int8)
+    dx = np.empty((m, K // BLOCK), np.float32)
+    _load().q8o_quantize_act_two_words(_ptr(x), m, K, _ptr(hi), _ptr(lo), _ptr(dx))
+    return hi, lo, dx
+
+
+def gemv_q8_two_words(hi: np.ndarray, lo: np.ndarray, dx: np.ndarray, q: np.ndarray,
+                      s: np.ndarray, cols: Optional[Sequence[int]] = None
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """``(y, bound)`` for two-word int8 activations
+    ``x_k = dx[r, k/32] * (hi[r, k] + lo[r, k] / 128)``."""
+    hi = _c(hi, np.int8)
+    lo = _c(lo, np.int8)
+    dx = _c(dx, np.float32)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    m, K = hi.shape
+    K2, N = q.shape
+    if (lo.shape != hi.shape or K2 != K or dx.shape != (m, K // BLOCK)
+            or s.shape != (K // BLOCK, N)):
+        raise ValueError("shape mismatch")
+    c, nc = _cols(cols, N)
+    y = np.empty((m, nc), np.float64)
+    b = np.empty((m, nc), np.float64)
+    rc = _load().q8o_gemv_q8_two_words(_ptr(hi), _ptr(lo), _ptr(dx), _ptr(q), _ptr(s), m, K,
+                                       N, None if c is None else _ptr(c), nc, _ptr(y), _ptr(b))
     if rc:
         raise ValueError("bad shape")
     return y, b

@@ -20,6 +20,9 @@
  *   [LANE] logicaffeine_compile/codegen_cuda/lane/plan.rs
  *          - const QBLOCK / struct Buffer field `quantized`: an activation's
  *            quantized form is int8 values and one scale per 32 values.
+ *          - enum Q8MatKind, variant TwoPassInt8, and struct Buffer field
+ *            `quantized`: the two-pass numerics keeps two int8 words a value
+ *            and one scale per 32.
  *          - enum Launch, variant GemvGlu: two projections of one activation
  *            through a gate, act(x.wg + bg) * (x.wu + bu), SwiGLU (the SiLU
  *            gate) when no activation is named.
@@ -206,6 +209,51 @@ void q8o_quantize_rows_f32(const float *z, int64_t m, int64_t K, int8_t *zq,
   }
 }
 
+/*
+ * The two-word form ([LANE] struct Buffer field `quantized`, enum Q8MatKind,
+ * variant TwoPassInt8: under the two-pass numerics the quantized form holds
+ * two int8 words per value and still one scale per 32).  The pages do not
+ * give the split.  Reading taken: the first word and the scale are the
+ * one-word quantizer's above; the second word carries the first word's
+ * rounding residual in steps of d/128:
+ *   quot = fp32(x / d),  hi = clamp(round_half_away(quot), -127, 127),
+ *   lo   = round_half_away(128 * (quot - hi)),      so |lo| <= 64,
+ * and the value the words stand for is d * (hi + lo / 128).  amax == 0 gives
+ * d = 0 and both words 0.  hi, lo are m x K; dx is m x K/32.
+ * Parity against the pages is unpinned here: they define no split, so the
+ * pins fix this reading (worked values, invariants, its reduction to the
+ * one-word quantizer), not a formula the pages give.
+ */
+void q8o_quantize_act_two_words(const uint16_t *x, int64_t m, int64_t K, int8_t *hi,
+                                int8_t *lo, float *dx) {
+  const int64_t NB = K / Q8O_BLOCK;
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t b = 0; b < NB; ++b) {
+      const uint16_t *xb = x + r * K + b * Q8O_BLOCK;
+      double amax = 0.0;
+      for (int i = 0; i < Q8O_BLOCK; ++i) {
+        double a = fabs(bf16_value(xb[i]));
+        if (a > amax) amax = a;
+      }
+      float d = (float)(amax / 127.0);
+      dx[r * NB + b] = d;
+      for (int i = 0; i < Q8O_BLOCK; ++i) {
+        int vh = 0, vl = 0;
+        if (d != 0.0f) {
+          float quot = (float)(bf16_value(xb[i]) / (double)d);
+          double rh = round_half_away((double)quot);
+          if (rh > 127.0) rh = 127.0;
+          if (rh < -127.0) rh = -127.0;
+          vh = (int)rh;
+          vl = (int)round_half_away(128.0 * ((double)quot - rh));
+        }
+        hi[r * K + b * Q8O_BLOCK + i] = (int8_t)vh;
+        lo[r * K + b * Q8O_BLOCK + i] = (int8_t)vl;
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------------ */
 /* [Q8] module doc -- the product                                            */
 /* ------------------------------------------------------------------------ */
@@ -308,6 +356,47 @@ int q8o_gemv_q8(const int8_t *xq, const float *dx, const int8_t *q,
         double scale = (double)dx[r * NB + b] * (double)s[b * N + n];
         acc += scale * (double)dot;
         bnd += fabs(scale) * (double)dot_abs;
+      }
+      y[r * ncols + j] = acc;
+      bound[r * ncols + j] = bnd;
+    }
+  }
+  return 0;
+}
+
+/*
+ * Two-word int8 activations, x_k = dx[r, k/32] * (hi[r,k] + lo[r,k] / 128):
+ *   y[r,n]     = sum_b dx[r,b] * s[b,n] * (D_hi[r,b,n] + D_lo[r,b,n] / 128)
+ *   bound[r,n] = sum_k |x_k * w_kn|
+ * with D_hi, D_lo the int64 block dots of each word (hi + lo/128 is exact in
+ * fp64).  Returns 0, or -1 on a bad shape.
+ */
+int q8o_gemv_q8_two_words(const int8_t *hi, const int8_t *lo, const float *dx,
+                          const int8_t *q, const float *s, int64_t m, int64_t K,
+                          int64_t N, const int64_t *cols, int64_t ncols, double *y,
+                          double *bound) {
+  if (m <= 0 || K <= 0 || N <= 0 || K % Q8O_BLOCK != 0) return -1;
+  if (!cols) ncols = N;
+  const int64_t NB = K / Q8O_BLOCK;
+  int nt = q8o_threads();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t j = 0; j < ncols; ++j) {
+    const int64_t n = col_at(cols, j);
+    for (int64_t r = 0; r < m; ++r) {
+      double acc = 0.0, bnd = 0.0;
+      for (int64_t b = 0; b < NB; ++b) {
+        int64_t dot_hi = 0, dot_lo = 0;
+        double dot_abs = 0.0;
+        for (int64_t i = 0; i < Q8O_BLOCK; ++i) {
+          const int64_t k = Q8O_BLOCK * b + i;
+          const int64_t w = q[k * N + n];
+          dot_hi += (int64_t)hi[r * K + k] * w;
+          dot_lo += (int64_t)lo[r * K + k] * w;
+          dot_abs += fabs(((double)hi[r * K + k] + (double)lo[r * K + k] / 128.0) * (double)w);
+        }
+        double scale = (double)dx[r * NB + b] * (double)s[b * N + n];
+        acc += scale * ((double)dot_hi + (double)dot_lo / 128.0);
+        bnd += fabs(scale) * dot_abs;
       }
       y[r * ncols + j] = acc;
       bound[r * ncols + j] = bnd;

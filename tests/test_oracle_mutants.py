@@ -63,6 +63,23 @@ MUTANTS = [
     ("gated pair adds the gate bias to the up product",
      "double uv = u[r * n + j] + (bu ? (double)bu[j] : 0.0);",
      "double uv = u[r * n + j] + (bg ? (double)bg[j] : 0.0);"),
+    ("two-word residual in steps of 1/127",
+     "vl = (int)round_half_away(128.0 * ((double)quot - rh));",
+     "vl = (int)round_half_away(127.0 * ((double)quot - rh));"),
+    ("two-word residual rounds ties to even",
+     "vl = (int)round_half_away(128.0 * ((double)quot - rh));",
+     "vl = (int)rint(128.0 * ((double)quot - rh));"),
+    ("two-word residual taken from the unrounded quotient's floor",
+     "vl = (int)round_half_away(128.0 * ((double)quot - rh));",
+     "vl = (int)round_half_away(128.0 * ((double)quot - floor((double)quot)));"),
+    ("two-word product reads the first word twice",
+     "dot_lo += (int64_t)lo[r * K + k] * w;", "dot_lo += (int64_t)hi[r * K + k] * w;"),
+    ("two-word product scales the second word by 1/127",
+     "acc += scale * ((double)dot_hi + (double)dot_lo / 128.0);",
+     "acc += scale * ((double)dot_hi + (double)dot_lo / 127.0);"),
+    ("two-word bound drops the second word",
+     "dot_abs += fabs(((double)hi[r * K + k] + (double)lo[r * K + k] / 128.0) * (double)w);",
+     "dot_abs += fabs((double)hi[r * K + k] * (double)w);"),
     ("view rows drop the K tail",
      "return m * ((K + chunk - 1) / chunk) * Q8O_BLOCK;", "return m * (K / chunk) * Q8O_BLOCK;"),
     ("byte model counts 2-byte scales",

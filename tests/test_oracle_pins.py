@@ -303,6 +303,81 @@ def test_quantize_act_invariants():
 
 
 # --------------------------------------------------------------------------
+# plan.rs, the two-pass numerics (enum Q8MatKind, variant TwoPassInt8): the
+# two-word activation, hi + lo/128 in steps of the block's scale
+# --------------------------------------------------------------------------
+
+def test_two_words_first_word_is_the_one_word_form():
+    x, _, _ = inputs.random_case(5, 1024, 1, seed=60)
+    x[0, :32] = 0                                  # a zero block
+    hi, lo, dx = oracle.quantize_act_two_words(x)
+    xq, d1 = oracle.quantize_act(x)
+    np.testing.assert_array_equal(hi, xq)
+    np.testing.assert_array_equal(dx.view(np.uint32), d1.view(np.uint32))
+    assert (lo[0, :32] == 0).all() and dx[0, 0] == 0.0
+
+
+def test_two_words_worked_values():
+    # one block whose max is 127/128, so d = 2^-7; each value v * 2^-14 has at
+    # most 8 significant bits (exact in bf16) and stands for v/128 steps of d
+    v = np.array([127 * 128, 133, 253, -253, 320, -320, 2.5, -2.5, 0], np.float64)
+    want_hi = [127, 1, 2, -2, 3, -3, 0, 0, 0]
+    # 133/128 = 1 + 5/128; 253/128 = 2 - 3/128; 320/128 = 2.5 -> 3 (ties away)
+    # - 64/128; 2.5/128 of a step -> lo = 2.5 -> 3 (ties away)
+    want_lo = [0, 5, -3, 3, -64, 64, 3, -3, 0]
+    row = np.zeros(32, np.float32)
+    row[:len(v)] = v * 2.0 ** -14
+    x = bf16(row)[None, :]
+    assert (xval(x)[0, :len(v)] == v * 2.0 ** -14).all()
+    hi, lo, dx = oracle.quantize_act_two_words(x)
+    assert dx[0, 0] == 2.0 ** -7
+    np.testing.assert_array_equal(hi[0, :len(v)], want_hi)
+    np.testing.assert_array_equal(lo[0, :len(v)], want_lo)
+
+
+def test_two_words_invariants():
+    x, _, _ = inputs.random_case(6, 2048, 1, seed=61)
+    hi, lo, dx = oracle.quantize_act_two_words(x)
+    xv = xval(x).reshape(6, 64, 32)
+    d = dx.astype(np.float64)[..., None]
+    recon = d * (hi.reshape(6, 64, 32) + lo.reshape(6, 64, 32) / 128.0)
+    # residual at most half a step of d/128, plus the fp32 quotient's rounding
+    assert np.all(np.abs(xv - recon) <= d * (1 / 256 + 128 * 2.0 ** -24))
+    assert np.abs(lo).max() <= 64 and np.abs(hi).max() <= 127
+    # the second word is not idle: it removes most of the one-word error
+    one = d * hi.reshape(6, 64, 32)
+    assert np.abs(xv - recon).max() < np.abs(xv - one).max() / 50
+
+
+def test_two_words_product_brute_force_and_word_split():
+    x, q, s = inputs.random_case(3, 768, 70, seed=62)
+    hi, lo, dx = oracle.quantize_act_two_words(x)
+    y, bnd = oracle.gemv_q8_two_words(hi, lo, dx, q, s)
+    # dense numpy path: the value the words stand for times the dequantized W
+    xt = np.repeat(dx.astype(np.float64), 32, axis=1) * (hi + lo / 128.0)
+    w = dense_w(q, s)
+    ref = xt @ w
+    refb = np.abs(xt) @ np.abs(w)
+    assert np.all(np.abs(y - ref) <= 1e-12 * refb)
+    assert np.all(np.abs(bnd - refb) <= 1e-12 * refb)
+    # the two passes: each word's one-word product, the second scaled by 1/128
+    yh, _ = oracle.gemv_q8(hi, dx, q, s)
+    yl, _ = oracle.gemv_q8(lo, dx, q, s)
+    assert np.all(np.abs(y - (yh + yl / 128.0)) <= 1e-12 * refb)
+
+
+def test_two_words_error_against_bf16_product():
+    # |y_2w - y_bf16| <= sum_k |x_k - xt_k| |w_k| <= sum_b d_b (1/256 + 2^-17) sum_i |w|
+    x, q, s = inputs.random_case(4, 1024, 50, seed=63)
+    hi, lo, dx = oracle.quantize_act_two_words(x)
+    y2, _ = oracle.gemv_q8_two_words(hi, lo, dx, q, s)
+    yb, _ = oracle.gemv_bf16(x, q, s)
+    absw = np.abs(dense_w(q, s)).reshape(32, 32, 50).sum(axis=1)        # (K/32, N)
+    lim = dx.astype(np.float64) @ absw * (1 / 256 + 2.0 ** -17)
+    assert np.all(np.abs(y2 - yb) <= lim + 1e-15)
+
+
+# --------------------------------------------------------------------------
 # from_q8.rs: byte model and view size, and the figures the page states
 # --------------------------------------------------------------------------
 

@@ -19,12 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libq8gemv.so")
 
 Q8_ACT_BF16 = 0
 Q8_ACT_Q8_0 = 1
+Q8_ACT_Q8_0_TWO_WORDS = 2
 Q8_KERNEL_VALU = 0
 Q8_KERNEL_MFMA = 1
 Q8_KERNEL_MFMA_COLS = 2
 Q8_MAX_ROWS = 32
 Q8_MAX_GEMM_ROWS = 8192
 Q8_MAX_PARTS = 4
+Q8_MAX_TWO_WORD_ROWS = 16
 
 STATUS = {0: "Q8_OK", 1: "Q8_ERR_SHAPE", 2: "Q8_ERR_ACT_FMT", 3: "Q8_ERR_NULL",
           4: "Q8_ERR_ALIGN", 5: "Q8_ERR_WORKSPACE", 6: "Q8_ERR_HIP", 7: "Q8_ERR_PLAN"}
@@ -74,10 +76,13 @@ _SIGS = {
     "q8_packed_scales_bytes": (_sz, [_i64, _i64]),
     "q8_act_scales_offset": (_sz, [_i64, _i64]),
     "q8_act_bytes": (_sz, [_i64, _i64]),
+    "q8_act_two_words_scales_offset": (_sz, [_i64, _i64]),
+    "q8_act_two_words_bytes": (_sz, [_i64, _i64]),
     "q8_gemv_workspace_bytes": (_sz, [_i64, _i64, _i64, _int]),
     "q8_repack": (_int, [_p, _p, _i64, _i64, _p, _p, _p]),
     "q8_unpack": (_int, [_p, _p, _i64, _i64, _p, _p, _p]),
     "q8_quantize_act": (_int, [_p, _p, _i64, _i64, _p]),
+    "q8_quantize_act_two_words": (_int, [_p, _p, _i64, _i64, _p]),
     "q8_gemv": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
     "q8_gemv_ws": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _p, _sz]),
     "q8_gemv_block_dots": (_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
@@ -188,6 +193,14 @@ def q8_act_bytes(m: int, K: int) -> int:
     return int(lib().q8_act_bytes(m, K))
 
 
+def q8_act_two_words_scales_offset(m: int, K: int) -> int:
+    return int(lib().q8_act_two_words_scales_offset(m, K))
+
+
+def q8_act_two_words_bytes(m: int, K: int) -> int:
+    return int(lib().q8_act_two_words_bytes(m, K))
+
+
 def q8_gemv_workspace_bytes(m: int, K: int, N: int, act_fmt: int) -> int:
     return int(lib().q8_gemv_workspace_bytes(m, K, N, act_fmt))
 
@@ -206,6 +219,10 @@ def q8_unpack(W_q8, W_q8_scale, K, N, q_kn, s_kn, stream=None) -> None:
 
 def q8_quantize_act(x_bf16, x_q8, m, K, stream=None) -> None:
     _check(lib().q8_quantize_act(_addr(x_bf16), _addr(x_q8), m, K, _stream(stream)))
+
+
+def q8_quantize_act_two_words(x_bf16, x_q8x2, m, K, stream=None) -> None:
+    _check(lib().q8_quantize_act_two_words(_addr(x_bf16), _addr(x_q8x2), m, K, _stream(stream)))
 
 
 def q8_gemv(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream=None) -> None:

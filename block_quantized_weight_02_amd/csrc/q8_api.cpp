@@ -71,9 +71,26 @@ int check_m(int64_t m, int64_t max_rows = Q8_MAX_ROWS) {
 }
 
 int check_act(int act_fmt) {
-  if (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)
-    return fail(Q8_ERR_ACT_FMT, "act_fmt = %d: no kernel for it (0 bf16, 1 Q8_0)",
-                act_fmt);
+  if (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0 && act_fmt != Q8_ACT_Q8_0_TWO_WORDS)
+    return fail(Q8_ERR_ACT_FMT,
+                "act_fmt = %d: no kernel for it (0 bf16, 1 Q8_0, 2 Q8_0 two words)", act_fmt);
+  return Q8_OK;
+}
+
+// Rows of a product for its activation format (two words: at most 16).
+int check_m_act(int64_t m, int act_fmt) {
+  int st = check_m(m);
+  if (st) return st;
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS) return check_m(m, Q8_MAX_TWO_WORD_ROWS);
+  return Q8_OK;
+}
+
+// The products that take no two-word activation.
+int check_one_word_act(int act_fmt, const char *what) {
+  int st = check_act(act_fmt);
+  if (st) return st;
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS)
+    return fail(Q8_ERR_ACT_FMT, "%s takes no two-word activation (act_fmt 2)", what);
   return Q8_OK;
 }
 
@@ -90,6 +107,12 @@ int hip_fail(hipError_t e, const char *what) {
 
 size_t act_scales_offset(int64_t m, int64_t K) {
   return (size_t)round_up(m * K, 256);
+}
+
+// Offset of the scales in the activation buffer of a format: the two-word
+// form holds 2m rows of words before its scales.
+size_t act_scales_offset_of(int act_fmt, int64_t m, int64_t K) {
+  return act_scales_offset(act_fmt == Q8_ACT_Q8_0_TWO_WORDS ? 2 * m : m, K);
 }
 
 // LDS per workgroup kept free for the kernels' static shared variables.
@@ -145,6 +168,22 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
   q8_plan p;
   p.kslices = 1;
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS) {
+    // The block-interleaved MFMA kernel, its 32 rows the two words' 16 each;
+    // K split for the LDS, then further while the splits still fill one
+    // workgroup per CU.
+    p.kernel = Q8_KERNEL_MFMA;
+    p.rows = 32;
+    p.waves = 16;
+    const size_t budget = (size_t)dev.lds_per_block - kStaticLdsReserve;
+    int64_t S = 1;
+    while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
+                                        (int)S) > budget)
+      ++S;
+    while (S < NB && T * (S + 1) <= dev.cus) ++S;
+    p.split_k = (int32_t)S;
+    return p;
+  }
   const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 4 : 8;
   if (m <= valu_rows) {
     p.kernel = Q8_KERNEL_VALU;
@@ -282,6 +321,8 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
              const PairArgs *pair = nullptr) {
   const bool write_dots = dots != nullptr;
   const int nw = pair ? 2 : 1;
+  if (pair && act_fmt == Q8_ACT_Q8_0_TWO_WORDS)
+    return fail(Q8_ERR_ACT_FMT, "the gated pair takes no two-word activation (act_fmt 2)");
   if (ep && ep->y_q8 && plan.kernel == Q8_KERNEL_MFMA_COLS && plan.split_k * nw < 2)
     return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel quantizes its output in the split-K "
                 "finish: y_q8 needs split_k >= 2 (or the MFMA or VALU kernel)");
@@ -300,8 +341,8 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   a.Npad = (int)Npad;
   a.T = (int)(Npad / Q8_TILE_COLS);
   a.split_k = plan.split_k;
-  a.act_scale_off = (unsigned)act_scales_offset(m, K);
-  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+  a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "activation too large");
   a.ep.N = (int)N;
   a.ep.write_y = 1;
@@ -346,6 +387,7 @@ int check_gemv_args(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   if ((st = check_m(m))) return st;
   if ((st = check_kn(K, N))) return st;
   if ((st = check_act(act_fmt))) return st;
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && (st = check_m(m, Q8_MAX_TWO_WORD_ROWS))) return st;
   if ((st = check_ptr(x, "x"))) return st;
   if ((st = check_ptr(W_q8, "W_q8"))) return st;
   if (need_scales && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
@@ -424,6 +466,7 @@ int check_glu_args(const void *x, const int8_t *Wg, const float *Wg_s, const int
                    int act_fmt, const q8_glu_epilogue *ep) {
   int st = check_gemv_args(x, Wg, Wg_s, y, "y", m, K, N, act_fmt, true, false);
   if (st) return st;
+  if ((st = check_one_word_act(act_fmt, "the gated pair"))) return st;
   if ((st = check_ptr(Wu, "Wu_q8")) || (st = check_ptr(Wu_s, "Wu_q8_scale"))) return st;
   return check_glu_epilogue(ep, y);
 }
@@ -458,7 +501,9 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
                      int act_fmt, int64_t *cols) {
   int st;
   if ((st = check_parts(parts, n_parts, cols))) return st;
-  if ((st = check_m(m)) || (st = check_kn(K, *cols)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_m(m)) || (st = check_kn(K, *cols)) ||
+      (st = check_one_word_act(act_fmt, "the product in parts")))
+    return st;
   if ((st = check_ptr(x, "x"))) return st;
   for (int i = 0; i < n_parts; ++i) {
     const q8_part &pt = parts[i];
@@ -590,7 +635,7 @@ size_t q8_act_bytes(int64_t m, int64_t K) {
 }
 
 size_t q8_gemv_workspace_bytes(int64_t m, int64_t K, int64_t N, int act_fmt) {
-  if (check_m(m) || check_kn(K, N) || check_act(act_fmt)) return 0;
+  if (check_act(act_fmt) || check_m_act(m, act_fmt) || check_kn(K, N)) return 0;
   return plan_ws_bytes(default_plan(m, K, N, act_fmt), m, N);
 }
 
@@ -636,9 +681,36 @@ int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
   return ok();
 }
 
+size_t q8_act_two_words_scales_offset(int64_t m, int64_t K) {
+  if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
+  return act_scales_offset(2 * m, K);
+}
+
+size_t q8_act_two_words_bytes(int64_t m, int64_t K) {
+  if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
+  return act_scales_offset(2 * m, K) + (size_t)(m * (K / Q8_BLOCK)) * 4;
+}
+
+int q8_quantize_act_two_words(const uint16_t *x_bf16, void *x_q8x2, int64_t m, int64_t K,
+                              hipStream_t stream) {
+  int st;
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS))) return st;
+  if ((st = check_kn(K, 1))) return st;
+  if (act_scales_offset(2 * m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the two-word layout",
+                (long long)(m * K));
+  if ((st = check_ptr(x_bf16, "x_bf16")) || (st = check_ptr(x_q8x2, "x_q8x2"))) return st;
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_quantize_act_two_words(x_bf16, x_q8x2, (int)m, (int)K,
+                                                   (unsigned)act_scales_offset(2 * m, K), stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize_act_two_words launch");
+  return ok();
+}
+
 int q8_gemv_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, q8_plan *plan) {
   int st;
-  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_act(act_fmt)) || (st = check_m_act(m, act_fmt)) || (st = check_kn(K, N)))
+    return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = default_plan(m, K, N, act_fmt);
   return ok();
@@ -688,7 +760,8 @@ int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
 int q8_gemv_fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
                                const q8_epilogue *epilogue, q8_plan *plan) {
   int st;
-  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_act(act_fmt)) || (st = check_m_act(m, act_fmt)) || (st = check_kn(K, N)))
+    return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = fused_default_plan(m, K, N, act_fmt, epilogue);
   return ok();
@@ -749,7 +822,9 @@ size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K, int64_t
 
 int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, q8_plan *plan) {
   int st;
-  if ((st = check_m(m)) || (st = check_kn(K, N)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_m(m)) || (st = check_kn(K, N)) ||
+      (st = check_one_word_act(act_fmt, "the gated pair")))
+    return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = glu_default_plan(m, K, N, act_fmt);
   return ok();
@@ -788,7 +863,8 @@ namespace {
 int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *y,
              int32_t *dots, int64_t m, int64_t K, int64_t N, int act_fmt, hipStream_t stream) {
   int st;
-  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, N)) || (st = check_act(act_fmt)))
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, N)) ||
+      (st = check_one_word_act(act_fmt, "q8_gemm")))
     return st;
   if ((st = check_ptr(x, "x")) || (st = check_ptr(W_q8, "W_q8"))) return st;
   if (!dots && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
@@ -875,7 +951,9 @@ int q8_gemv_parts_default_plan(const q8_part *parts, int n_parts, int64_t m, int
   int st;
   int64_t cols = 0;
   if ((st = check_parts(parts, n_parts, &cols))) return st;
-  if ((st = check_m(m)) || (st = check_kn(K, cols)) || (st = check_act(act_fmt))) return st;
+  if ((st = check_m(m)) || (st = check_kn(K, cols)) ||
+      (st = check_one_word_act(act_fmt, "the product in parts")))
+    return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = parts_default_plan(m, K, cols, act_fmt);
   return ok();

@@ -28,7 +28,11 @@ constexpr int kChunkBytes = 2048;   // one tile x one block of values
 constexpr int kHalfBytes = 1024;    // 16 k-values of each of the 64 columns
 constexpr int kLayoutVersion = 2;
 
-enum Act { kActBf16 = 0, kActQ8 = 1 };
+// Activation forms: bf16; int8 with one scale per 32 (one word); and two
+// int8 words per value with one scale per 32, the second word the first's
+// rounding residual in steps of 1/128 of the scale (a buffer laid out as
+// 2m one-word rows: the first words, then the second, then m rows of scales).
+enum Act { kActBf16 = 0, kActQ8 = 1, kActQ8x2 = 2 };
 
 // Several products of one activation in one launch (the GEMV in parts): part
 // p multiplies by its own packed weight (wq[p], wsc[p], N[p] columns) into
@@ -90,6 +94,8 @@ hipError_t launch_unpack(const int8_t *wq, const float *wsc, int K, int N,
                          int8_t *q_kn, float *s_kn, hipStream_t stream);
 hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
                                unsigned scale_off, hipStream_t stream);
+hipError_t launch_quantize_act_two_words(const uint16_t *x, void *x_q8x2, int m, int K,
+                                         unsigned scale_off, hipStream_t stream);
 // kernel: 0 VALU, 1 MFMA (waves split K, each over all 64 columns), 2 MFMA
 // (waves own 16-column groups); rows: 1,2,4,8,16,32; act: Act; waves: 4, 8
 // or 16; kslices: waves sharing one column group's K range (kernel 2 only).

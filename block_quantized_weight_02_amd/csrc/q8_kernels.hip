@@ -109,6 +109,35 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ xq,
   }
 }
 
+// The two-word form: the first word and the scale as above, the second word
+// round_half_away(128 * (quot - hi)) of the fp32 quotient quot = v / d.
+// quot - hi is exact in fp32 (hi is quot rounded, within a factor of two of
+// it or zero) and the scaling by 128 is exact, so the second word is unique.
+__global__ void __launch_bounds__(256)
+quantize_act_two_words_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ hi,
+                              int8_t *__restrict__ lo, float *__restrict__ dx,
+                              long long total) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = idx < total;
+  const float v = valid ? __uint_as_float((uint32_t)x[idx] << 16) : 0.0f;
+  float a = fabsf(v);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
+  const float d = q8_scale_of(a);
+  if (valid) {
+    int h = 0, l = 0;
+    if (d != 0.0f) {
+      const float quot = (float)((double)v / (double)d);
+      const float rh = fminf(fmaxf(roundf(quot), -127.0f), 127.0f);
+      h = (int)rh;
+      l = (int)roundf((quot - rh) * 128.0f);
+    }
+    hi[idx] = (int8_t)h;
+    lo[idx] = (int8_t)l;
+    if ((idx & 31) == 0) dx[idx >> 5] = d;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // the product: shared pieces
 // ---------------------------------------------------------------------------
@@ -576,6 +605,9 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
   constexpr int ppr = kRowBytes / 16;
   const int total = nblk * MR * ppr;
   const char *xbase = static_cast<const char *>(xv);
+  // Two-word form (MR = 32, m <= 16): LDS rows 0-15 take the first words of
+  // rows 0-15, rows 16-31 the second words (buffer rows m .. 2m-1).
+  constexpr bool kTwo = ACT == kActQ8x2;
   for (int p0 = threadIdx.x; p0 < total; p0 += NTHREADS * kBatch) {
     uint4 v[kBatch];
 #pragma unroll
@@ -584,8 +616,9 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
       const int piece = p % ppr;
       const int r = (p / ppr) % MR;
       const int bb = p / (ppr * MR);
+      const int src = kTwo ? min(r & 15, m - 1) + (r >= 16 ? m : 0) : min(r, m - 1);
       v[q] = *reinterpret_cast<const uint4 *>(
-          xbase + ((size_t)min(r, m - 1) * K + (size_t)(b_lo + bb) * kBlock) * (kRowBytes / 32) +
+          xbase + ((size_t)src * K + (size_t)(b_lo + bb) * kBlock) * (kRowBytes / 32) +
           piece * 16);
     }
 #pragma unroll
@@ -594,10 +627,10 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
       const int r = (p / ppr) % MR;
       if (p < total)
         *reinterpret_cast<uint4 *>(lds + (size_t)p * 16) =
-            (r < m) ? v[q] : make_uint4(0u, 0u, 0u, 0u);
+            ((kTwo ? (r & 15) : r) < m) ? v[q] : make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  if constexpr (ACT == kActQ8) {
+  if constexpr (ACT != kActBf16) {
     float *dxs = reinterpret_cast<float *>(lds + (size_t)nblk * MR * kRowBytes);
     const float *dxp = reinterpret_cast<const float *>(xbase + act_scale_off);
     const int nd = nblk * MR;
@@ -606,12 +639,14 @@ __device__ __forceinline__ void stage_activation(char *lds, const void *__restri
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int p = min(p0 + q * NTHREADS, nd - 1);
-        v[q] = dxp[(size_t)min(p % MR, m - 1) * NB + b_lo + p / MR];
+        const int r = kTwo ? (p % MR) & 15 : p % MR;
+        v[q] = dxp[(size_t)min(r, m - 1) * NB + b_lo + p / MR];
       }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         const int p = p0 + q * NTHREADS;
-        if (p < nd) dxs[p] = (p % MR < m) ? v[q] : 0.0f;
+        const int r = kTwo ? (p % MR) & 15 : p % MR;
+        if (p < nd) dxs[p] = (r < m) ? v[q] : 0.0f;
       }
     }
   }
@@ -1105,6 +1140,30 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
               for (int e = 0; e < 4; ++e) acc[rg][g][e] = fmaf(scs[g], d[e], acc[rg][g][e]);
             }
           }
+        } else if constexpr (ACT == kActQ8x2) {
+          // First words in rows 0-15, second words in rows 16-31: one int8
+          // MFMA each, and the two passes' dots meet exactly in int32
+          // (|128 D_hi + D_lo| <= 128 * 516128 + 64 * 127 * 32 < 2^27).
+          const long ahi = *reinterpret_cast<const long *>(
+              lds + ((size_t)lb * MR + li) * kRowBytes + lj * 8);
+          const long alo = *reinterpret_cast<const long *>(
+              lds + ((size_t)lb * MR + 16 + li) * kRowBytes + lj * 8);
+          const float4 dx4 = *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + lj * 4);
+          const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const long bw = __builtin_bit_cast(long, st.w[u][g]);
+            const i32x4_t dh =
+                __builtin_amdgcn_mfma_i32_16x16x32_i8(ahi, bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+            const i32x4_t dl =
+                __builtin_amdgcn_mfma_i32_16x16x32_i8(alo, bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+            const float scg = (g == 0) ? st.sc[u].x : (g == 1) ? st.sc[u].y
+                            : (g == 2) ? st.sc[u].z : st.sc[u].w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[0][g][e] = fmaf(dxv[e] * scg, (float)(dh[e] * 128 + dl[e]) * 0.0078125f,
+                                  acc[0][g][e]);
+          }
         } else {
           long a[RG];
           float4 dx4[RG];
@@ -1166,8 +1225,10 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     // The W waves meet in LDS, then the tile is stored (or its split-K
     // partial published and combined by the last split to arrive).
     if (red_on_stage) __syncthreads();   // every wave is done reading the stage
+    // the two-word form carries its rows in the first row group only
+    constexpr int kOutRG = ACT == kActQ8x2 ? 1 : RG;
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
+    for (int rg = 0; rg < kOutRG; ++rg)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -1301,7 +1362,7 @@ hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
 
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
-  if constexpr (!DOTS) {
+  if constexpr (!DOTS && ACT != kActQ8x2) {
     if (a.ep.nw == 2) return launch_mfma_k<MR, ACT, DOTS, W, true, false>(a, stream);
     if (a.ep.parts.n > 0) return launch_mfma_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }
@@ -1378,6 +1439,8 @@ Launcher pick_mfma(int rows, int act, bool dots) {
   if (act == kActBf16) return dots ? nullptr : pick_mfma_rows<kActBf16, false, W>(rows);
   if (act == kActQ8)
     return dots ? pick_mfma_rows<kActQ8, true, W>(rows) : pick_mfma_rows<kActQ8, false, W>(rows);
+  // two words: the first words fill rows 0-15 and the second rows 16-31
+  if (act == kActQ8x2 && !dots && rows == 32) return &launch_mfma<32, kActQ8x2, false, W>;
   return nullptr;
 }
 
@@ -1462,6 +1525,16 @@ hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
   int8_t *xq = static_cast<int8_t *>(x_q8);
   float *dx = reinterpret_cast<float *>(static_cast<char *>(x_q8) + scale_off);
   quantize_act_kernel<<<blocks_for(total), 256, 0, stream>>>(x, xq, dx, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_two_words(const uint16_t *x, void *x_q8x2, int m, int K,
+                                         unsigned scale_off, hipStream_t stream) {
+  const long long total = (long long)m * K;
+  int8_t *hi = static_cast<int8_t *>(x_q8x2);
+  int8_t *lo = hi + total;
+  float *dx = reinterpret_cast<float *>(static_cast<char *>(x_q8x2) + scale_off);
+  quantize_act_two_words_kernel<<<blocks_for(total), 256, 0, stream>>>(x, hi, lo, dx, total);
   return hipGetLastError();
 }
 

@@ -56,8 +56,9 @@ extern "C" {
 
 /* Activation formats. */
 typedef enum {
-  Q8_ACT_BF16 = 0, /* x is m x K bf16 */
-  Q8_ACT_Q8_0 = 1  /* x is the q8_quantize_act buffer */
+  Q8_ACT_BF16 = 0,           /* x is m x K bf16                              */
+  Q8_ACT_Q8_0 = 1,           /* x is the q8_quantize_act buffer              */
+  Q8_ACT_Q8_0_TWO_WORDS = 2  /* x is the q8_quantize_act_two_words buffer    */
 } q8_act_fmt;
 
 /* Status codes (errors are values, as the pages' lowering returns its
@@ -76,6 +77,7 @@ typedef enum {
 #define Q8_BLOCK 32     /* K rows per Q8_0 block                              */
 #define Q8_MAX_ROWS 32  /* most activation rows per call (fn q8_gemv_applies) */
 #define Q8_TILE_COLS 64 /* column tile: N is padded to a multiple of this     */
+#define Q8_MAX_TWO_WORD_ROWS 16 /* most rows of a two-word activation product */
 
 /* ---- sizes (host functions, no device work) ---------------------------- */
 
@@ -90,6 +92,10 @@ size_t q8_packed_scales_bytes(int64_t K, int64_t N);
 size_t q8_act_scales_offset(int64_t m, int64_t K);
 /* Total bytes of a quantized activation buffer. 0 on a bad shape. */
 size_t q8_act_bytes(int64_t m, int64_t K);
+/* The same two for the two-word form: its 2*m*K bytes of words, then the
+ * scales at 2*m*K rounded up to 256 (m rows of K/32 fp32). */
+size_t q8_act_two_words_scales_offset(int64_t m, int64_t K);
+size_t q8_act_two_words_bytes(int64_t m, int64_t K);
 /* Bytes of the split-K workspace q8_gemv_ws needs for this shape (may be 0). */
 size_t q8_gemv_workspace_bytes(int64_t m, int64_t K, int64_t N, int act_fmt);
 
@@ -116,7 +122,8 @@ int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K,
 
 /*
  * q8_quantize_act: bf16 activation -> its quantized form, per row and per
- * 32-value block (plan.rs, const QBLOCK: "int8 values and a scale per 32").
+ * 32-value block (plan.rs, const QBLOCK and struct Buffer field `quantized`:
+ * int8 values with one scale for each 32 of them).
  * The pages do not give the formula; this library computes
  *     amax = max|x|,  d = fp32(amax / 127)  (amax == 0: d = 0, xq = 0),
  *     xq   = clamp(round_half_away_from_zero(fp32(x / d)), -127, 127)
@@ -126,12 +133,35 @@ int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K,
 int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
                     hipStream_t stream);
 
+/*
+ * q8_quantize_act_two_words: bf16 activation -> its two-word form, the
+ * quantized form of the two-pass numerics (plan.rs, enum Q8MatKind, variant
+ * TwoPassInt8, and struct Buffer field `quantized`: two int8 words a value,
+ * still one scale per 32).  The pages do not give the split; this library
+ * takes d and the first word hi as q8_quantize_act does and puts the first
+ * word's rounding residual, in steps of d/128, in the second:
+ *     quot = fp32(x / d),  hi = clamp(round_half_away(quot), -127, 127),
+ *     lo   = round_half_away(128 * (quot - hi))        (|lo| <= 64)
+ * so the words stand for d * (hi + lo/128).  Layout: hi as m x K int8 at 0,
+ * lo as m x K int8 at m*K (the two are the rows of a 2m-row one-word
+ * buffer), the m x K/32 fp32 scales at q8_act_two_words_scales_offset(m, K);
+ * q8_act_two_words_bytes(m, K) bytes in all.  Requires 1 <= m <=
+ * Q8_MAX_GEMM_ROWS, K > 0, K % 32 == 0.
+ */
+int q8_quantize_act_two_words(const uint16_t *x_bf16, void *x_q8x2, int64_t m,
+                              int64_t K, hipStream_t stream);
+
 /* ---- the product ---------------------------------------------------------- */
 
 /*
  * q8_gemv: y = x . W over the packed Q8_0 weight (from_q8.rs, module doc and
- * fn q8_fold).  x per act_fmt; y is m x N_pad fp32.  Requires 1 <= m <= 32,
- * K > 0, K % 32 == 0, N >= 1.  When the chosen plan splits K across
+ * fn q8_fold).  x per act_fmt; y is m x N_pad fp32.  Requires 1 <= m <= 32
+ * (two-word activations: m <= Q8_MAX_TWO_WORD_ROWS), K > 0, K % 32 == 0,
+ * N >= 1.  Two-word activations run each block's two int8 passes on the
+ * matrix cores and join them exactly in int32 before the block's scale
+ * (128 * D_hi + D_lo, then times dx * s / 128); only the MFMA kernel takes
+ * them (plans naming another kernel are Q8_ERR_PLAN), and the gated pair,
+ * the parts and q8_gemm do not (Q8_ERR_ACT_FMT).  When the chosen plan splits K across
  * workgroups it uses a workspace the library allocates on first need and
  * keeps per (device, stream) until q8_release_workspaces(); that first call
  * allocates, so it must not be inside a graph capture.  Calls on one stream

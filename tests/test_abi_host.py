@@ -73,7 +73,7 @@ def test_whole_block_error_names_declared_and_bound():
 
 
 def test_act_fmt_error():
-    expect(2, q8.q8_gemv, A, A, A, A, 1, 64, 8, 2, S0)
+    expect(2, q8.q8_gemv, A, A, A, A, 1, 64, 8, 3, S0)
     expect(2, q8.q8_gemv, A, A, A, A, 1, 64, 8, -1, S0)
 
 
@@ -242,3 +242,32 @@ def test_parts_plan_is_the_side_by_side_product():
                 assert got.split_k >= wide.split_k
             assert got.split_k == K // 32 or units * (got.split_k + 1) > 256 or \
                 got.split_k == wide.split_k and units * got.split_k > 256
+
+
+def test_two_word_rules():
+    TW = q8.Q8_ACT_Q8_0_TWO_WORDS
+    # sizes: 2m rows of words, then m rows of K/32 scales
+    assert q8.q8_act_two_words_scales_offset(3, 64) == 512
+    assert q8.q8_act_two_words_bytes(3, 64) == 512 + 3 * 2 * 4
+    assert q8.q8_act_two_words_bytes(0, 64) == 0 and q8.q8_act_two_words_bytes(1, 48) == 0
+    expect(1, q8.q8_quantize_act_two_words, A, A, 0, 64, S0)
+    expect(1, q8.q8_quantize_act_two_words, A, A, 1, 48, S0)
+    expect(3, q8.q8_quantize_act_two_words, None, A, 1, 64, S0)
+    expect(4, q8.q8_quantize_act_two_words, A, A + 2, 1, 64, S0)
+    # at most 16 rows; only the MFMA kernel; not the pair, the parts or the GEMM
+    expect(1, q8.q8_gemv, A, A, A, A, 17, 64, 8, TW, S0)
+    expect(1, q8.q8_gemv_default_plan, 17, 64, 8, TW)
+    assert q8.q8_gemv_workspace_bytes(17, 64, 8, TW) == 0
+    p = q8.q8_gemv_default_plan(16, 4096, 14336, TW)
+    assert (p.kernel, p.rows, p.waves) == (q8.Q8_KERNEL_MFMA, 32, 16)
+    small = q8.q8_gemv_default_plan(1, 4096, 4096, TW)
+    assert small.split_k >= 2          # 64 tiles: the splits fill the CUs
+    for kernel, rows, waves in ((q8.Q8_KERNEL_VALU, 1, 8), (q8.Q8_KERNEL_MFMA, 16, 16),
+                                (q8.Q8_KERNEL_MFMA_COLS, 32, 16)):
+        bad = q8.q8_plan()
+        bad.kernel, bad.rows, bad.split_k, bad.waves, bad.kslices = kernel, rows, 2, waves, 1
+        expect(7, q8.q8_gemv_planned, A, A, A, A, 1, 64, 8, TW, bad, S0, A, 1 << 30)
+    expect(2, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, TW, None, S0)
+    expect(2, q8.q8_gemv_glu_default_plan, 1, 64, 8, TW)
+    expect(2, q8.q8_gemv_parts, A, [q8.make_part(A, A, A, 64)], 1, 64, TW, S0)
+    expect(2, q8.q8_gemm, A, A, A, A, 64, 64, 8, TW, S0)

@@ -25,7 +25,9 @@ times the product with bias, residual and quantized output beside the plain
 product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
 one launch) beside two plain products, at m = 1 and m = 16, and the product
 in parts (query, key and value projections of one activation in one launch)
-beside the same products one by one, at m = 1 and m = 16; `context` gives
+beside the same products one by one, at m = 1 and m = 16, and the two-word
+int8 activation (quantize then product) beside the one-word step, at m = 1
+and m = 16; `context` gives
 the headline with one weight copy reused and a 1 GiB device copy's rate;
 `prefill` times the many-row product (m = 512) against the MFMA peak.
 """
@@ -395,6 +397,60 @@ def measure_parts(pw, steps, warmup, rotate=True):
                      "waves": plan.waves, "kslices": plan.kslices}}
 
 
+def measure_two_words(w, steps, warmup, rotate=True):
+    """The two-word int8 activation (the two-pass numerics): a step is
+    q8_quantize_act_two_words then q8_gemv, beside the one-word step
+    (q8_quantize_act then q8_gemv) on the same weights."""
+    import torch
+    st = Setup(w, rotate=rotate)
+    q8 = st.q8
+    m, K, N = w.m, w.K, w.N
+    lib = q8.lib()
+    sp = st.stream.cuda_stream
+    x2 = torch.empty(q8.q8_act_two_words_bytes(m, K), dtype=torch.uint8, device="cuda:0")
+    tw = q8.Q8_ACT_Q8_0_TWO_WORDS
+    gemv_args = [(x2.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), st.y.data_ptr(), m, K, N, tw, sp)
+                 for (Wq, Ws) in st.W]
+    one_args = [(st.xq.data_ptr(), Wq.data_ptr(), Ws.data_ptr(), st.y.data_ptr(), m, K, N,
+                 q8.Q8_ACT_Q8_0, sp) for (Wq, Ws) in st.W]
+    quant2 = (st.x.data_ptr(), x2.data_ptr(), m, K, sp)
+    plan = q8.q8_gemv_default_plan(m, K, N, tw)
+
+    def ok(rc):
+        if rc:
+            raise RuntimeError(q8.q8_last_error())
+
+    def two(i):
+        ok(lib.q8_quantize_act_two_words(*quant2))
+        ok(lib.q8_gemv(*gemv_args[i % st.copies]))
+
+    def two_product(i):
+        ok(lib.q8_gemv(*gemv_args[i % st.copies]))
+
+    def one(i):
+        ok(st._quant(*st._quant_args))
+        ok(lib.q8_gemv(*one_args[i % st.copies]))
+
+    for i in range(warmup):
+        two(i)
+        one(i)
+    product_ms = time_loop(two_product, steps)
+    two_ms = time_loop(two, steps)
+    one_ms = time_loop(one, steps)
+    b = algorithmic_bytes(w)
+    xbytes = 2 * m * K + 4 * m * (K // 32)
+    nbytes = b["values"] + b["scales"] + xbytes + b["y"]
+    del st
+    torch.cuda.empty_cache()
+    log(f"[bench] two words {w.name}: step {two_ms * 1e3:.2f} us (product {product_ms * 1e3:.2f} us) "
+        f"vs one word {one_ms * 1e3:.2f} us, plan={plan}")
+    return {"workload": w.name, "two_words_step_us": two_ms * 1e3,
+            "two_words_product_us": product_ms * 1e3, "one_word_step_us": one_ms * 1e3,
+            "product_bytes": nbytes, "product_gbs": nbytes / (product_ms * 1e-3) / 1e9,
+            "plan": {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
+                     "waves": plan.waves, "kslices": plan.kslices}}
+
+
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "q8_0": 5000.0}   # MI355X dense, published
 
 
@@ -581,6 +637,10 @@ def main():
             r = measure_parts(inputs.PARTS_WORKLOADS[other], max(200, args.steps // 4),
                               max(20, args.warmup // 4), rotate=not args.no_rotate)
             fused[f"parts_m{inputs.PARTS_WORKLOADS[other].m}"] = r
+        for other in (name, "batch16_k4096_n14336"):
+            r = measure_two_words(inputs.WORKLOADS[other], max(200, args.steps // 4),
+                                  max(20, args.warmup // 4), rotate=not args.no_rotate)
+            fused[f"two_words_m{inputs.WORKLOADS[other].m}"] = r
 
     prefill = {}
     if not args.no_prefill:

@@ -154,13 +154,17 @@ int rows_for(int64_t m) {
 
 // The default launch (settled by measurement on MI355X, see the design notes):
 //  * VALU kernel (lane per column) while the rows are few enough that the
-//    vector ALU keeps up with HBM: bf16 up to 4 rows, int8 up to 8 rows;
-//    MFMA kernel above.
-//  * VALU: 8 waves per workgroup; K split across workgroups only when the
-//    column tiles alone leave CUs idle (splits = CUs / tiles, each split at
-//    least 8 blocks).
+//    vector ALU keeps up with HBM: bf16 up to 3 rows, int8 up to 4 rows;
+//    MFMA kernel above.  Measured on MI355X at K = 4096, N = 14336 (loop
+//    us, VALU best / MFMA): bf16 m=3 14.2 / 14.8, m=4 16.0 / 14.8; int8 m=4
+//    13.1 / 15.5, m=5 21.9 / 15.8.
+//  * VALU: 8 waves per workgroup for 1-2 rows, 16 for 3-4 rows (more waves
+//    hide the longer per-block work: int8 m=4 13.1 us with 16 waves, 18.3
+//    with 8); K split across workgroups only when the column tiles alone
+//    leave CUs idle (splits = CUs / tiles, each split at least 8 blocks).
 //  * MFMA (see below): 16 waves; the fewest K splits whose staged activation
-//    fits the LDS.
+//    fits the LDS, more (each at least 32 blocks) while the splits still fit
+//    one workgroup per CU.
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
@@ -170,8 +174,8 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   p.kslices = 1;
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS) {
     // The block-interleaved MFMA kernel, its 32 rows the two words' 16 each;
-    // K split for the LDS, then further while the splits still fill one
-    // workgroup per CU.
+    // K split for the LDS, then further (each split at least 32 blocks)
+    // while the splits still fill one workgroup per CU.
     p.kernel = Q8_KERNEL_MFMA;
     p.rows = 32;
     p.waves = 16;
@@ -180,26 +184,30 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
     while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
                                         (int)S) > budget)
       ++S;
-    while (S < NB && T * (S + 1) <= dev.cus) ++S;
+    while (S < NB / 32 && T * (S + 1) <= dev.cus) ++S;
     p.split_k = (int32_t)S;
     return p;
   }
-  const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 4 : 8;
+  const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 3 : 4;
   if (m <= valu_rows) {
     p.kernel = Q8_KERNEL_VALU;
     p.rows = rows_for(m);
-    p.waves = 8;
+    p.waves = p.rows >= 4 ? 16 : 8;
     int64_t S = dev.cus / T;
     if (S > smax) S = smax;
     if (S < 1) S = 1;
     p.split_k = (int32_t)S;
     return p;
   }
-  // Matrix cores.  bf16 activations: waves split K and each covers the whole
-  // tile, so one LDS fragment read serves four MFMAs.  int8 activations: each
-  // wave owns a 16-column group and the workgroup walks tiles with the
-  // activation staged once (measured faster for the int8 shapes).
-  p.kernel = act_fmt == Q8_ACT_BF16 ? Q8_KERNEL_MFMA : Q8_KERNEL_MFMA_COLS;
+  // Matrix cores.  Up to 16 rows, and for bf16 activations at any row
+  // count: waves split K and each covers the whole tile, so one LDS fragment
+  // read serves four MFMAs.  int8 activations of 17-32 rows: each wave owns a
+  // 16-column group and the workgroup walks tiles with the activation staged
+  // once.  Measured on MI355X: int8, m = 16, K = 4096, N = 14336: 16.2 us
+  // block-interleaved against 24-52 us column-group over its splits and
+  // widths; int8, m = 32, K = 5120, N = 32000: column-group, 2 splits,
+  // 50.6 us against 60.9 us.
+  p.kernel = (act_fmt == Q8_ACT_BF16 || m <= 16) ? Q8_KERNEL_MFMA : Q8_KERNEL_MFMA_COLS;
   p.rows = m <= 16 ? 16 : 32;
   p.waves = 16;
   p.kslices = 1;
@@ -208,6 +216,16 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
                                       (int)S) > budget - kStaticLdsReserve)
     ++S;
+  // Then more splits while they still fit one workgroup per CU, each split
+  // at least 32 blocks: a narrow product's few tiles alone leave CUs idle.
+  // Measured on MI355X: bf16, m = 4, K = 4096, N = 640: 1 split 12.2 us,
+  // 4 splits 8.9, 16 splits 11.1; m = 16, N = 4096: 1 split 13.6, 4 splits
+  // 10.2, 8 splits 15.0; int8, m = 32, K = 5120, N = 40: 2 splits 28.7,
+  // 5 splits 22.9, 20 splits 44.5.
+  const int64_t tiles_per_wg = p.kernel == Q8_KERNEL_MFMA_COLS ? p.waves / (4 * p.kslices) : 1;
+  const int64_t wgs = (T + tiles_per_wg - 1) / tiles_per_wg;
+  const int64_t smax_mfma = NB / 32 > 1 ? NB / 32 : 1;
+  while (S < smax_mfma && wgs * (S + 1) <= dev.cus) ++S;
   p.split_k = (int32_t)S;
   return p;
 }
@@ -422,14 +440,15 @@ q8_plan fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
 // (the VALU split count counts both weights' tiles); its two weights always
 // meet in the workspace, so the column-group kernel's quantizer needs no
 // K split.
-// With the VALU kernel, the pair's twice as many workgroups take 4 waves
-// each once they outnumber the CUs, which keeps the waves streaming at once
-// (and the bytes each wave streams) those of the single product (measured on
-// MI355X, m = 1, K = 4096, N = 14336: 4 waves 23.0 us, 8 waves 24.2 us).
+// With the VALU kernel, the pair's twice as many workgroups take half the
+// single product's waves each once they outnumber the CUs, which keeps the
+// waves streaming at once (and the bytes each wave streams) those of the
+// single product (measured on MI355X, m = 1, K = 4096, N = 14336: 4 waves
+// 23.0 us, 8 waves 24.2 us).
 q8_plan glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   q8_plan p = default_plan(m, K, 2 * round_up(N, Q8_TILE_COLS), act_fmt);
   const int64_t units = 2 * round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
-  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > device_facts().cus) p.waves = 4;
+  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > device_facts().cus) p.waves /= 2;
   return p;
 }
 
@@ -518,10 +537,11 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
 
 // The product's plan over the parts' columns side by side, on a kernel that
 // walks units of any part (VALU or block-interleaved MFMA); the VALU kernel
-// takes 4 waves a workgroup once the workgroups outnumber the CUs, as the
-// gated pair does.  The MFMA kernel splits K further while the splits still
+// takes half its waves once the workgroups outnumber the CUs, as the gated
+// pair does.  The MFMA kernel splits K further while the splits still
 // fit one workgroup per CU: the parts of one attention block are narrower
-// than the products the single-product plan was settled on (measured on
+// than the products the single-product plan was settled on; each split
+// keeps at least 32 blocks (measured on
 // MI355X, m = 16, K = 4096, N = 4096 + 1024 + 1024: one split 14.7 us, two
 // 12.1 us, three 16.0 us).
 q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
@@ -542,10 +562,10 @@ q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
   }
   if (p.kernel == Q8_KERNEL_MFMA) {
     int64_t S = p.split_k;
-    while (S < NB && units * (S + 1) <= dev.cus) ++S;
+    while (S < NB / 32 && units * (S + 1) <= dev.cus) ++S;
     p.split_k = (int32_t)S;
   }
-  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > dev.cus) p.waves = 4;
+  if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > dev.cus) p.waves /= 2;
   return p;
 }
 

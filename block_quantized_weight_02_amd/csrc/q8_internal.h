@@ -2,7 +2,7 @@
 // gfx950 kernels (q8_kernels.hip).  Not installed; the public ABI is
 // include/q8gemv.h.
 //
-// Packed weight layout (version 1), private to this library:
+// Packed weight layout (version 2), private to this library:
 //   N is padded to N_pad = 64*T columns; the weight is T column tiles of 64.
 //   K is NB = K/32 Q8_0 blocks.  Tile t, block b is one contiguous 2048-byte
 //   chunk at byte (t*NB + b)*2048, itself two 1024-byte halves h (k 0..15 and

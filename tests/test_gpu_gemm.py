@@ -150,3 +150,19 @@ def test_prefill_full_size(name):
     assert_close(y[:, cols], ref, bnd, name)
     assert (y[:, N:].view(np.uint32) == 0).all()
     assert np.isfinite(y).all()
+
+
+def test_gemm_most_rows():
+    """m = Q8_MAX_GEMM_ROWS (8192 rows, 64 row blocks of 128), both formats."""
+    m, K, N = q8.Q8_MAX_GEMM_ROWS, 256, 130
+    x, q, s = inputs.random_case(m, K, N, seed=5000)
+    Wq, Ws = g.pack(q, s)
+    y = gemm(xdev(x), Wq, Ws, m, K, N, BF16)
+    ref, bnd = oracle.gemv_bf16(x, q, s)
+    assert_close(y[:, :N], ref, bnd, "gemm bf16 m=8192")
+    assert (y[:, N:].view(np.uint32) == 0).all()
+    buf = g.quantize(x)
+    xq, dx = g.act_host(buf, m, K)
+    y = gemm(buf, Wq, Ws, m, K, N, Q8)
+    ref, bnd = oracle.gemv_q8(xq, dx, q, s)
+    assert_close(y[:, :N], ref, bnd, "gemm int8 m=8192")

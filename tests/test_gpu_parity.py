@@ -389,3 +389,42 @@ def test_row_split_halves():
     yref, bnd = oracle.gemv_bf16(x, q, s)
     err = np.abs(ysum - yref)
     assert np.all(err <= REL * bnd + 2 * ABS), np.max(err / (REL * bnd + 2 * ABS))
+
+
+# ------------------------------------------------------------------------------
+# maximum sizes
+# ------------------------------------------------------------------------------
+
+def test_long_k():
+    """K = 2^20 (32768 blocks, a 2 MiB activation row): the default plan and
+    explicit VALU and MFMA plans with many K splits, bf16 and int8."""
+    m, K, N = 3, 1 << 20, 70
+    x, q, s = inputs.random_case(m, K, N, seed=97)
+    Wq, Ws = g.pack(q, s)
+    ref, bnd = oracle.gemv_bf16(x, q, s)
+    for plan in (None, g.plan(q8.Q8_KERNEL_VALU, 4, 3, 8), g.plan(q8.Q8_KERNEL_MFMA, 16, 512, 16)):
+        y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16, plan)
+        assert_close(y[:, :N], ref, bnd, f"K=2^20 bf16 plan={plan}")
+        assert (y[:, N:].view(np.uint32) == 0).all()
+    buf = g.quantize(x)
+    xq, dx = g.act_host(buf, m, K)
+    rq, rd = oracle.quantize_act(x)
+    np.testing.assert_array_equal(xq, rq)
+    np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32))
+    ref, bnd = oracle.gemv_q8(xq, dx, q, s)
+    y = g.gemv(buf, Wq, Ws, m, K, N, Q8)
+    assert_close(y[:, :N], ref, bnd, "K=2^20 int8")
+
+
+def test_widest_n():
+    """N = 2^24 - 5, the widest the library takes (2^18 column tiles, the
+    last one ragged), one block of K."""
+    m, K, N = 1, 32, (1 << 24) - 5
+    x, q, s = inputs.random_case(m, K, N, seed=98)
+    Wq, Ws = g.pack(q, s)
+    y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16)
+    cols = _sample_cols(N, n=2048, seed=98)
+    ref, bnd = oracle.gemv_bf16(x, q, s, cols)
+    assert_close(y[:, cols], ref, bnd, "N=2^24-5")
+    assert (y[:, N:].view(np.uint32) == 0).all()
+    assert y.shape[1] == 1 << 24

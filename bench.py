@@ -81,12 +81,23 @@ def kernel_name(plan: dict, w) -> str:
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with its comments and blank lines removed (string
+    literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def csrc_hash() -> str:
+    """Hash of the library's sources, comments aside: the profiler counters
+    stay valid for a kernel whose code has not changed."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "block_quantized_weight_02_amd", "csrc")
     for name in sorted(os.listdir(d)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -883,13 +883,12 @@ namespace {
 int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *y,
              int32_t *dots, int64_t m, int64_t K, int64_t N, int act_fmt, hipStream_t stream) {
   int st;
-  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, N)) ||
-      (st = check_one_word_act(act_fmt, "q8_gemm")))
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, N)) || (st = check_act(act_fmt)))
     return st;
   if ((st = check_ptr(x, "x")) || (st = check_ptr(W_q8, "W_q8"))) return st;
   if (!dots && (st = check_ptr(W_q8_scale, "W_q8_scale"))) return st;
   if (dots ? (st = check_ptr(dots, "dots")) : (st = check_ptr(y, "y"))) return st;
-  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
@@ -904,7 +903,7 @@ int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *
   a.NB = (int)(K / Q8_BLOCK);
   a.Npad = (int)Npad;
   a.T = (int)(Npad / Q8_TILE_COLS);
-  a.act_scale_off = (unsigned)act_scales_offset(m, K);
+  a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
   (void)hipGetLastError();
   hipError_t e = q8::launch_gemm(act_fmt, dots != nullptr, q8::gemm_rows_per_block(m), a, stream);
   if (e != hipSuccess) {

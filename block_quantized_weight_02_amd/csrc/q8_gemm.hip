@@ -45,7 +45,10 @@ struct GemmShape {
   static constexpr int WN = 4 / WM;             // waves along N, one 64-column tile each
   static constexpr int BN = 64 * WN;
   static constexpr int kRowB = ACT == kActBf16 ? 64 : 32;   // activation bytes, one row x block
-  static constexpr int kA = kGemmCB * BM * kRowB;           // activation bytes per stage
+  // staged activation rows: the two-word form stages its BM rows' first
+  // words, then the same rows' second words
+  static constexpr int kRowsA = ACT == kActQ8x2 ? 2 * BM : BM;
+  static constexpr int kA = kGemmCB * kRowsA * kRowB;       // activation bytes per stage
   static constexpr int kDx = ACT == kActBf16 ? 0 : kGemmCB * BM * 4;   // int8 row scales
   static constexpr int kW = WN * kGemmCB * kChunkBytes;     // weight values per stage (global)
   // in LDS the bf16 form holds the values as bf16 (converted once, at staging)
@@ -115,19 +118,23 @@ __device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, i
   const int tid = (int)threadIdx.x;
   // activation pieces: consecutive threads take the parts of consecutive
   // rows of one block (so a store's 16 lanes write 4 rows: distinct banks)
+  constexpr int RA = S::kRowsA;
 #pragma unroll
   for (int k = 0; k < P::kNA; ++k) {
     const int p = k * kGemmThreads + tid;
-    const int q = p % kPPB, r = (p / kPPB) % BM, cb = p / (kPPB * BM);
-    const int rc = min(row0 + r, m - 1) - row0;
+    const int q = p % kPPB, r = (p / kPPB) % RA, cb = p / (kPPB * RA);
+    // staged row r: row row0 + r, or (two words, r >= BM) the second words
+    // of row row0 + r - BM, m rows further on
+    const int rr = r < BM ? r : r - BM;
+    const int rc = min(row0 + rr, m - 1) - row0 + (r < BM ? 0 : m);
     pl.asrc[k] = (unsigned)rc * (unsigned)K * kElt + cb * kBlock * kElt + q * 16;
     pl.acb[k] = cb;
     if constexpr (ACT == kActBf16) {
-      pl.adst[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, q);
+      pl.adst[k] = (cb * RA + r) * S::kRowB + a_part<ACT>(r, q);
       pl.adst2[k] = 0;
     } else {
-      pl.adst[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, 2 * q);
-      pl.adst2[k] = (cb * BM + r) * S::kRowB + a_part<ACT>(r, 2 * q + 1);
+      pl.adst[k] = (cb * RA + r) * S::kRowB + a_part<ACT>(r, 2 * q);
+      pl.adst2[k] = (cb * RA + r) * S::kRowB + a_part<ACT>(r, 2 * q + 1);
     }
   }
 #pragma unroll
@@ -149,7 +156,7 @@ __device__ __forceinline__ void gemm_plan(GemmPlan<ACT, BM> &pl, int m, int K, i
     pl.scb = cb;
     pl.sdst = S::kA + S::kDx + S::kWL + (wn * kGemmCB + cb) * kTile * 4 + q * 16;
   }
-  if constexpr (ACT == kActQ8) {
+  if constexpr (ACT != kActBf16) {
 #pragma unroll
     for (int k = 0; k < S::kDxPer; ++k) {
       const int p = min(k * kGemmThreads + tid, kGemmCB * BM - 1);
@@ -187,7 +194,7 @@ __device__ __forceinline__ void gemm_load(GemmStaging<ACT, BM> &st, const GemmPl
     for (int k = 0; k < P::kNW; ++k) st.vw[k] = *reinterpret_cast<const u32x4_t *>(wbase + pl.wsrc[k]);
     if (!DOTS && (int)threadIdx.x < P::kNS)
       st.vs = *reinterpret_cast<const u32x4_t *>(sbase + pl.ssrc);
-    if constexpr (ACT == kActQ8 && !DOTS) {
+    if constexpr (ACT != kActBf16 && !DOTS) {
 #pragma unroll
       for (int k = 0; k < GemmShape<ACT, BM>::kDxPer; ++k) st.dx[k] = dxbase[pl.dxsrc[k]];
     }
@@ -207,7 +214,7 @@ __device__ __forceinline__ void gemm_load(GemmStaging<ACT, BM> &st, const GemmPl
       const unsigned back = (unsigned)max(pl.scb - nvalid + 1, 0);
       st.vs = *reinterpret_cast<const u32x4_t *>(sbase + pl.ssrc - back * (kTile * 4));
     }
-    if constexpr (ACT == kActQ8 && !DOTS) {
+    if constexpr (ACT != kActBf16 && !DOTS) {
 #pragma unroll
       for (int k = 0; k < GemmShape<ACT, BM>::kDxPer; ++k)
         st.dx[k] = dxbase[pl.dxsrc[k] - (unsigned)max(pl.dxcb[k] - nvalid + 1, 0)];
@@ -223,7 +230,7 @@ __device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st,
   using P = GemmPlan<ACT, BM>;
 #pragma unroll
   for (int k = 0; k < P::kNA; ++k) {
-    if constexpr (ACT == kActQ8) {
+    if constexpr (ACT != kActBf16) {
       *reinterpret_cast<u32x2_t *>(buf + pl.adst[k]) = u32x2_t{st.va[k].x, st.va[k].y};
       *reinterpret_cast<u32x2_t *>(buf + pl.adst2[k]) = u32x2_t{st.va[k].z, st.va[k].w};
     } else {
@@ -248,7 +255,7 @@ __device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st,
     }
   }
   if (!DOTS && (int)threadIdx.x < P::kNS) *reinterpret_cast<u32x4_t *>(buf + pl.sdst) = st.vs;
-  if constexpr (ACT == kActQ8 && !DOTS) {
+  if constexpr (ACT != kActBf16 && !DOTS) {
     float *dxs = reinterpret_cast<float *>(buf + S::kA);
 #pragma unroll
     for (int k = 0; k < S::kDxPer; ++k) {
@@ -312,7 +319,7 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     for (int cb = 0; cb < kGemmCB; ++cb) {
       const int b = b0 + cb;
       if (b >= NB) break;
-      const char *As = buf + cb * BM * S::kRowB;
+      const char *As = buf + cb * S::kRowsA * S::kRowB;
       const char *Ws = buf + S::kA + S::kDx + (wn * kGemmCB + cb) * kChunkBytes * S::kWElt;
       float4 sc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if constexpr (!DOTS)
@@ -338,6 +345,35 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
           for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[rt][g][e] = fmaf(scs[g], d[g][e], acc[rt][g][e]);
+        }
+      } else if constexpr (ACT == kActQ8x2) {
+        // Two words: the first words' and the second words' int8 MFMAs meet
+        // exactly in int32 (|128 D_hi + D_lo| < 2^27), then one FMA with the
+        // block's dx * s / 128.
+        uint2 bw[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bw[g] = *reinterpret_cast<const uint2 *>(Ws + w_lane + g * 256);
+        const float *dxs = reinterpret_cast<const float *>(buf + S::kA) + cb * BM;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const long ahi = *reinterpret_cast<const long *>(
+              As + (wm * 64 + rt * 16 + li) * S::kRowB + a_lane);
+          const long alo = *reinterpret_cast<const long *>(
+              As + (BM + wm * 64 + rt * 16 + li) * S::kRowB + a_lane);
+          const float4 d4 = *reinterpret_cast<const float4 *>(dxs + wm * 64 + rt * 16 + lj * 4);
+          const float dxv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const long b8 = __builtin_bit_cast(long, bw[g]);
+            const i32x4_t dh =
+                __builtin_amdgcn_mfma_i32_16x16x32_i8(ahi, b8, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+            const i32x4_t dl =
+                __builtin_amdgcn_mfma_i32_16x16x32_i8(alo, b8, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[rt][g][e] = fmaf(dxv[e] * scs[g], (float)(dh[e] * 128 + dl[e]) * 0.0078125f,
+                                   acc[rt][g][e]);
+          }
         }
       } else {
         uint2 bw[4];
@@ -458,6 +494,10 @@ hipError_t launch_gemm(int act, bool write_dots, int bm, const GemmArgs &a, hipS
     if (bm == 128)
       return write_dots ? launch_gemm_k<kActQ8, 128, true>(a, stream)
                         : launch_gemm_k<kActQ8, 128, false>(a, stream);
+  }
+  if (act == kActQ8x2 && !write_dots) {
+    if (bm == 64) return launch_gemm_k<kActQ8x2, 64, false>(a, stream);
+    if (bm == 128) return launch_gemm_k<kActQ8x2, 128, false>(a, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -160,8 +160,8 @@ int q8_quantize_act_two_words(const uint16_t *x_bf16, void *x_q8x2, int64_t m,
  * N >= 1.  Two-word activations run each block's two int8 passes on the
  * matrix cores and join them exactly in int32 before the block's scale
  * (128 * D_hi + D_lo, then times dx * s / 128); only the MFMA kernel takes
- * them (plans naming another kernel are Q8_ERR_PLAN), and the gated pair,
- * the parts and q8_gemm do not (Q8_ERR_ACT_FMT).  When the chosen plan splits K across
+ * them (plans naming another kernel are Q8_ERR_PLAN), and the gated pair
+ * and the parts do not (Q8_ERR_ACT_FMT).  When the chosen plan splits K across
  * workgroups it uses a workspace the library allocates on first need and
  * keeps per (device, stream) until q8_release_workspaces(); that first call
  * allocates, so it must not be inside a graph capture.  Calls on one stream
@@ -379,7 +379,11 @@ size_t q8_parts_workspace_bytes(const q8_plan *plan, const q8_part *parts,
  * columns 0).  The pages' CUDA planner runs the product as a tensor-core GEMM
  * above its GEMV's rows (codegen_cuda/lane/plan.rs, Launch::on_tensor_cores,
  * gemm_blk_rows); this is its matrix-core form on gfx950.  No workspace; the
- * call allocates nothing.  Requires K > 0, K % 32 == 0, N >= 1.
+ * call allocates nothing.  Requires K > 0, K % 32 == 0, N >= 1.  Two-word
+ * activations (act_fmt 2, the pages' two-pass numerics, whose GEMM plan.rs
+ * runs with fewer rows per block): each block's first and second words run
+ * as two int8 matrix-core passes joined exactly in int32 before the scale,
+ * as in q8_gemv.
  */
 int q8_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale,
             float *y, int64_t m, int64_t K, int64_t N, int act_fmt,

@@ -249,7 +249,7 @@ def test_two_word_rules():
     expect(1, q8.q8_quantize_act_two_words, A, A, 1, 48, S0)
     expect(3, q8.q8_quantize_act_two_words, None, A, 1, 64, S0)
     expect(4, q8.q8_quantize_act_two_words, A, A + 2, 1, 64, S0)
-    # at most 16 rows; only the MFMA kernel; not the pair, the parts or the GEMM
+    # GEMV: at most 16 rows, only the MFMA kernel; not the pair or the parts
     expect(1, q8.q8_gemv, A, A, A, A, 17, 64, 8, TW, S0)
     expect(1, q8.q8_gemv_default_plan, 17, 64, 8, TW)
     assert q8.q8_gemv_workspace_bytes(17, 64, 8, TW) == 0
@@ -265,4 +265,4 @@ def test_two_word_rules():
     expect(2, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, TW, None, S0)
     expect(2, q8.q8_gemv_glu_default_plan, 1, 64, 8, TW)
     expect(2, q8.q8_gemv_parts, A, [q8.make_part(A, A, A, 64)], 1, 64, TW, S0)
-    expect(2, q8.q8_gemm, A, A, A, A, 64, 64, 8, TW, S0)
+    expect(3, q8.q8_gemm, None, A, A, A, 64, 64, 8, TW, S0)   # the GEMM takes it

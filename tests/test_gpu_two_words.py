@@ -179,3 +179,57 @@ def test_full_size_two_words(name):
     err = np.abs(y[:, cols].astype(np.float64) - z)
     lim = REL * bnd + ABS
     assert np.all(err <= lim), f"{name}: max err/lim {np.max(err / lim):.3g}"
+
+
+# ------------------------------------------------------------------------------
+# the many-row product (q8_gemm) over two-word activations
+# ------------------------------------------------------------------------------
+
+def gemm2(buf, Wq, Ws, m, K, N):
+    y = torch.full((m, q8.q8_padded_cols(N)), float("nan"), dtype=torch.float32, device=g.DEV)
+    q8.q8_gemm(buf, Wq, Ws, y, m, K, N, TW)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+GEMM_SHAPES = [(m, K, N) for m in (1, 17, 64, 65, 200) for (K, N) in ((32, 1), (1056, 200), (2176, 257))]
+
+
+@pytest.mark.parametrize("m,K,N", GEMM_SHAPES)
+def test_gemm_two_words(m, K, N):
+    x, q, s = inputs.random_case(m, K, N, seed=860 + m + K + N)
+    buf = quantize2(x)
+    Wq, Ws = g.pack(q, s)
+    y = gemm2(buf, Wq, Ws, m, K, N)
+    z, bnd = oracle.gemv_q8_two_words(*words_host(buf, m, K), q, s)
+    check(y, z, bnd, N, f"gemm two words m={m} K={K} N={N}")
+
+
+def test_gemm_two_words_most_rows_and_exact():
+    m, K, N = q8.Q8_MAX_GEMM_ROWS, 256, 130
+    x, q, s = inputs.random_case(m, K, N, seed=870)
+    buf = quantize2(x)
+    Wq, Ws = g.pack(q, s)
+    y = gemm2(buf, Wq, Ws, m, K, N)
+    z, bnd = oracle.gemv_q8_two_words(*words_host(buf, m, K), q, s)
+    check(y, z, bnd, N, "gemm two words m=8192")
+    x, q, s, _, _ = inputs.exact_case(70, 512, 100, seed=38)
+    buf = quantize2(x)
+    Wq, Ws = g.pack(q, s)
+    y = gemm2(buf, Wq, Ws, 70, 512, 100)
+    z, _ = oracle.gemv_q8_two_words(*words_host(buf, 70, 512), q, s)
+    np.testing.assert_array_equal(y[:, :100].astype(np.float64), z)
+
+
+def test_gemm_two_words_prefill_full_size():
+    w = inputs.WORKLOADS["prefill_q8act_m512_k4096_n14336"]
+    x, q, s = inputs.generate(w)
+    m, K, N = w.m, w.K, w.N
+    buf = quantize2(x)
+    Wq, Ws = g.pack(q, s)
+    y = gemm2(buf, Wq, Ws, m, K, N)
+    blocks = np.random.default_rng(w.seed_x + 19).choice(N // 32, size=16, replace=False)
+    cols = np.sort((blocks[:, None] * 32 + np.arange(32)[None, :]).ravel())
+    z, bnd = oracle.gemv_q8_two_words(*words_host(buf, m, K), q, s, cols)
+    err = np.abs(y[:, cols].astype(np.float64) - z)
+    assert np.all(err <= REL * bnd + ABS), np.max(err / (REL * bnd + ABS))

@@ -29,7 +29,8 @@ beside the same products one by one, at m = 1 and m = 16, and the two-word
 int8 activation (quantize then product) beside the one-word step, at m = 1
 and m = 16; `context` gives
 the headline with one weight copy reused and a 1 GiB device copy's rate;
-`prefill` times the many-row product (m = 512) against the MFMA peak.
+`prefill` times the many-row product (m = 512) against the MFMA peak, with
+bf16, one-word and two-word int8 activations.
 """
 import argparse
 import hashlib
@@ -465,16 +466,25 @@ def measure_two_words(w, steps, warmup, rotate=True):
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "q8_0": 5000.0}   # MI355X dense, published
 
 
-def measure_gemm(w, steps, warmup, rotate=True):
+def measure_gemm(w, steps, warmup, rotate=True, two_words=False):
     """The many-row product (prefill chunk): q8_gemm per step; with Q8_0
-    activations the step also quantizes them (reported apart too)."""
+    activations (one or two words) the step also quantizes them (reported
+    apart too).  TFLOP/s count the product's 2*m*K*N; the two-word form runs
+    twice that on the matrix cores."""
     import torch
     st = Setup(w, rotate=rotate)
     q8 = st.q8
     m, K, N = w.m, w.K, w.N
     act = q8.Q8_ACT_BF16 if w.act == "bf16" else q8.Q8_ACT_Q8_0
-    gemm = q8.lib().q8_gemm
+    quant, quant_args = st._quant, st._quant_args
     xin = st.x.data_ptr() if w.act == "bf16" else st.xq.data_ptr()
+    if two_words:
+        act = q8.Q8_ACT_Q8_0_TWO_WORDS
+        x2 = torch.empty(q8.q8_act_two_words_bytes(m, K), dtype=torch.uint8, device="cuda:0")
+        xin = x2.data_ptr()
+        quant = q8.lib().q8_quantize_act_two_words
+        quant_args = (st.x.data_ptr(), xin, m, K, st.stream.cuda_stream)
+    gemm = q8.lib().q8_gemm
     sp = st.stream.cuda_stream
     args = [(xin, Wq.data_ptr(), Ws.data_ptr(), st.y.data_ptr(), m, K, N, act, sp)
             for (Wq, Ws) in st.W]
@@ -486,7 +496,7 @@ def measure_gemm(w, steps, warmup, rotate=True):
 
     def step(i):
         if w.act != "bf16":
-            rc = st._quant(*st._quant_args)
+            rc = quant(*quant_args)
             if rc:
                 raise RuntimeError(q8.q8_last_error())
         product(i)
@@ -501,9 +511,11 @@ def measure_gemm(w, steps, warmup, rotate=True):
     del st
     torch.cuda.empty_cache()
     tf = flops / (gemm_ms * 1e-3) / 1e12
-    log(f"[bench] gemm {w.name}: {gemm_ms * 1e3:.2f} us/launch ({tf:.0f} TFLOP/s, "
+    form = " two words" if two_words else ""
+    log(f"[bench] gemm {w.name}{form}: {gemm_ms * 1e3:.2f} us/launch ({tf:.0f} TFLOP/s, "
         f"{100 * tf / peak:.1f}% of {peak:.0f}), step {step_ms * 1e3:.2f} us")
-    return {"workload": w.name, "m": m, "K": K, "N": N, "act": w.act,
+    return {"workload": w.name, "m": m, "K": K, "N": N,
+            "act": w.act + ("_two_words" if two_words else ""),
             "us_per_step": step_ms * 1e3, "kernel_us_mean": gemm_ms * 1e3,
             "tflops": tf, "peak_tflops": peak, "frac_of_mfma_peak": tf / peak,
             "gbs_algorithmic": b["total"] / (gemm_ms * 1e-3) / 1e9}
@@ -659,6 +671,9 @@ def main():
             prefill[inputs.WORKLOADS[other].act] = measure_gemm(
                 inputs.WORKLOADS[other], max(100, args.steps // 10), max(10, args.warmup // 10),
                 rotate=not args.no_rotate)
+        prefill["q8_0_two_words"] = measure_gemm(
+            inputs.WORKLOADS["prefill_q8act_m512_k4096_n14336"], max(100, args.steps // 10),
+            max(10, args.warmup // 10), rotate=not args.no_rotate, two_words=True)
 
     context = None
     if not args.no_rows:

@@ -4,7 +4,8 @@
 
 hipcc cross-compiles; no GPU is needed to build.  Packed-FP32 instructions are
 disabled for every device compile (-Xclang -target-feature -Xclang
--packed-fp32-ops).
+-packed-fp32-ops), and fp32 division is correctly rounded (the quantizers
+rely on it).
 """
 import os
 import subprocess
@@ -50,6 +51,7 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
              "-Wall", "-Wno-unused-command-line-argument",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fhip-fp32-correctly-rounded-divide-sqrt",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC, *extra]
     with tempfile.TemporaryDirectory(prefix="q8build") as d:
         objs = [os.path.join(d, os.path.splitext(s)[0] + ".o") for s in SOURCES]

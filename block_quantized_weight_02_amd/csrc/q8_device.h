@@ -74,12 +74,18 @@ __device__ __forceinline__ int scale_pos(int c) { return ((c & 15) << 2) | (c >>
 
 
 // The quantizer of an activation block (also the product's output
-// quantizer): scale from the block's amax, then one code per value.
-__device__ __forceinline__ float q8_scale_of(float amax) { return (float)((double)amax / 127.0); }
+// quantizer): scale from the block's amax, then one code per value.  Both
+// divisions are fp32 divisions rounded correctly (the library is built with
+// -fhip-fp32-correctly-rounded-divide-sqrt): the same value as an fp64
+// quotient of the fp32 operands rounded once to fp32, since 53 >= 2 * 24 + 2
+// bits make that double rounding innocuous.
+__device__ __forceinline__ float q8_quot(float a, float b) { return a / b; }
+
+__device__ __forceinline__ float q8_scale_of(float amax) { return q8_quot(amax, 127.0f); }
 
 __device__ __forceinline__ int8_t q8_code_of(float v, float d) {
   if (d == 0.0f) return 0;
-  const float rq = roundf((float)((double)v / (double)d));   // ties away from zero
+  const float rq = roundf(q8_quot(v, d));   // ties away from zero
   return (int8_t)(int)fminf(fmaxf(rq, -127.0f), 127.0f);
 }
 

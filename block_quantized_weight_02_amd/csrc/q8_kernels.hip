@@ -110,7 +110,8 @@ quantize_act_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ xq,
 }
 
 // The two-word form: the first word and the scale as above, the second word
-// round_half_away(128 * (quot - hi)) of the fp32 quotient quot = v / d.
+// round_half_away(128 * (quot - hi)) of the correctly rounded fp32 quotient
+// quot = v / d.
 // quot - hi is exact in fp32 (hi is quot rounded, within a factor of two of
 // it or zero) and the scaling by 128 is exact, so the second word is unique.
 __global__ void __launch_bounds__(256)
@@ -127,7 +128,7 @@ quantize_act_two_words_kernel(const uint16_t *__restrict__ x, int8_t *__restrict
   if (valid) {
     int h = 0, l = 0;
     if (d != 0.0f) {
-      const float quot = (float)((double)v / (double)d);
+      const float quot = q8_quot(v, d);
       const float rh = fminf(fmaxf(roundf(quot), -127.0f), 127.0f);
       h = (int)rh;
       l = (int)roundf((quot - rh) * 128.0f);

@@ -614,8 +614,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the product shards by columns across GPUs with no collective; see the design notes)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the product shards by columns across GPUs with no collective)",
               file=sys.stderr)
         sys.exit(2)
 

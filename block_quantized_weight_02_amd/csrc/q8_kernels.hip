@@ -361,7 +361,7 @@ __device__ __forceinline__ void valu_load(ValuStage<MR, ACT, DOTS> &st, const Va
       st.wa[u] = ld_stream16(c);
       st.wb[u] = ld_stream16(c + kHalfBytes);
       if constexpr (!DOTS)
-        st.sc[u] = ld_stream4f(reinterpret_cast<const float *>(
+        st.sc[u] = ld_scale4f(reinterpret_cast<const float *>(
             reinterpret_cast<const char *>(src.sp) + (size_t)b * (kTile * 4) + src.ls));
     }
     if constexpr (ValuX<MR, ACT>::kPrefetch) {
@@ -583,7 +583,7 @@ __device__ __forceinline__ void cols_load(ColsStage &st, const int8_t *wcol, con
   for (int u = 0; u < kColsUnroll; ++u) {
     const int b = min(b0 + u * KW, b_hi - 1);
     st.w[u] = ld_stream8(wcol + (size_t)b * kChunkBytes);
-    if constexpr (!DOTS) st.sc[u] = ld_stream4f(scol + (size_t)b * kTile);
+    if constexpr (!DOTS) st.sc[u] = ld_scale4f(scol + (size_t)b * kTile);
   }
 }
 
@@ -1040,7 +1040,7 @@ __device__ __forceinline__ void mfma_load(MfmaStage &st, const int8_t *wlane,
     const int8_t *c = wlane + (size_t)b * kChunkBytes;
 #pragma unroll
     for (int g = 0; g < 4; ++g) st.w[u][g] = ld_stream8(c + g * 256);
-    if constexpr (!DOTS) st.sc[u] = ld_stream16f(slane + (size_t)b * (kTile / 4));
+    if constexpr (!DOTS) st.sc[u] = ld_scale16f(slane + (size_t)b * (kTile / 4));
   }
 }
 

@@ -267,7 +267,9 @@ constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4 * 4;
 size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N, int nw = 1) {
   if (p.split_k * nw <= 1) return 0;
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
-  return kCounterBytes + (size_t)round_up((int64_t)nw * p.split_k * m * Npad * 4, 256);
+  // the column-group kernel keeps whole 16-column records of its tile rows
+  const int64_t rows = p.kernel == Q8_KERNEL_MFMA_COLS ? p.rows : m;
+  return kCounterBytes + (size_t)round_up((int64_t)nw * p.split_k * rows * Npad * 4, 256);
 }
 
 // ---- library-owned workspaces, per (device, stream) ---------------------------

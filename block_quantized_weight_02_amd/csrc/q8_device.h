@@ -59,6 +59,22 @@ __device__ __forceinline__ float buf_ld4f(buf_t r, unsigned voff, unsigned soff)
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 
+// 16-byte stores and loads with the cache-policy bits of a system-scope
+// relaxed atomic (sc0 sc1): written through to memory and read from it, past
+// the per-XCD L2s, so a workgroup on another XCD sees them once the writer's
+// stores have completed.
+constexpr int kBufSys = 17;
+__device__ __forceinline__ void buf_st16_sys(buf_t r, unsigned voff, float4 v) {
+  const u32x4_t d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                     __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, kBufSys);
+}
+__device__ __forceinline__ float4 buf_ld16_sys(buf_t r, unsigned voff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kBufSys);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
 // The four signed bytes of a dword as fp32 (exact); byte j is k = 4d + j.
 __device__ __forceinline__ void i8x4_to_f32(uint32_t v, float *f) {
   f[0] = (float)(int8_t)(v);

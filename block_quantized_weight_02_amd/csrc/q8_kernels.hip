@@ -701,32 +701,43 @@ __device__ __forceinline__ void epi_final_groups(const Epi &ep, int Npad, int m,
       }
 }
 
-// Sums over the S splits (in split order) of weight wsel's partial carries
-// for v[0][e][h]'s places (rows row0 + 4j + e, columns col0 + 16h + i); the
-// loads of one split are issued together.
-template <int H>
-__device__ __forceinline__ void cols_sum_partials(const float *__restrict__ partial, int m,
-                                                  int Npad, int S, int wsel, int row0,
-                                                  size_t col0, int lane, float (&v)[1][4][H]) {
-  const int li = lane & 15, lj = lane >> 4;
-  const float *p = partial + ((size_t)wsel * S * m + row0 + lj * 4) * Npad + col0 + li;
+// The column-group kernel's partial carries: one record per (split, unit,
+// 16-column group) of MR * 16 floats, lane-major: lane l's carries of row
+// group rg (rows 16rg + 4j + e, e = 0..3; column 16g + i) are the four floats
+// at rg * 256 + 4l, so a wave writes and reads whole 1 KiB runs.
+// T: the launch's units.
+template <int MR>
+__device__ __forceinline__ buf_t cols_record(float *partial, int T, int s, int tv, int g) {
+  const size_t rec = ((size_t)s * T + tv) * 4 + g;
+  return make_buf(partial + rec * (16 * MR), 16 * MR * 4);
+}
+
+// Sums over the S splits (in split order) of unit tv's partial carries for
+// v[0][e][h]'s places (row group rg: rows 16rg + 4j + e; column group g0 + h);
+// the loads of one split are issued together.
+template <int MR, int H>
+__device__ __forceinline__ void cols_sum_partials(float *partial, int T, int S, int tv, int g0,
+                                                  int rg, int lane, float (&v)[1][4][H]) {
+  const unsigned off = (unsigned)(rg * 256 + lane * 4) * 4u;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int h = 0; h < H; ++h)
-      v[0][e][h] = (row0 + lj * 4 + e < m)
-                       ? __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_SYSTEM)
-                       : 0.0f;
+  for (int h = 0; h < H; ++h) {
+    const float4 a = buf_ld16_sys(cols_record<MR>(partial, T, 0, tv, g0 + h), off);
+    v[0][0][h] = a.x;
+    v[0][1][h] = a.y;
+    v[0][2][h] = a.z;
+    v[0][3][h] = a.w;
+  }
   for (int ss = 1; ss < S; ++ss) {
-    p += (size_t)m * Npad;
+    float4 a[H];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int h = 0; h < H; ++h) a[h] = buf_ld16_sys(cols_record<MR>(partial, T, ss, tv, g0 + h), off);
 #pragma unroll
-      for (int h = 0; h < H; ++h)
-        if (row0 + lj * 4 + e < m)
-          v[0][e][h] += __hip_atomic_load(p + (size_t)e * Npad + 16 * h, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_SYSTEM);
+    for (int h = 0; h < H; ++h) {
+      v[0][0][h] += a[h].x;
+      v[0][1][h] += a[h].y;
+      v[0][2][h] += a[h].z;
+      v[0][3][h] += a[h].w;
+    }
   }
 }
 
@@ -735,10 +746,12 @@ __device__ __forceinline__ void cols_sum_partials(const float *__restrict__ part
 // this path below the main loop's): sums of the partials, the epilogue, y,
 // and with QUANT the quantized output (H == 2: a row's 32 values are two per
 // lane across 16 lanes).
+// tv0: the unit of the (first) weight; g0: the first column group, at
+// column col0 of y.
 template <int RG, int H, bool QUANT, bool PAIR>
-__device__ __forceinline__ void cols_finish(const Epi &ep, float *__restrict__ y,
-                                            const float *__restrict__ partial, int m, int Npad,
-                                            int S, size_t col0, int lane) {
+__device__ __forceinline__ void cols_finish(const Epi &ep, float *__restrict__ y, float *partial,
+                                            int m, int Npad, int T, int S, int tv0, int g0,
+                                            size_t col0, int lane) {
   const int li = lane & 15, lj = lane >> 4;
   // The row stride as an opaque value, so the addresses below are formed
   // here and not hoisted into registers held across the caller's main loop.
@@ -748,9 +761,9 @@ __device__ __forceinline__ void cols_finish(const Epi &ep, float *__restrict__ y
     const int row0 = rg * 16;
     if (row0 >= m) break;
     float v[1][4][H], vu[1][4][H];
-    cols_sum_partials<H>(partial, m, Npad, S, 0, row0, col0, lane, v);
+    cols_sum_partials<RG * 16, H>(partial, T, S, tv0, g0, rg, lane, v);
     if constexpr (PAIR) {
-      cols_sum_partials<H>(partial, m, Npad, S, 1, row0, col0, lane, vu);
+      cols_sum_partials<RG * 16, H>(partial, T, S, tv0 + 1, g0, rg, lane, vu);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -963,15 +976,13 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
       cols_store_group<RG>(ep, y, Npad, m, col - li, lane, v);
       continue;
     }
+    {
+      const buf_t rec = cols_record<MR>(partial, T, s, tv, g);
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rg * 16 + lj * 4 + e;
-        if (r < m)
-          __hip_atomic_store(&partial[(((size_t)wsel * S + s) * m + r) * Npad + col], acc[rg][e],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
+      for (int rg = 0; rg < RG; ++rg)
+        buf_st16_sys(rec, (unsigned)(rg * 256 + lane * 4) * 4u,
+                     make_float4(acc[rg][0], acc[rg][1], acc[rg][2], acc[rg][3]));
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -985,30 +996,23 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
       prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     prev = __builtin_amdgcn_readfirstlane(prev);
     if (prev != last) continue;
+    const int tv0 = pair ? (tv & ~1) : tv;   // the unit of the pair's first weight
     if constexpr (QO) {
-      cols_finish<RG, 2, true, PAIR>(ep, y, partial, m, Npad, S, (size_t)t * kTile + 16 * (g & 2),
-                                     lane);
+      cols_finish<RG, 2, true, PAIR>(ep, y, partial, m, Npad, T, S, tv0, g & 2,
+                                     (size_t)t * kTile + 16 * (g & 2), lane);
     } else if constexpr (PAIR) {
-      cols_finish<RG, 1, false, true>(ep, y, partial, m, Npad, S, col - li, lane);
+      cols_finish<RG, 1, false, true>(ep, y, partial, m, Npad, T, S, tv0, g, col - li, lane);
     } else {
       // one weight, no quantizer: the split sums in place (this form keeps
       // the main loop's register allocation of the plain build)
       float v[RG][4][1];
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg)
+      for (int rg = 0; rg < RG; ++rg) {
+        float w[1][4][1];
+        cols_sum_partials<MR, 1>(partial, T, S, tv, g, rg, lane, w);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rg * 16 + lj * 4 + e;
-          float a = 0.0f;
-          if (r < m) {
-            a = __hip_atomic_load(&partial[(size_t)r * Npad + col], __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_SYSTEM);
-            for (int ss = 1; ss < S; ++ss)
-              a += __hip_atomic_load(&partial[((size_t)ss * m + r) * Npad + col],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          }
-          v[rg][e][0] = a;
-        }
+        for (int e = 0; e < 4; ++e) v[rg][e][0] = w[0][e][0];
+      }
       cols_store_group<RG>(ep, y, Npad, m, col - li, lane, v);
     }
     if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -301,6 +301,64 @@ __device__ __forceinline__ void finish_tile(const float *red, const TileOut &o,
     __hip_atomic_store(&counters[o.cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// The gated pair's epilogue when one workgroup holds both weights of its
+// tile (the block-interleaved MFMA kernel): red[w][r][c] holds the gate's
+// carries in waves 0 .. W/2-1 and the up weight's in waves W/2 .. W-1
+// (written, __syncthreads() done by the caller).  Each weight's waves are
+// summed in order; with one split the gate is applied here, otherwise both
+// weights' partials are published and the last of the tile's S arrivals sums
+// each weight's S partials in split order (the protocol of finish_tile).
+template <int MR, int W>
+__device__ __forceinline__ void finish_pair_tile(const float *red, const TileOut &o,
+                                                 float *__restrict__ partial,
+                                                 unsigned *__restrict__ counters, int m, int s,
+                                                 int S, const Epi &ep) {
+  constexpr int WH = W / 2;
+  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
+    const int r = idx >> 6, c = idx & 63;
+    if (r < m) {
+      float vg = red[idx], vu = red[WH * MR * 64 + idx];
+#pragma unroll
+      for (int w = 1; w < WH; ++w) {
+        vg += red[w * MR * 64 + idx];
+        vu += red[(WH + w) * MR * 64 + idx];
+      }
+      if (S == 1) {
+        store_final(ep, o.y, o.Npad, r, o.col0 + c,
+                    final_value<true>(ep, o.Npad, r, o.col0 + c, vg, vu));
+      } else {
+        __hip_atomic_store(&partial[((size_t)s * m + r) * o.pstride + o.pcol0 + c], vg,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&partial[(((size_t)S + s) * m + r) * o.pstride + o.pcol0 + c], vu,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+  if (S == 1) return;
+  __shared__ int is_last_pair;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last_pair = (__hip_atomic_fetch_add(&counters[o.cidx], 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM) == (unsigned)(S - 1))
+                       ? 1 : 0;
+  __syncthreads();
+  if (!is_last_pair) return;
+  for (int idx = threadIdx.x; idx < MR * 64; idx += 64 * W) {
+    const int r = idx >> 6, c = idx & 63;
+    if (r < m) {
+      const float vg = sum_partials(partial, m, o.pstride, S, 0, r, o.pcol0 + c);
+      const float vu = sum_partials(partial, m, o.pstride, S, 1, r, o.pcol0 + c);
+      store_final(ep, o.y, o.Npad, r, o.col0 + c,
+                  final_value<true>(ep, o.Npad, r, o.col0 + c, vg, vu));
+    }
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&counters[o.cidx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // ---------------------------------------------------------------------------
 // the product, VALU form: lane = column, activation in scalar registers
 // ---------------------------------------------------------------------------
@@ -1071,12 +1129,19 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
   const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
 
-  // Units tv = (tile, weight), T of them: a gated pair's two weights are
-  // adjacent units.
+  // Units tv, T of them: the product's tiles, the parts' tiles side by side,
+  // or the gated pair's output tiles, whose two weights the workgroup's two
+  // halves of waves stream together (waves 0 .. W/2-1 the gate, the rest the
+  // up weight), so the pair meets in LDS.  WH waves split each weight's
+  // blocks.
   constexpr bool pair = PAIR;
-  constexpr int step = W * kMfmaUnroll;
+  constexpr int WH = PAIR ? W / 2 : W;
+  const int wsel_w = PAIR ? wave / WH : 0;   // the weight this wave streams
+  const int wave_in = PAIR ? wave - wsel_w * WH : wave;
+  constexpr int step = WH * kMfmaUnroll;
   MfmaStage A, B;
-  // unit tv's weight and scales, and its tile within its product
+  // unit tv's weight and scales (for this wave), and its tile within its
+  // product
   auto unit_src = [&](int tv, const int8_t *&wb, const float *&sb, int &tt) {
     if constexpr (PARTS) {
       const int p = part_of(ep.parts, tv);
@@ -1084,20 +1149,19 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       wb = ep.parts.wq[p];
       sb = ep.parts.wsc[p];
     } else {
-      tt = pair ? tv >> 1 : tv;
-      const int w0 = pair ? (tv & 1) : 0;
-      wb = w0 ? ep.wq_u : wq;
-      sb = w0 ? ep.wsc_u : wsc;
+      tt = tv;
+      wb = wsel_w ? ep.wq_u : wq;
+      sb = wsel_w ? ep.wsc_u : wsc;
     }
   };
-  if (jwg < T && b_lo + wave < b_hi) {
+  if (jwg < T && b_lo + wave_in < b_hi) {
     const int8_t *wb;
     const float *sb;
     int t0;
     unit_src(jwg, wb, sb, t0);
-    mfma_load<DOTS, W>(A, wb + (size_t)t0 * NB * kChunkBytes + lane_off,
-                       reinterpret_cast<const float4 *>(sb + (size_t)t0 * NB * kTile) + li,
-                       b_lo + wave, b_hi);
+    mfma_load<DOTS, WH>(A, wb + (size_t)t0 * NB * kChunkBytes + lane_off,
+                        reinterpret_cast<const float4 *>(sb + (size_t)t0 * NB * kTile) + li,
+                        b_lo + wave_in, b_hi);
   }
   stage_activation<MR, ACT, 64 * W>(lds, xv, m, K, NB, b_lo, nblk, act_scale_off);
   __syncthreads();
@@ -1108,7 +1172,6 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       lds + (red_on_stage ? (size_t)0 : mfma_stage_bytes(MR, ACT, nblk_max)));
 
   for (int tv = jwg; tv < T; tv += G) {
-    const int wsel = pair ? (tv & 1) : 0;
     const int8_t *wb;
     const float *sb;
     int t;
@@ -1124,7 +1187,7 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     auto compute = [&](const MfmaStage &st, int b0) {
 #pragma unroll
       for (int u = 0; u < kMfmaUnroll; ++u) {
-        const int bb = b0 + u * W;
+        const int bb = b0 + u * WH;
         if (bb >= b_hi) break;
         const int lb = bb - b_lo;
         if constexpr (ACT == kActBf16) {
@@ -1207,9 +1270,9 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       }
     };
 
-    int b = b_lo + wave;
+    int b = b_lo + wave_in;
     if (b < b_hi) {
-      if (tv != jwg) mfma_load<DOTS, W>(A, wlane, slane, b, b_hi);
+      if (tv != jwg) mfma_load<DOTS, WH>(A, wlane, slane, b, b_hi);
       // One compute site: the next stage is loaded into B while A is
       // computed, then copied into A (the copy waits for B, which the next
       // compute needs anyway).
@@ -1218,7 +1281,7 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
           compute(A, b);
           break;
         }
-        mfma_load<DOTS, W>(B, wlane, slane, b + step, b_hi);
+        mfma_load<DOTS, WH>(B, wlane, slane, b + step, b_hi);
         __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
         compute(A, b);
         A = B;
@@ -1243,10 +1306,14 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     if constexpr (PARTS) {
       const PartUnit u = part_unit(ep, tv, T);
       finish_tile<MR, W, false>(red, u.out, partial, counters, m, s, S, 0, u.ep);
+    } else if constexpr (PAIR) {
+      finish_pair_tile<MR, W>(red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad,
+                                           (unsigned)t},
+                              partial, counters, m, s, S, ep);
     } else {
-      finish_tile<MR, W, PAIR>(red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad,
-                                            (unsigned)t},
-                               partial, counters, m, s, S, wsel, ep);
+      finish_tile<MR, W, false>(red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad,
+                                             (unsigned)t},
+                                partial, counters, m, s, S, 0, ep);
     }
     __syncthreads();   // red is free again for the next tile
   }
@@ -1348,19 +1415,21 @@ hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
   // once and walks tiles j, j+G, ... (carries apart), if that fits in LDS.
   hipError_t e = grant_lds(kern, lds_alias, granted);
   if (e != hipSuccess) return e;
-  int G = a.tiles(), red_on_stage = 1;
+  // units: output tiles (the pair's two weights share a workgroup)
+  const int units = PAIR ? a.T : a.tiles();
+  int G = units, red_on_stage = 1;
   size_t lds = lds_alias;
   const int fit_alias = resident_workgroups(kern, 64 * W, lds_alias) / a.split_k;
-  if (fit_alias < a.tiles() && lds_sep + 1024 <= (size_t)max_lds) {
+  if (fit_alias < units && lds_sep + 1024 <= (size_t)max_lds) {
     e = grant_lds(kern, lds_sep, granted);
     if (e != hipSuccess) return e;
-    G = balanced_grid(resident_workgroups(kern, 64 * W, lds_sep) / a.split_k, a.tiles());
+    G = balanced_grid(resident_workgroups(kern, 64 * W, lds_sep) / a.split_k, units);
     red_on_stage = 0;
     lds = lds_sep;
   }
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
-      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.tiles(),
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, units,
       a.split_k, G, nblk_max, red_on_stage, a.act_scale_off, a.ep);
   return hipGetLastError();
 }

@@ -97,6 +97,8 @@ PLANS = [
     (1, BF16, (q8.Q8_KERNEL_VALU, 1, 3, 8, 1)),
     (4, Q8, (q8.Q8_KERNEL_VALU, 4, 1, 16, 1)),
     (16, BF16, (q8.Q8_KERNEL_MFMA, 16, 2, 8, 1)),
+    (8, BF16, (q8.Q8_KERNEL_MFMA, 16, 3, 4, 1)),
+    (5, Q8, (q8.Q8_KERNEL_MFMA, 16, 1, 4, 1)),
     (32, Q8, (q8.Q8_KERNEL_MFMA, 32, 1, 16, 1)),
     (32, Q8, (q8.Q8_KERNEL_MFMA_COLS, 32, 1, 16, 1)),
     (16, BF16, (q8.Q8_KERNEL_MFMA_COLS, 16, 3, 8, 2)),

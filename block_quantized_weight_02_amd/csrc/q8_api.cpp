@@ -165,6 +165,11 @@ int rows_for(int64_t m) {
 //  * MFMA (see below): 16 waves; the fewest K splits whose staged activation
 //    fits the LDS, more (each at least 32 blocks) while the splits still fit
 //    one workgroup per CU.
+// Rows up to which two-word activations take the VALU kernel (the rows whose
+// activation it prefetches; from 3 rows the MFMA kernel, whose 32-row tile
+// holds both words of up to 16 rows).
+constexpr int64_t kValuTwoWordRows = 2;
+
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
@@ -172,6 +177,18 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
   q8_plan p;
   p.kslices = 1;
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && m <= kValuTwoWordRows) {
+    // Few rows: the VALU kernel, two sdot4 passes per block and row
+    // (m = 1, K = 4096, N = 14336: 12.7 us against 16.0 on the MFMA kernel).
+    p.kernel = Q8_KERNEL_VALU;
+    p.rows = rows_for(m);
+    p.waves = p.rows >= 2 ? 16 : 8;
+    int64_t S = dev.cus / T;
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    p.split_k = (int32_t)S;
+    return p;
+  }
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS) {
     // The block-interleaved MFMA kernel, its 32 rows the two words' 16 each;
     // K split for the LDS, then further (each split at least 32 blocks)
@@ -188,11 +205,18 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
     p.split_k = (int32_t)S;
     return p;
   }
-  const int64_t valu_rows = act_fmt == Q8_ACT_BF16 ? 3 : 4;
-  if (m <= valu_rows) {
+  // The VALU kernel up to 2 rows: there the activation of each stage is
+  // prefetched into scalar registers with the weight; from 3 rows it is read
+  // when used, and when the activation has just been written (by its
+  // producer, as in a decode step) those reads miss the caches.  Measured on
+  // MI355X, K = 4096, N = 14336, activation rewritten before every product
+  // (rewrite included): bf16 m = 3: 17.6 us VALU against 16.3 MFMA; int8
+  // m = 3: 20.8 against 17.3, m = 4: 23.9 against 17.4; 16 waves for 2 rows
+  // (bf16 m = 2: 13.9 against 14.8 us with 8).
+  if (m <= 2) {
     p.kernel = Q8_KERNEL_VALU;
     p.rows = rows_for(m);
-    p.waves = p.rows >= 4 ? 16 : 8;
+    p.waves = p.rows >= 2 ? 16 : 8;
     int64_t S = dev.cus / T;
     if (S > smax) S = smax;
     if (S < 1) S = 1;

@@ -370,13 +370,14 @@ __device__ __forceinline__ void finish_pair_tile(const float *red, const TileOut
 constexpr int kUnroll = Q8_VALU_UNROLL;
 
 // Rows whose activation is prefetched with the stage (scalar registers): one
-// bf16 row is 16 dwords a block, an int8 row 8 dwords and its scale; more
-// rows than two would overflow the scalar registers.
+// bf16 row is 16 dwords a block, an int8 row 8 dwords and its scale (two-word
+// rows: 8 dwords of each word); more rows than two would overflow the scalar
+// registers.
 template <int MR, int ACT>
 struct ValuX {
   static constexpr bool kPrefetch = MR <= 2;
   static constexpr int kRows = kPrefetch ? MR : 1;
-  static constexpr int kWords = (ACT == kActBf16) ? 16 : 8;
+  static constexpr int kWords = (ACT == kActQ8) ? 8 : 16;
 };
 
 template <int MR, int ACT, bool DOTS>
@@ -436,6 +437,12 @@ __device__ __forceinline__ void valu_load(ValuStage<MR, ACT, DOTS> &st, const Va
               static_cast<const int8_t *>(xv) + (size_t)rr * K + (size_t)b * kBlock);
 #pragma unroll
           for (int p = 0; p < 8; ++p) st.x[u][r][p] = xr[p];
+          if constexpr (ACT == kActQ8x2) {   // the second words: rows m .. 2m-1
+            const uint32_t *xl = reinterpret_cast<const uint32_t *>(
+                static_cast<const int8_t *>(xv) + ((size_t)m + rr) * K + (size_t)b * kBlock);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) st.x[u][r][8 + p] = xl[p];
+          }
           if constexpr (!DOTS)
             st.dx[u][r] = reinterpret_cast<const float *>(static_cast<const char *>(xv) +
                                                           act_scale_off)[(size_t)rr * NB + b];
@@ -499,7 +506,19 @@ __device__ __forceinline__ void valu_compute(const ValuStage<MR, ACT, DOTS> &st,
 #pragma unroll
           for (int d = 0; d < 8; ++d)
             D = __builtin_amdgcn_sdot4((int)wd[d], kPre ? (int)st.x[u][r][d] : xr[d], D, false);
-          if constexpr (DOTS) {
+          if constexpr (ACT == kActQ8x2) {
+            // The second words' dot, joined with the first exactly in int32
+            // (|128 D_hi + D_lo| < 2^27), then one FMA with the block's scales.
+            const int *xl =
+                reinterpret_cast<const int *>(xq + ((size_t)m + r) * K + (size_t)b * kBlock);
+            int Dl = 0;
+#pragma unroll
+            for (int d = 0; d < 8; ++d)
+              Dl = __builtin_amdgcn_sdot4((int)wd[d], kPre ? (int)st.x[u][r][8 + d] : xl[d], Dl,
+                                          false);
+            const float dxv = kPre ? st.dx[u][r] : dxp[(size_t)r * NB + b];
+            acc[r] = fmaf(dxv * st.sc[u], (float)(D * 128 + Dl) * 0.0078125f, acc[r]);
+          } else if constexpr (DOTS) {
             dots[((size_t)r * NB + b) * Npad + (size_t)t * kTile + lane] = D;
           } else {
             const float dxv = kPre ? st.dx[u][r] : dxp[(size_t)r * NB + b];
@@ -1353,7 +1372,7 @@ hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
 // product carries none of the pair's code.
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
-  if constexpr (!DOTS) {
+  if constexpr (!DOTS && ACT != kActQ8x2) {
     if (a.ep.nw == 2) return launch_valu_k<MR, ACT, DOTS, W, true, false>(a, stream);
     if (a.ep.parts.n > 0) return launch_valu_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }
@@ -1543,6 +1562,15 @@ Launcher pick_valu(int rows, int act, bool dots) {
   if (act == kActBf16) return dots ? nullptr : pick_valu_rows<kActBf16, false, W>(rows);
   if (act == kActQ8)
     return dots ? pick_valu_rows<kActQ8, true, W>(rows) : pick_valu_rows<kActQ8, false, W>(rows);
+  // two words: up to 4 rows (two sdot4 passes per block and row)
+  if (act == kActQ8x2 && !dots) {
+    switch (rows) {
+      case 1: return &launch_valu<1, kActQ8x2, false, W>;
+      case 2: return &launch_valu<2, kActQ8x2, false, W>;
+      case 4: return &launch_valu<4, kActQ8x2, false, W>;
+      default: return nullptr;
+    }
+  }
   return nullptr;
 }
 

@@ -249,15 +249,21 @@ def test_two_word_rules():
     expect(1, q8.q8_quantize_act_two_words, A, A, 1, 48, S0)
     expect(3, q8.q8_quantize_act_two_words, None, A, 1, 64, S0)
     expect(4, q8.q8_quantize_act_two_words, A, A + 2, 1, 64, S0)
-    # GEMV: at most 16 rows, only the MFMA kernel; not the pair or the parts
+    # GEMV: at most 16 rows, on the MFMA kernel's 32-row tile or (up to 4 rows)
+    # the VALU kernel; not the pair or the parts
     expect(1, q8.q8_gemv, A, A, A, A, 17, 64, 8, TW, S0)
     expect(1, q8.q8_gemv_default_plan, 17, 64, 8, TW)
     assert q8.q8_gemv_workspace_bytes(17, 64, 8, TW) == 0
     p = q8.q8_gemv_default_plan(16, 4096, 14336, TW)
     assert (p.kernel, p.rows, p.waves) == (q8.Q8_KERNEL_MFMA, 32, 16)
+    p = q8.q8_gemv_default_plan(3, 4096, 14336, TW)
+    assert (p.kernel, p.rows) == (q8.Q8_KERNEL_MFMA, 32)
+    for m, rows in ((1, 1), (2, 2)):
+        p = q8.q8_gemv_default_plan(m, 4096, 14336, TW)
+        assert (p.kernel, p.rows) == (q8.Q8_KERNEL_VALU, rows)
     small = q8.q8_gemv_default_plan(1, 4096, 4096, TW)
     assert small.split_k >= 2          # 64 tiles: the splits fill the CUs
-    for kernel, rows, waves in ((q8.Q8_KERNEL_VALU, 1, 8), (q8.Q8_KERNEL_MFMA, 16, 16),
+    for kernel, rows, waves in ((q8.Q8_KERNEL_VALU, 8, 8), (q8.Q8_KERNEL_MFMA, 16, 16),
                                 (q8.Q8_KERNEL_MFMA_COLS, 32, 16)):
         bad = q8.q8_plan()
         bad.kernel, bad.rows, bad.split_k, bad.waves, bad.kslices = kernel, rows, 2, waves, 1

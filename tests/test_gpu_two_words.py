@@ -113,6 +113,36 @@ def test_gemv_two_words(m, N, pl):
     check(y, z, bnd, N, f"m={m} N={N} plan={pl}")
 
 
+# The VALU kernel's two-word form (few rows): (m, rows, split_k, waves).
+VALU_PLANS = [(1, 1, 1, 8), (1, 1, 3, 4), (2, 2, 2, 16), (3, 4, 1, 16), (4, 4, 3, 8)]
+
+
+@pytest.mark.parametrize("m,rows,split,waves", VALU_PLANS)
+@pytest.mark.parametrize("N", [200, 40])
+def test_gemv_two_words_valu(m, rows, split, waves, N):
+    K = 2176
+    x, q, s = inputs.random_case(m, K, N, seed=850 + m + N)
+    buf = quantize2(x)
+    Wq, Ws = g.pack(q, s)
+    y = gemv2(buf, Wq, Ws, m, K, N, g.plan(q8.Q8_KERNEL_VALU, rows, split, waves))
+    hi, lo, dx = words_host(buf, m, K)
+    z, bnd = oracle.gemv_q8_two_words(hi, lo, dx, q, s)
+    check(y, z, bnd, N, f"VALU m={m} N={N} rows={rows} split={split} waves={waves}")
+
+
+def test_two_words_valu_exact_case():
+    # exact-integer inputs (d = 1, lo = 0): every sum exact in any order
+    for m, waves, split in ((1, 8, 1), (2, 16, 2)):
+        x, q, s, _, _ = inputs.exact_case(m, 512, 100, seed=38 + m)
+        buf = quantize2(x)
+        hi, lo, dx = words_host(buf, m, 512)
+        assert (lo == 0).all() and (dx == 1.0).all()
+        Wq, Ws = g.pack(q, s)
+        y = gemv2(buf, Wq, Ws, m, 512, 100, g.plan(q8.Q8_KERNEL_VALU, m, split, waves))
+        z, _ = oracle.gemv_q8_two_words(hi, lo, dx, q, s)
+        np.testing.assert_array_equal(y[:, :100].astype(np.float64), z)
+
+
 def test_two_words_one_block_and_exact_case():
     m, K, N = 3, 32, 70
     x, q, s = inputs.random_case(m, K, N, seed=830)

@@ -102,6 +102,7 @@ PLANS = [
     (32, Q8, (q8.Q8_KERNEL_MFMA, 32, 1, 16, 1)),
     (32, Q8, (q8.Q8_KERNEL_MFMA_COLS, 32, 1, 16, 1)),
     (16, BF16, (q8.Q8_KERNEL_MFMA_COLS, 16, 3, 8, 2)),
+    (20, Q8, (q8.Q8_KERNEL_MFMA_COLS, 32, 2, 16, 1)),
 ]
 
 

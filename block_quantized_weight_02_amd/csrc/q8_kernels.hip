@@ -1153,7 +1153,6 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   // halves of waves stream together (waves 0 .. W/2-1 the gate, the rest the
   // up weight), so the pair meets in LDS.  WH waves split each weight's
   // blocks.
-  constexpr bool pair = PAIR;
   constexpr int WH = PAIR ? W / 2 : W;
   const int wsel_w = PAIR ? wave / WH : 0;   // the weight this wave streams
   const int wave_in = PAIR ? wave - wsel_w * WH : wave;

@@ -152,16 +152,13 @@ int rows_for(int64_t m) {
   return r;
 }
 
-// The default launch (settled by measurement on MI355X, see the design notes):
-//  * VALU kernel (lane per column) while the rows are few enough that the
-//    vector ALU keeps up with HBM: bf16 up to 3 rows, int8 up to 4 rows;
-//    MFMA kernel above.  Measured on MI355X at K = 4096, N = 14336 (loop
-//    us, VALU best / MFMA): bf16 m=3 14.2 / 14.8, m=4 16.0 / 14.8; int8 m=4
-//    13.1 / 15.5, m=5 21.9 / 15.8.
-//  * VALU: 8 waves per workgroup for 1-2 rows, 16 for 3-4 rows (more waves
-//    hide the longer per-block work: int8 m=4 13.1 us with 16 waves, 18.3
-//    with 8); K split across workgroups only when the column tiles alone
-//    leave CUs idle (splits = CUs / tiles, each split at least 8 blocks).
+// The default launch (settled by measurement on MI355X):
+//  * VALU kernel (lane per column) up to 2 rows, the rows whose activation
+//    it prefetches into scalar registers with each weight stage; MFMA kernel
+//    above (the reasons and figures are at the VALU branch below).
+//  * VALU: 8 waves per workgroup for 1 row, 16 for 2; K split across
+//    workgroups only when the column tiles alone leave CUs idle (splits =
+//    CUs / tiles, each split at least 8 blocks).
 //  * MFMA (see below): 16 waves; the fewest K splits whose staged activation
 //    fits the LDS, more (each at least 32 blocks) while the splits still fit
 //    one workgroup per CU.

@@ -65,17 +65,18 @@ struct GemmShape {
 
 // Byte offset, within one row's staged activation, of 16-byte part `unit`
 // of row r (bf16), or of 8-byte unit `unit` (int8).  The parts of a row are
-// permuted by a function of r % 16 chosen so that an MFMA operand read (16
-// rows, one part each) hits distinct LDS banks whether the LDS serves 16
-// lanes from 64 banks or 8 lanes from 32 banks per cycle: with
-// r % 16 = 8a + 4b + 2c + d, bf16 parts are XORed with 2(a ^ c) + b, which
-// is a bijection over (a, b) for fixed (c, d) and over (b, c) for fixed
-// (a, d).
+// permuted by a function of r % 16 so that the MFMA operand read (lane
+// (i, j) reads part j of row i, 16 bytes) does not stall on LDS banks.  The
+// bf16 parts are XORed with bits 1-2 of the row: measured with the LDS
+// bank-conflict counter on MI355X, that read is conflict-free, while rows
+// at a 64-byte stride unpermuted, or XORed with bits 0-1, 2-3, or
+// (bit 3 ^ bit 1, bit 2), stall on about a sixth of their LDS cycles; the
+// staging writes (lane l writes part l % 4 of row l / 4) are conflict-free
+// under any of these.
 template <int ACT>
 __device__ __forceinline__ int a_part(int r, int unit) {
   if constexpr (ACT == kActBf16) {
-    const int f = ((((r >> 3) ^ (r >> 1)) & 1) << 1) | ((r >> 2) & 1);
-    return (unit ^ f) * 16;
+    return (unit ^ ((r >> 1) & 3)) * 16;
   } else {
     return (unit ^ (((r >> 3) & 1) << 1)) * 8;
   }

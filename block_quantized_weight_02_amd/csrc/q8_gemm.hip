@@ -72,13 +72,16 @@ struct GemmShape {
 // at a 64-byte stride unpermuted, or XORed with bits 0-1, 2-3, or
 // (bit 3 ^ bit 1, bit 2), stall on about a sixth of their LDS cycles; the
 // staging writes (lane l writes part l % 4 of row l / 4) are conflict-free
-// under any of these.
+// under any of these.  The int8 rows' four 8-byte units are XORed with bits
+// 2-3 of the row: both the operand read (lane (i, j): unit j of row i) and the
+// staging writes (two 8-byte units a lane) conflict-free, where the earlier
+// permutation stalled the writes on half their cycles.
 template <int ACT>
 __device__ __forceinline__ int a_part(int r, int unit) {
   if constexpr (ACT == kActBf16) {
     return (unit ^ ((r >> 1) & 3)) * 16;
   } else {
-    return (unit ^ (((r >> 3) & 1) << 1)) * 8;
+    return (unit ^ ((r >> 2) & 3)) * 8;
   }
 }
 

@@ -158,10 +158,16 @@ int rows_for(int64_t m) {
 //    above (the reasons and figures are at the VALU branch below).
 //  * VALU: 8 waves per workgroup for 1 row, 16 for 2; K split across
 //    workgroups only when the column tiles alone leave CUs idle (splits =
-//    CUs / tiles, each split at least 8 blocks).
+//    CUs / tiles, each split at least 40 blocks: the split-K combine costs
+//    more than the extra workgroups gain below that; measured on MI355X,
+//    m = 1, K = 1024, N = 1024: 1 split 3.9-4.0 us against 4 splits 5.1;
+//    K = 4096, N = 4096: 3 splits 7.1-7.2 against 2 splits 7.3-7.5 and
+//    4 splits 7.6-7.7).
 //  * MFMA (see below): 16 waves; the fewest K splits whose staged activation
 //    fits the LDS, more (each at least 32 blocks) while the splits still fit
-//    one workgroup per CU.
+//    one workgroup per CU.  Block-interleaved, except for 17-32 rows whose
+//    LDS splits alone give more workgroups than CUs: there the column-group
+//    form.
 // Rows up to which two-word activations take the VALU kernel (the rows whose
 // activation it prefetches; from 3 rows the MFMA kernel, whose 32-row tile
 // holds both words of up to 16 rows).
@@ -171,7 +177,7 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   const DeviceFacts dev = device_facts();
-  const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
+  const int64_t smax = NB / 40 > 0 ? NB / 40 : 1;
   q8_plan p;
   p.kslices = 1;
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && m <= kValuTwoWordRows) {
@@ -220,29 +226,44 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
     p.split_k = (int32_t)S;
     return p;
   }
-  // Matrix cores.  Up to 16 rows, and for bf16 activations at any row
-  // count: waves split K and each covers the whole tile, so one LDS fragment
-  // read serves four MFMAs.  int8 activations of 17-32 rows: each wave owns a
+  // Matrix cores.  The block-interleaved kernel: waves split K and each
+  // covers the whole tile, so one LDS fragment read serves four MFMAs.  For
+  // 17-32 rows whose 32-row stage needs K splits that already give more
+  // workgroups than CUs, the column-group kernel instead: each wave owns a
   // 16-column group and the workgroup walks tiles with the activation staged
-  // once.  Measured on MI355X: int8, m = 16, K = 4096, N = 14336: 16.2 us
+  // once, so no split beyond the LDS's is paid for.  Measured on MI355X
+  // (int8, m = 32, K = 5120, where the stage needs 2 splits): N = 40
+  // block-interleaved 11.4 us against column-group 16.6; N = 4096 13.4
+  // against 22.2; N = 8192 16.4 against 22.2 (its best); N = 14336 (448
+  // workgroups) 28.2 against 26.7, N = 32000 52.0 against 49.9.  m = 24,
+  // K = 4096, N = 14336 (one split): 17.8 against 24.7.  bf16, m = 32,
+  // K = 4096 (2 splits): N = 4096 block-interleaved 12.0 against 13.0;
+  // N = 14336 25.1 against 23.2.  int8, m = 16, K = 4096, N = 14336: 16.2 us
   // block-interleaved against 24-52 us column-group over its splits and
-  // widths; int8, m = 32, K = 5120, N = 32000: column-group, 2 splits,
-  // 50.6 us against 60.9 us.
-  p.kernel = (act_fmt == Q8_ACT_BF16 || m <= 16) ? Q8_KERNEL_MFMA : Q8_KERNEL_MFMA_COLS;
+  // widths.
+  p.kernel = Q8_KERNEL_MFMA;
   p.rows = m <= 16 ? 16 : 32;
   p.waves = 16;
   p.kslices = 1;
-  int64_t S = 1;
   const size_t budget = (size_t)dev.lds_per_block;
-  while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
-                                      (int)S) > budget - kStaticLdsReserve)
-    ++S;
+  const auto lds_splits = [&](const q8_plan &pl) {
+    int64_t s = 1;
+    while (s < NB && q8::gemv_lds_bytes(pl.kernel, pl.rows, act_fmt, pl.waves, pl.kslices,
+                                        (int)NB, (int)s) > budget - kStaticLdsReserve)
+      ++s;
+    return s;
+  };
+  int64_t S = lds_splits(p);
+  if (m > 16 && T * S > dev.cus) {
+    p.kernel = Q8_KERNEL_MFMA_COLS;
+    S = lds_splits(p);
+  }
   // Then more splits while they still fit one workgroup per CU, each split
   // at least 32 blocks: a narrow product's few tiles alone leave CUs idle.
   // Measured on MI355X: bf16, m = 4, K = 4096, N = 640: 1 split 12.2 us,
   // 4 splits 8.9, 16 splits 11.1; m = 16, N = 4096: 1 split 13.6, 4 splits
-  // 10.2, 8 splits 15.0; int8, m = 32, K = 5120, N = 40: 2 splits 28.7,
-  // 5 splits 22.9, 20 splits 44.5.
+  // 10.2, 8 splits 15.0; int8, m = 32, K = 5120, N = 40: 3 splits 12.3,
+  // 4 splits 11.4, 5 splits 11.7, 8 splits 12.1.
   const int64_t tiles_per_wg = p.kernel == Q8_KERNEL_MFMA_COLS ? p.waves / (4 * p.kslices) : 1;
   const int64_t wgs = (T + tiles_per_wg - 1) / tiles_per_wg;
   const int64_t smax_mfma = NB / 32 > 1 ? NB / 32 : 1;

@@ -216,8 +216,9 @@ def test_parts_validation():
     if need:
         expect(5, q8.q8_gemv_parts_planned, A, three, 1, 4096, 0, p, S0, None, 0)
         expect(5, q8.q8_gemv_parts_planned, A, three, 1, 4096, 0, p, S0, A, need - 16)
-    cols = q8.q8_gemv_default_plan(32, 4096, 6144, 1)
-    assert cols.kernel == q8.Q8_KERNEL_MFMA_COLS
+    cols = q8.q8_plan()
+    cols.kernel, cols.rows, cols.split_k, cols.waves, cols.kslices = \
+        q8.Q8_KERNEL_MFMA_COLS, 32, 1, 16, 1
     expect(7, q8.q8_gemv_parts_planned, A, three, 32, 4096, 1, cols, S0, A, 1 << 30)
     assert q8.q8_parts_workspace_bytes(p, [], 1, 4096) == 0
 

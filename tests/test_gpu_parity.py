@@ -352,7 +352,7 @@ def test_two_streams():
 def test_library_workspace_reused_across_shapes():
     # One stream's library workspace serves calls of different shapes in turn:
     # the split-K counters keep fixed places, so no call sees another's carries.
-    shapes = [(1, 1056, 200), (4, 4096, 640), (1, 1056, 200), (2, 8192, 64), (4, 4096, 640)]
+    shapes = [(1, 2592, 200), (4, 4096, 640), (1, 2592, 200), (2, 8192, 64), (4, 4096, 640)]
     for i, (m, K, N) in enumerate(shapes):
         x, q, s = inputs.random_case(m, K, N, seed=300 + i)
         assert q8.q8_gemv_default_plan(m, K, N, BF16).split_k > 1

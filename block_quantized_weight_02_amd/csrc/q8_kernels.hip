@@ -188,13 +188,27 @@ __device__ __forceinline__ void store_final(const Epi &ep, float *__restrict__ y
 }
 
 // Sum over the S splits of weight `wsel`'s partial carries of (r, col), in
-// split order.  partial holds [wsel][split][row][column] carries.
+// split order.  partial holds [wsel][split][row][column] carries.  The loads
+// go out eight at a time (a place past the last split reloads the last one,
+// unused), so the last arrival waits about one memory round trip per eight
+// splits rather than one per split; the additions keep split order, so the
+// sum has the bits of the plain serial one.
 __device__ __forceinline__ float sum_partials(const float *__restrict__ partial, int m, int Npad,
                                               int S, int wsel, int r, size_t col) {
+  constexpr int kBatch = 8;
   const float *p = partial + ((size_t)wsel * S * m + r) * Npad + col;
-  float v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  for (int ss = 1; ss < S; ++ss)
-    v += __hip_atomic_load(p + (size_t)ss * m * Npad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const size_t stride = (size_t)m * Npad;
+  float v = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float t[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      t[q] = __hip_atomic_load(p + (size_t)min(s0 + q, S - 1) * stride, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (s0 + q < S) v = (s0 + q == 0) ? t[q] : v + t[q];
+  }
   return v;
 }
 
@@ -790,30 +804,38 @@ __device__ __forceinline__ buf_t cols_record(float *partial, int T, int s, int t
 }
 
 // Sums over the S splits (in split order) of unit tv's partial carries for
-// v[0][e][h]'s places (row group rg: rows 16rg + 4j + e; column group g0 + h);
-// the loads of one split are issued together.
+// v[0][e][h]'s places (row group rg: rows 16rg + 4j + e; column group g0 + h).
+// The loads of four splits are issued together (a place past the last split
+// reloads the last one, unused); the additions keep split order.
 template <int MR, int H>
 __device__ __forceinline__ void cols_sum_partials(float *partial, int T, int S, int tv, int g0,
                                                   int rg, int lane, float (&v)[1][4][H]) {
+  constexpr int kBatch = 4;
   const unsigned off = (unsigned)(rg * 256 + lane * 4) * 4u;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float4 a[kBatch][H];
 #pragma unroll
-  for (int h = 0; h < H; ++h) {
-    const float4 a = buf_ld16_sys(cols_record<MR>(partial, T, 0, tv, g0 + h), off);
-    v[0][0][h] = a.x;
-    v[0][1][h] = a.y;
-    v[0][2][h] = a.z;
-    v[0][3][h] = a.w;
-  }
-  for (int ss = 1; ss < S; ++ss) {
-    float4 a[H];
+    for (int q = 0; q < kBatch; ++q)
 #pragma unroll
-    for (int h = 0; h < H; ++h) a[h] = buf_ld16_sys(cols_record<MR>(partial, T, ss, tv, g0 + h), off);
+      for (int h = 0; h < H; ++h)
+        a[q][h] = buf_ld16_sys(cols_record<MR>(partial, T, min(s0 + q, S - 1), tv, g0 + h), off);
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      v[0][0][h] += a[h].x;
-      v[0][1][h] += a[h].y;
-      v[0][2][h] += a[h].z;
-      v[0][3][h] += a[h].w;
+    for (int q = 0; q < kBatch; ++q) {
+      if (s0 + q >= S) break;
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        if (s0 + q == 0) {
+          v[0][0][h] = a[q][h].x;
+          v[0][1][h] = a[q][h].y;
+          v[0][2][h] = a[q][h].z;
+          v[0][3][h] = a[q][h].w;
+        } else {
+          v[0][0][h] += a[q][h].x;
+          v[0][1][h] += a[q][h].y;
+          v[0][2][h] += a[q][h].z;
+          v[0][3][h] += a[q][h].w;
+        }
+      }
     }
   }
 }

@@ -18,9 +18,12 @@ the counters into bytes.
 Prints ONE JSON line on stdout.  `value` is the whole-job rate in GB/s of
 algorithmic bytes (weight values + fp32 scales + activation + output) over
 the timed steps; `roofline` prices the product kernel's own average duration
-(HIP events around each launch, on the launch stream) against 8 TB/s;
+against 8 TB/s.  Every timed region is exactly its step count of launches,
+queued behind a bounded device-side hold so that they run back to back (HIP
+events on the launch stream around them; see time_loop);
 `cpu_baseline` times the CPU oracle on the same workload on this host;
-`by_rows` gives the same measurement at m = 16 and m = 32; `fused_epilogue`
+`by_config` gives the same measurement (step and product) at every other
+configuration (m = 1, 16 and 32); `fused_epilogue`
 times the product with bias, residual and quantized output beside the plain
 product, at m = 1 and m = 32, and the gated pair (gate and up through SiLU in
 one launch) beside two plain products, at m = 1 and m = 16, and the product
@@ -28,7 +31,9 @@ in parts (query, key and value projections of one activation in one launch)
 beside the same products one by one, at m = 1 and m = 16, and the two-word
 int8 activation (quantize then product) beside the one-word step, at m = 1
 and m = 16; `context` gives
-the headline with one weight copy reused and a 1 GiB device copy's rate;
+the read ceiling (q8_stream_read over the headline's bytes, best of a grid
+sweep), the headline with one weight copy reused and a 1 GiB device copy's
+rate;
 `prefill` times the many-row product (m = 512) against the MFMA peak, with
 bf16, one-word and two-word int8 activations.
 """
@@ -174,35 +179,63 @@ class Setup:
             raise RuntimeError(self.q8.q8_last_error())
 
 
-def time_loop(fn, steps):
-    """Milliseconds per step of `steps` back-to-back steps on the stream."""
+_HOLD = {"cycles_per_ms": None}
+
+
+def _hold_cycles_per_ms():
+    """Clock rate of the device-side hold (torch's bounded spin kernel), timed
+    once with events."""
+    import torch
+    if _HOLD["cycles_per_ms"] is None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(2_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _HOLD["cycles_per_ms"] = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    return _HOLD["cycles_per_ms"]
+
+
+def time_loop(fn, steps, info=None):
+    """Milliseconds per step of exactly `steps` steps run back to back on the
+    launch stream.
+
+    The launches are queued behind a bounded device-side hold (a spin kernel)
+    and the start event is recorded after it, so the host's launch latency
+    cannot open gaps between them: the GPU finds every launch already queued.
+    That the host finished queueing before the hold ended is checked (the
+    start event has not been reached yet); otherwise the hold is lengthened
+    and the measurement retaken (at most three times; `info["back_to_back"]`
+    says whether it held)."""
     import torch
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        fn(i)
-    e1.record()
-    torch.cuda.synchronize()
+    hold_ms = 2.0 + 0.02 * steps           # ~20 us of host time per queued step
+    queued = False
+    for _ in range(3):
+        torch.cuda._sleep(int(hold_ms * _hold_cycles_per_ms()))
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        queued = not e0.query()
+        torch.cuda.synchronize()
+        if queued:
+            break
+        hold_ms *= 4
+    if info is not None:
+        info["back_to_back"] = queued
+        info["hold_ms"] = hold_ms
     return e0.elapsed_time(e1) / steps
 
 
-def time_each(fn, steps):
-    """Per-launch durations (ms) from an event pair around every launch."""
-    import torch
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record()
-        fn(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    return np.array([a.elapsed_time(b) for a, b in ev])
-
-
 def measure(w, steps, warmup, rotate=True):
+    """One workload's step and product: `warmup` untimed steps, then exactly
+    `steps` timed steps back to back; for Q8_0 activations the product alone
+    is timed the same way (its launches are the step's minus the quantize)."""
     import torch
     st = Setup(w, rotate=rotate)
     b = algorithmic_bytes(w)
@@ -211,17 +244,13 @@ def measure(w, steps, warmup, rotate=True):
     for i in range(warmup):
         st.step(i)
     torch.cuda.synchronize()
+    info = {}
     t0 = time.perf_counter()
-    ms = time_loop(st.step, steps)
+    ms = time_loop(st.step, steps, info)
     wall = time.perf_counter() - t0
-    # The product kernel alone, back to back on its stream: events around the
-    # timed region, divided by the launches (this is what a kernel trace's
-    # average duration agrees with; an event pair around every single launch
-    # adds the events' own overhead, reported separately).
-    gemv_ms = ms if w.act == "bf16" else time_loop(st.gemv_only, steps)
-    each = time_each(st.gemv_only, min(steps, 500))
+    gemv_ms = ms if w.act == "bf16" else time_loop(st.gemv_only, steps, info)
     log(f"[bench] {w.name}: {ms * 1e3:.2f} us/step, product kernel {gemv_ms * 1e3:.2f} us/launch "
-        f"(event pair per launch: mean {each.mean() * 1e3:.2f} us)")
+        f"(back to back: {info['back_to_back']})")
     step_bytes = b["total"]
     weights = w.K * w.N
     res = {
@@ -231,9 +260,7 @@ def measure(w, steps, warmup, rotate=True):
         "weights_per_s": weights / (ms * 1e-3),
         "macs_per_s": w.m * weights / (ms * 1e-3),
         "kernel_us_mean": gemv_ms * 1e3,
-        "event_pair_us_mean": float(each.mean() * 1e3),
-        "event_pair_us_p10": float(np.percentile(each, 10) * 1e3),
-        "event_pair_us_p90": float(np.percentile(each, 90) * 1e3),
+        "launches_timed": steps, "back_to_back": info["back_to_back"],
         "bytes": b, "copies": st.copies, "wall_s": wall,
         "plan": {"kernel": st.plan.kernel, "rows": st.plan.rows,
                  "split_k": st.plan.split_k, "waves": st.plan.waves, "kslices": st.plan.kslices},
@@ -246,6 +273,44 @@ def measure(w, steps, warmup, rotate=True):
     del st
     torch.cuda.empty_cache()
     return res
+
+
+def read_ceiling(torch, nbytes, steps):
+    """The read ceiling at the product's size: q8_stream_read over `nbytes`
+    (the product's algorithmic bytes), each launch a different window of a
+    1 GiB buffer (as the product rotates its weight copies), over a sweep of
+    grid shapes; returns the best and every shape's rate."""
+    import block_quantized_weight_02_amd as q8
+    span = 2 ** 30
+    buf = torch.empty(span, dtype=torch.uint8, device="cuda:0")
+    buf.random_(0, 255)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    n = (nbytes + 15) // 16 * 16
+    nwin = max(2, (span - n) // n)
+    offs = [(i * n) // 256 * 256 for i in range(nwin)]
+    base = buf.data_ptr()
+    lib = q8.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+    sink_p = sink.data_ptr()
+    rows = []
+    for wgs in (224, 256, 512, 1024, 2048):
+        for waves in (4, 8, 16):
+            for depth in (1, 2, 4):
+                def call(i, wgs=wgs, waves=waves, depth=depth):
+                    rc = lib.q8_stream_read(base + offs[i % nwin], n, wgs, waves, depth, sink_p, sp)
+                    if rc:
+                        raise RuntimeError(q8.q8_last_error())
+                for i in range(20):
+                    call(i)
+                ms = time_loop(call, steps)
+                rows.append({"workgroups": wgs, "waves": waves, "depth": depth,
+                             "us": ms * 1e3, "gbs": n / (ms * 1e-3) / 1e9})
+    del buf, sink
+    torch.cuda.empty_cache()
+    best = max(rows, key=lambda r: r["gbs"])
+    log(f"[bench] read ceiling over {n} B: {best['us']:.2f} us, {best['gbs']:.0f} GB/s "
+        f"({best['workgroups']} x {best['waves']} waves, depth {best['depth']})")
+    return {"bytes": n, "launches_per_shape": steps, "best": best, "sweep": rows}
 
 
 def measure_fused(w, steps, warmup, rotate=True):
@@ -598,21 +663,57 @@ def copy_calibration(torch, nbytes=256 * 2 ** 20, reps=20):
                       "ms_per_copy": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+CONFIG_IDS = {"decode_k1024_n1024": "C1", "decode_k4096_n4096": "C2",
+              "ffn_down_k14336_n4096": "C3", "batch16_k4096_n14336": "C4",
+              "q8act_m32_k5120_n40": "C5a", "q8act_m32_k5120_n32000": "C5b",
+              "decode_k4096_n14336": "T"}
+
+
+def summarize_kernel_trace(path):
+    """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV: count,
+    mean, median, p10 and p90 of the dispatch durations (us), in order of
+    total time.  Prints one JSON line."""
+    import csv
+    durs = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("KernelName") or row.get("Name")
+            t0, t1 = row.get("Start_Timestamp"), row.get("End_Timestamp")
+            if not name or t0 is None or t1 is None:
+                continue
+            durs.setdefault(name, []).append((int(t1) - int(t0)) / 1e3)
+    out = []
+    for name, d in durs.items():
+        a = np.array(d)
+        out.append({"kernel": name, "dispatches": int(a.size), "total_us": float(a.sum()),
+                    "mean_us": float(a.mean()), "median_us": float(np.median(a)),
+                    "p10_us": float(np.percentile(a, 10)), "p90_us": float(np.percentile(a, 90))})
+    out.sort(key=lambda r: -r["total_us"])
+    print(json.dumps({"trace": os.path.basename(path), "kernels": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None, help="headline workload name (default: the m=1 decode shape)")
-    ap.add_argument("--no-rows", action="store_true", help="skip the m=16 and m=32 rows")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other configurations (m = 1, 16 and 32 shapes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-epilogue lines")
     ap.add_argument("--no-prefill", action="store_true", help="skip the many-row (prefill) lines")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling sweep")
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy (for profiler counter calibration)")
+    ap.add_argument("--summarize-kernel-trace", metavar="CSV", default=None,
+                    help="print per-kernel dispatch statistics of a rocprofv3 kernel trace")
     args = ap.parse_args()
 
+    if args.summarize_kernel_trace:
+        summarize_kernel_trace(args.summarize_kernel_trace)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the product shards by columns across GPUs with no collective)",
@@ -635,16 +736,19 @@ def main():
     w = inputs.WORKLOADS[name]
     head = measure(w, args.steps, args.warmup, rotate=not args.no_rotate)
 
-    by_rows = {}
+    # every other configuration, product and step, at least 200 launches each
+    by_config = {}
     if not args.no_rows:
-        for other in ("batch16_k4096_n14336", "q8act_m32_k5120_n32000"):
+        for other, cid in CONFIG_IDS.items():
             if other == name:
                 continue
-            r = measure(inputs.WORKLOADS[other], max(200, args.steps // 4), max(20, args.warmup // 4),
+            r = measure(inputs.WORKLOADS[other], max(200, args.steps), max(20, args.warmup),
                         rotate=not args.no_rotate)
-            by_rows[f"m{inputs.WORKLOADS[other].m}"] = {
-                k: r[k] for k in ("workload", "us_per_step", "gbs", "pct_hbm_peak", "weights_per_s",
-                                  "macs_per_s", "kernel_us_mean", "kernel_gbs", "kernel_pct_hbm_peak", "plan")}
+            by_config[cid] = {
+                k: r[k] for k in ("workload", "m", "K", "N", "act", "us_per_step", "gbs",
+                                  "pct_hbm_peak", "weights_per_s", "macs_per_s",
+                                  "kernel_us_mean", "kernel_gbs", "kernel_pct_hbm_peak",
+                                  "launches_timed", "back_to_back", "plan")}
 
     fused = {}
     if not args.no_fused:
@@ -675,9 +779,13 @@ def main():
             inputs.WORKLOADS["prefill_q8act_m512_k4096_n14336"], max(100, args.steps // 10),
             max(10, args.warmup // 10), rotate=not args.no_rotate, two_words=True)
 
-    context = None
+    context = {}
+    if not args.no_ceiling:
+        context["read_ceiling"] = read_ceiling(torch, head["bytes"]["total"], 200)
+        best = context["read_ceiling"]["best"]["gbs"]
+        context["product_frac_of_read_ceiling"] = head["kernel_gbs"] / best
     if not args.no_rows:
-        context = bandwidth_context(torch, w, 200)
+        context.update(bandwidth_context(torch, w, 200))
         log(f"[bench] context: one weight copy {context['mall_hot_us']:.2f} us; 1 GiB copy "
             f"{context['copy_1gib_gbs_read_plus_write']:.0f} GB/s read+write")
 
@@ -686,8 +794,8 @@ def main():
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": kernel_name(head["plan"], w),
-            "kernel_us_mean": head["kernel_us_mean"], "loop_us_per_step": head["us_per_step"],
-            "bytes_per_launch": head["bytes"]["total"]}
+            "kernel_us_mean": head["kernel_us_mean"], "launches_timed": head["launches_timed"],
+            "back_to_back": head["back_to_back"], "bytes_per_launch": head["bytes"]["total"]}
 
     cpu = None
     if not args.no_cpu:
@@ -714,11 +822,9 @@ def main():
         "pct_hbm_peak": head["pct_hbm_peak"],
         "weights_per_s": head["weights_per_s"],
         "macs_per_s": head["macs_per_s"],
-        "kernel_us": {k: head[k] for k in ("kernel_us_mean", "event_pair_us_mean", "event_pair_us_p10",
-                                           "event_pair_us_p90")},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "by_rows": by_rows,
+        "by_config": by_config,
         "fused_epilogue": fused,
         "context": context,
         "prefill": prefill,

@@ -118,6 +118,7 @@ _SIGS = {
     "q8_status_string": (ctypes.c_char_p, [_int]),
     "q8_last_error": (ctypes.c_char_p, []),
     "q8_release_workspaces": (_int, []),
+    "q8_stream_read": (_int, [_p, _sz, _int, _int, _int, _p, _p]),
     "q8_layout_version": (_int, []),
 }
 
@@ -388,3 +389,9 @@ def q8_release_workspaces() -> None:
 
 def q8_layout_version() -> int:
     return int(lib().q8_layout_version())
+
+
+def q8_stream_read(src, nbytes, workgroups, waves, depth, sink, stream=None) -> None:
+    _check(lib().q8_stream_read(_addr(src), nbytes, workgroups, waves, depth, _addr(sink),
+                                _stream(stream)))
+

@@ -39,6 +39,22 @@ int ok() {
   return Q8_OK;
 }
 
+}  // namespace
+
+namespace q8 {
+int report_error(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+}  // namespace q8
+
+namespace {
+
 int64_t round_up(int64_t v, int64_t to) { return (v + to - 1) / to * to; }
 
 // Largest sizes the 32-bit launch arithmetic admits (checked, not assumed).
@@ -333,6 +349,16 @@ int library_workspace(hipStream_t stream, size_t need, void **out) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace &w = g_ws[{dev, stream}];
   if (w.bytes < need) {
+    // Allocating (and clearing) a workspace is not a graph-capturable step:
+    // refuse under capture rather than record a memset node and bake a
+    // buffer the library may later retire into the graph.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+      return fail(Q8_ERR_WORKSPACE,
+                  "this call needs a %zu-byte split-K workspace and the stream is being "
+                  "captured: the library does not allocate under capture; pass a workspace "
+                  "(q8_gemv_ws / the _planned calls) or make one uncaptured call first",
+                  need);
     // Work already queued on the stream may still use the old buffer: retire
     // it rather than free it.
     if (w.ptr) g_ws_retired.push_back({dev, w.ptr});
@@ -1007,6 +1033,33 @@ int q8_release_workspaces(void) {
 }
 
 int q8_layout_version(void) { return q8::kLayoutVersion; }
+
+int q8_stream_read(const void *src, size_t bytes, int workgroups, int waves, int depth,
+                   void *sink, hipStream_t stream) {
+  int st;
+  if ((st = check_ptr(src, "src")) || (st = check_ptr(sink, "sink"))) return st;
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(Q8_ERR_SHAPE, "bytes = %zu: need a positive multiple of 16", bytes);
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(Q8_ERR_SHAPE, "workgroups = %d out of range: need 1 <= workgroups <= 65536",
+                workgroups);
+  if (waves < 1 || waves > 16)
+    return fail(Q8_ERR_SHAPE, "waves = %d out of range: need 1 <= waves <= 16", waves);
+  if (depth != 1 && depth != 2 && depth != 4)
+    return fail(Q8_ERR_SHAPE, "depth = %d: need 1, 2 or 4", depth);
+  const size_t slice = ((bytes + 1023) / 1024 + workgroups - 1) / workgroups * 1024;
+  if (slice > ((size_t)1 << 31))
+    return fail(Q8_ERR_SHAPE, "a workgroup's slice of %zu bytes exceeds 2^31: more workgroups",
+                slice);
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_stream_read(src, bytes, workgroups, waves, depth,
+                                        static_cast<unsigned *>(sink), stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_fail(e, "stream read launch");
+  }
+  return ok();
+}
 
 
 int q8_gemv_parts_default_plan(const q8_part *parts, int n_parts, int64_t m, int64_t K,

@@ -121,4 +121,13 @@ struct GemmArgs {
 int gemm_rows_per_block(int64_t m);
 hipError_t launch_gemm(int act, bool write_dots, int bm, const GemmArgs &a, hipStream_t stream);
 
+// The read ceiling (q8_measure.hip): reads `bytes` once, `workgroups`
+// contiguous slices of whole KiB, `waves` waves each with `depth` (1, 2, 4)
+// pieces of 1 KiB in flight.
+hipError_t launch_stream_read(const void *src, unsigned long long bytes, int workgroups,
+                              int waves, int depth, unsigned *sink, hipStream_t stream);
+
+// Sets the calling thread's q8_last_error() message and returns status.
+int report_error(int status, const char *fmt, ...);
+
 }  // namespace q8

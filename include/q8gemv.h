@@ -163,9 +163,11 @@ int q8_quantize_act_two_words(const uint16_t *x_bf16, void *x_q8x2, int64_t m,
  * them (plans naming another kernel are Q8_ERR_PLAN), and the gated pair
  * and the parts do not (Q8_ERR_ACT_FMT).  When the chosen plan splits K across
  * workgroups it uses a workspace the library allocates on first need and
- * keeps per (device, stream) until q8_release_workspaces(); that first call
- * allocates, so it must not be inside a graph capture.  Calls on one stream
- * are ordered; calls on different streams use different workspaces.
+ * keeps per (device, stream) until q8_release_workspaces(); a call that would
+ * allocate while its stream is being captured returns Q8_ERR_WORKSPACE
+ * instead (make one uncaptured call first, or pass a workspace through
+ * q8_gemv_ws).  Calls on one stream are ordered; calls on different streams
+ * use different workspaces.
  */
 int q8_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
             float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
@@ -403,11 +405,30 @@ int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
 const char *q8_status_string(int status);
 /* Thread-local message of this thread's last failing call ("" if none). */
 const char *q8_last_error(void);
-/* Frees the workspaces q8_gemv allocated (synchronizes the device first). */
+/* Frees the workspaces q8_gemv allocated (synchronizes the device first).  A
+ * graph captured over a library workspace keeps that buffer's address: after
+ * this call such a graph must not be replayed. */
 int q8_release_workspaces(void);
 /* Version of the packed layout: weights packed by another version are
  * rejected by no check -- repack them. */
 int q8_layout_version(void);
+
+/* ---- measurement ------------------------------------------------------------ */
+
+/*
+ * q8_stream_read: the read ceiling of the product.  A decode step is bound by
+ * the weight's bytes (from_q8.rs, module doc), so the rate at which this chip
+ * reads a given number of bytes once bounds the product's.  This call reads
+ * `bytes` at `src` once with the product's weight-stream loads (16-byte
+ * non-temporal loads; `workgroups` contiguous slices of whole KiB, each read
+ * by `waves` waves with `depth` KiB in flight per wave) and computes nothing
+ * from them; `sink` (4 bytes, 16-byte aligned) is written only for an input
+ * no caller supplies.  Requires bytes a positive multiple of 16, 1 <=
+ * workgroups <= 65536, 1 <= waves <= 16, depth 1, 2 or 4, and a slice of at
+ * most 2^31 bytes (Q8_ERR_SHAPE otherwise).  Allocates nothing.
+ */
+int q8_stream_read(const void *src, size_t bytes, int workgroups, int waves, int depth,
+                   void *sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,7 @@ def _configure(lib):
                                           _p, _p]
     lib.q8o_gemv_q8_two_words.restype = ctypes.c_int
     lib.q8o_swiglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _p]
+    lib.q8o_epilogue.argtypes = [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p]
     lib.q8o_view_rows.argtypes = [_i64, _i64]
     lib.q8o_view_rows.restype = _i64
     lib.q8o_fold_bytes.argtypes = [_i64, _i64, _i64, _i64, _i64,
@@ -289,6 +290,101 @@ def gemv_glu_q8(xq, dx, qg, sg, qu, su, bg=None, bu=None, cols=None):
     out = swiglu(g, u, None if bg is None else np.asarray(bg)[c],
                  None if bu is None else np.asarray(bu)[c])
     return out, g, u, bnd_g, bnd_u
+
+
+def epilogue(y: np.ndarray, bound: np.ndarray, bias: Optional[np.ndarray] = None,
+             residual: Optional[np.ndarray] = None,
+             cols: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """``(z, bound)`` of a fused projection: ``z = y + bias + residual`` over
+    the listed columns, in fp64 (plan.rs, enum Launch, variant Gemv, field
+    ``bias``; the residual add of its gemv_norm_epilogue note).  ``y, bound``
+    are a product's ``m x len(cols)`` output from gemv_bf16 / gemv_q8; ``bias``
+    holds one fp32 value per column of the whole output, ``residual`` is an
+    fp32 ``m x W`` array (W >= the largest listed column + 1)."""
+    y = _c(y, np.float64)
+    bound = _c(bound, np.float64)
+    m, nc = y.shape
+    if bound.shape != y.shape:
+        raise ValueError("y and bound must have one shape")
+    ncols_all = None
+    b = None if bias is None else _c(bias, np.float32)
+    r = None if residual is None else _c(residual, np.float32)
+    if b is not None:
+        ncols_all = b.shape[0]
+    if r is not None:
+        if r.ndim != 2 or r.shape[0] != m:
+            raise ValueError("residual must be m x W")
+        ncols_all = r.shape[1] if ncols_all is None else min(ncols_all, r.shape[1])
+    c = None
+    if cols is not None:
+        c = _c(cols, np.int64)
+        if c.shape != (nc,):
+            raise ValueError("one column per output column")
+        if ncols_all is not None and c.size and (c.min() < 0 or c.max() >= ncols_all):
+            raise ValueError("column list out of range")
+    elif ncols_all is not None and nc > ncols_all:
+        raise ValueError("bias or residual narrower than y")
+    z = np.empty((m, nc), np.float64)
+    zb = np.empty((m, nc), np.float64)
+    _load().q8o_epilogue(_ptr(y), _ptr(bound), m, nc, None if c is None else _ptr(c),
+                         None if b is None else _ptr(b), None if r is None else _ptr(r),
+                         0 if r is None else r.shape[1], _ptr(z), _ptr(zb))
+    return z, zb
+
+
+# ---------------------------------------------------------------------------
+# The library's packed weight layout, written out from its definition (layout
+# version 2).  The pages fix only the canonical tensors (from_q8.rs, enum
+# Q8Part: the host repacks the checkpoint's blocks into a values tensor and a
+# scales tensor); the device layout is this library's own choice, and these
+# two functions state it independently of the HIP code, as a plain numpy
+# permutation of the canonical arrays:
+#   * N is padded to N_pad = 64 * ceil(N / 64) with zero values and scales;
+#     T = N_pad / 64 column tiles, NB = K / 32 blocks;
+#   * values: tile t, block b is a 2048-byte chunk at (t * NB + b) * 2048, in
+#     two 1024-byte halves h (rows 0-15 and 16-31 of the block); inside half
+#     h, column c (0..63 within the tile) holds its 16 values, k ascending,
+#     at bytes c * 16 .. c * 16 + 15;
+#   * scales: tile t, block b is a 64-float row at (t * NB + b) * 64; the
+#     scale of column c = 16 g + i (i < 16, g < 4) sits at position 4 i + g.
+# ---------------------------------------------------------------------------
+
+def _padded(N: int) -> int:
+    return (N + 63) // 64 * 64
+
+
+def repack_ref(q: np.ndarray, s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Packed ``(values, scales)`` of the canonical ``q`` (K x N int8) and
+    ``s`` (K/32 x N fp32): ``values`` is ``K * N_pad`` int8, ``scales`` is
+    ``K/32 * N_pad`` fp32, both flat."""
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    K, N = q.shape
+    if K % BLOCK or s.shape != (K // BLOCK, N):
+        raise ValueError("shape mismatch")
+    NB, Np = K // BLOCK, _padded(N)
+    T = Np // 64
+    qp = np.zeros((K, Np), np.int8)
+    qp[:, :N] = q
+    sp = np.zeros((NB, Np), np.float32)
+    sp[:, :N] = s
+    # q index (k, n) = (32 b + 16 h + kk, 64 t + c)  ->  [t, b, h, c, kk]
+    v = qp.reshape(NB, 2, 16, T, 64).transpose(3, 0, 1, 4, 2)
+    # s index (b, n) = (b, 64 t + 16 g + i)  ->  [t, b, i, g]
+    w = sp.reshape(NB, T, 4, 16).transpose(1, 0, 3, 2)
+    return np.ascontiguousarray(v).ravel(), np.ascontiguousarray(w).ravel()
+
+
+def unpack_ref(values: np.ndarray, scales: np.ndarray, K: int, N: int
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """The inverse of repack_ref: canonical ``(q, s)`` of the first N columns."""
+    NB, Np = K // BLOCK, _padded(N)
+    T = Np // 64
+    v = np.asarray(values).view(np.int8)[: K * Np].reshape(T, NB, 2, 64, 16)
+    w = np.asarray(scales, np.float32)[: NB * Np].reshape(T, NB, 16, 4)
+    q = v.transpose(1, 2, 4, 0, 3).reshape(K, Np)
+    s = w.transpose(1, 0, 3, 2).reshape(NB, Np)
+    return np.ascontiguousarray(q[:, :N]), np.ascontiguousarray(s[:, :N])
 
 
 def view_rows(m: int, K: int) -> int:

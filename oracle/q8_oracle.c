@@ -445,3 +445,41 @@ void q8o_fold_bytes(int64_t m, int64_t K, int64_t N, int64_t wb,
   *weight = K * padded + 4 * (K / Q8O_BLOCK) * padded;
   *view_reads = (n_t / wb) * ((K + tile - 1) / tile) * m * tile * x_bytes;
 }
+
+/* ------------------------------------------------------------------------ */
+/* [LANE] enum Launch, variant Gemv: the projection's epilogue               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The fused epilogue of one product, over the listed columns: the pages'
+ * projection adds its bias to x.w (field `bias`), and the note on
+ * gemv_norm_epilogue folds the residual add into the projection's epilogue.
+ * Reading taken: bias first, then the residual, each added to the product in
+ * fp64 (exact here up to the one rounding of each sum):
+ *   z[r,j]     = y[r,j] + bias[n] + residual[r, n]
+ *   zbound[r,j] = bound[r,j] + |bias[n]| + |residual[r, n]|
+ * with n = cols[j] (or j when cols is NULL).  y and bound are m x ncols (a
+ * product's output from the functions above); bias has one value per column
+ * (NULL: none); residual is m rows of res_stride values (NULL: none).
+ */
+void q8o_epilogue(const double *y, const double *bound, int64_t m, int64_t ncols,
+                  const int64_t *cols, const float *bias, const float *residual,
+                  int64_t res_stride, double *z, double *zbound) {
+  for (int64_t r = 0; r < m; ++r) {
+    for (int64_t j = 0; j < ncols; ++j) {
+      const int64_t n = col_at(cols, j);
+      double v = y[r * ncols + j];
+      double b = bound[r * ncols + j];
+      if (bias) {
+        v += (double)bias[n];
+        b += fabs((double)bias[n]);
+      }
+      if (residual) {
+        v += (double)residual[r * res_stride + n];
+        b += fabs((double)residual[r * res_stride + n]);
+      }
+      z[r * ncols + j] = v;
+      zbound[r * ncols + j] = b;
+    }
+  }
+}

@@ -4,6 +4,7 @@ import numpy as np
 import torch
 
 import block_quantized_weight_02_amd as q8
+import oracle
 
 DEV = "cuda:0"
 
@@ -25,9 +26,18 @@ def pack(q: np.ndarray, s: np.ndarray):
 
 
 def quantize(x_bits: np.ndarray):
+    """The HIP quantizer's buffer of x, checked bit for bit against the
+    oracle's quantizer before any product reads it (so a product test that
+    starts from this buffer compares quantize-then-product end to end)."""
     m, K = x_bits.shape
     buf = empty_bytes(q8.q8_act_bytes(m, K))
     q8.q8_quantize_act(dev(x_bits.view(np.int16)), buf, m, K)
+    torch.cuda.synchronize()
+    xq, dx = act_host(buf, m, K)
+    rq, rd = oracle.quantize_act(x_bits)
+    np.testing.assert_array_equal(xq, rq, err_msg="HIP quantizer codes differ from the oracle's")
+    np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32),
+                                  err_msg="HIP quantizer scales differ from the oracle's")
     return buf
 
 

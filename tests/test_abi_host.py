@@ -273,3 +273,15 @@ def test_two_word_rules():
     expect(2, q8.q8_gemv_glu_default_plan, 1, 64, 8, TW)
     expect(2, q8.q8_gemv_parts, A, [q8.make_part(A, A, A, 64)], 1, 64, TW, S0)
     expect(3, q8.q8_gemm, None, A, A, A, 64, 64, 8, TW, S0)   # the GEMM takes it
+
+
+def test_stream_read_argument_errors():
+    expect(3, q8.q8_stream_read, None, 1024, 256, 8, 2, A, S0)
+    expect(4, q8.q8_stream_read, A + 4, 1024, 256, 8, 2, A, S0)
+    expect(1, q8.q8_stream_read, A, 1000, 256, 8, 2, A, S0)       # not whole 16 bytes
+    expect(1, q8.q8_stream_read, A, 0, 256, 8, 2, A, S0)
+    expect(1, q8.q8_stream_read, A, 1024, 0, 8, 2, A, S0)
+    expect(1, q8.q8_stream_read, A, 1024, 256, 17, 2, A, S0)
+    expect(1, q8.q8_stream_read, A, 1024, 256, 8, 3, A, S0)
+    msg = expect(1, q8.q8_stream_read, A, 1 << 33, 1, 8, 2, A, S0)  # an 8 GiB slice
+    assert "slice" in msg

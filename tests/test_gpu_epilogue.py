@@ -4,9 +4,9 @@ oracle, through the C ABI.
 What the epilogue computes is z = x.W + bias + residual per output, then y = z
 and/or z's quantized form per 32 columns (the pages' plan.rs, enum Launch,
 variant Gemv, fields `bias` and `quant`; the residual add of its
-`gemv_norm_epilogue` note).  The oracle gives x.W and its bound in fp64; the
-test adds bias and residual (plain additions) and quantizes with the oracle's
-own fp32-input quantizer.
+`gemv_norm_epilogue` note).  The oracle gives x.W and its bound in fp64 and
+adds bias and residual (its epilogue), and quantizes with its own fp32-input
+quantizer.
 
 The bar:
 * exact cases (inputs whose sums are exact in fp32 in any order): y, the
@@ -63,24 +63,15 @@ def run_fused(xin, Wq, Ws, m, K, N, act, bias=None, residual=None, quant=False,
     return yh, None, None
 
 
-def reference(x, q, s, act, xbuf=None, bias=None, residual=None):
-    """(z, bound) over the N real columns, fp64: the oracle's product plus
-    bias and residual."""
-    m, K = x.shape
-    N = q.shape[1]
+def reference(x, q, s, act, xbuf=None, bias=None, residual=None, cols=None):
+    """(z, bound) over the N real columns (or the listed ones), fp64: the
+    oracle's product from its own quantizer (Q8_0) and its epilogue."""
     if act == BF16:
-        y, bnd = oracle.gemv_bf16(x, q, s)
+        y, bnd = oracle.gemv_bf16(x, q, s, cols)
     else:
-        xq, dx = g.act_host(xbuf, m, K)
-        y, bnd = oracle.gemv_q8(xq, dx, q, s)
-    z = y.copy()
-    if bias is not None:
-        z += bias[None, :N].astype(np.float64)
-        bnd = bnd + np.abs(bias[None, :N]).astype(np.float64)
-    if residual is not None:
-        z += residual[:, :N].astype(np.float64)
-        bnd = bnd + np.abs(residual[:, :N]).astype(np.float64)
-    return z, bnd
+        xq, dx = oracle.quantize_act(x)
+        y, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
+    return oracle.epilogue(y, bnd, bias, residual, cols)
 
 
 def check_y(y, z, bnd, N, what):
@@ -277,19 +268,6 @@ def test_full_size_fused(name):
     xbuf = g.quantize(x) if act == Q8 else None
     xin = xbuf if act == Q8 else g.dev(x.view(np.int16))
     y, codes, scales = run_fused(xin, Wq, Ws, m, K, N, act, bias, res, quant=True)
-    # whole 32-column blocks, sampled when the oracle's full product is slow
-    if m * K * N > 64 * 2 ** 20:
-        blocks = np.random.default_rng(w.seed_x + 9).choice(N // 32, size=48, replace=False)
-        cols = np.sort((blocks[:, None] * 32 + np.arange(32)[None, :]).ravel())
-    else:
-        cols = np.arange(N)
-    if act == BF16:
-        yr, bnd = oracle.gemv_bf16(x, q, s, cols)
-    else:
-        xq, dx = g.act_host(xbuf, m, K)
-        yr, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
-    z = yr + bias[cols][None, :].astype(np.float64) + res[:, cols].astype(np.float64)
-    bnd = bnd + np.abs(bias[cols])[None, :] + np.abs(res[:, cols])
-    check_y(y[:, cols], z, bnd, len(cols), name)
-    cb = cols.reshape(-1, 32)[:, 0] // 32
-    check_quant(codes[:, cols], scales[:, cb], z, bnd, len(cols), name)
+    z, bnd = reference(x, q, s, act, xbuf, bias, res)
+    check_y(y, z, bnd, N, name)
+    check_quant(codes, scales, z, bnd, N, name)

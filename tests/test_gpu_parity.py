@@ -75,6 +75,28 @@ def test_repack_unpack_round_trip(K, N):
     np.testing.assert_array_equal(sp, np.sort(np.concatenate([s.ravel(), np.zeros((K // 32) * (Npad - N), np.float32)])))
 
 
+@pytest.mark.parametrize("name", ["q8act_m32_k5120_n40", "decode_k4096_n14336",
+                                  "ffn_down_k14336_n4096"])
+def test_repack_matches_layout_reference(name):
+    """q8_repack's bytes are the oracle's numpy statement of the packed layout,
+    byte for byte (values) and bit for bit (scales)."""
+    w = inputs.WORKLOADS[name]
+    _, q, s = inputs.generate(w)
+    Wq, Ws = g.pack(q, s)
+    v, sc = oracle.repack_ref(q, s)
+    np.testing.assert_array_equal(Wq.cpu().numpy()[: v.size].view(np.int8), v)
+    np.testing.assert_array_equal(Ws.cpu().numpy()[: sc.size].view(np.uint32), sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("K,N", [(32, 1), (64, 130), (1056, 200), (160, 257)])
+def test_repack_matches_layout_reference_small(K, N):
+    _, q, s = inputs.random_case(1, K, N, seed=K * 3 + N)
+    Wq, Ws = g.pack(q, s)
+    v, sc = oracle.repack_ref(q, s)
+    np.testing.assert_array_equal(Wq.cpu().numpy()[: v.size].view(np.int8), v)
+    np.testing.assert_array_equal(Ws.cpu().numpy()[: sc.size].view(np.uint32), sc.view(np.uint32))
+
+
 # ------------------------------------------------------------------------------
 # activation quantize: bit-exact
 # ------------------------------------------------------------------------------
@@ -112,7 +134,7 @@ def test_block_dots_bit_exact(m, K, N):
     x, q, _ = inputs.random_case(m, K, N, seed=m * 7 + N)
     Wq, _ = g.pack(q, np.ones((K // 32, N), np.float32))
     buf = g.quantize(x)
-    xq, _ = g.act_host(buf, m, K)
+    xq, _ = oracle.quantize_act(x)
     D = g.block_dots(buf, Wq, m, K, N)
     ref = oracle.block_dots(xq, q)
     np.testing.assert_array_equal(D[:, :, :N].astype(np.int64), ref)
@@ -151,8 +173,8 @@ def test_gemv_bf16_small(m, K, N):
 @pytest.mark.parametrize("m,K,N", SMALL)
 def test_gemv_q8_small(m, K, N):
     x, q, s = inputs.random_case(m, K, N, seed=2000 + 3 * m + K + N)
-    y, buf = run_q8(x, q, s)
-    xq, dx = g.act_host(buf, m, K)
+    y, _ = run_q8(x, q, s)
+    xq, dx = oracle.quantize_act(x)
     ref, bnd = oracle.gemv_q8(xq, dx, q, s)
     assert_close(y[:, :N], ref, bnd, f"q8 m={m} K={K} N={N}")
     assert (y[:, N:].view(np.uint32) == 0).all()
@@ -199,7 +221,7 @@ def test_every_plan(act, m):
         ref, bnd = oracle.gemv_bf16(x, q, s)
     else:
         xin = g.quantize(x)
-        xq, dx = g.act_host(xin, m, K)
+        xq, dx = oracle.quantize_act(x)
         ref, bnd = oracle.gemv_q8(xq, dx, q, s)
         Dref = oracle.block_dots(xq, q)
     ran = 0
@@ -232,30 +254,31 @@ def _sample_cols(N, n=384, seed=0):
 
 @pytest.mark.parametrize("name", [n for n, w in inputs.WORKLOADS.items() if w.m <= q8.Q8_MAX_ROWS])
 def test_workload_full_size(name):
+    """Every configuration at its full size, in the launch configuration the
+    benchmark times (the default plan): every output column against the
+    oracle, and in Q8_0 mode every int32 block dot bit for bit."""
     w = inputs.WORKLOADS[name]
     x, q, s = inputs.generate(w)
     m, K, N = w.m, w.K, w.N
     Wq, Ws = g.pack(q, s)
-    cols = None if m * K * N <= 64 * 2 ** 20 else _sample_cols(N)
     if w.act == "bf16":
         y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16)
-        ref, bnd = oracle.gemv_bf16(x, q, s, cols)
+        ref, bnd = oracle.gemv_bf16(x, q, s)
     else:
-        buf = g.quantize(x)
-        xq, dx = g.act_host(buf, m, K)
-        rq, rd = oracle.quantize_act(x)
-        np.testing.assert_array_equal(xq, rq)
-        np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32))
+        buf = g.quantize(x)                       # bit-equal to the oracle's
+        xq, dx = oracle.quantize_act(x)
         y = g.gemv(buf, Wq, Ws, m, K, N, Q8)
-        ref, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
+        ref, bnd = oracle.gemv_q8(xq, dx, q, s)
         D = g.block_dots(buf, Wq, m, K, N)
-        dcols = np.arange(N) if cols is None else cols
-        np.testing.assert_array_equal(D[:, :, dcols].astype(np.int64),
-                                      oracle.block_dots(xq, q, dcols))
+        step = 4096                               # the oracle's int64 dots, a slab at a time
+        for c0 in range(0, N, step):
+            cols = np.arange(c0, min(N, c0 + step))
+            np.testing.assert_array_equal(D[:, :, c0:c0 + len(cols)].astype(np.int64),
+                                          oracle.block_dots(xq, q, cols),
+                                          err_msg=f"{name}: dots of columns {c0}..")
         assert (D[:, :, N:] == 0).all()
         del D
-    got = y[:, :N] if cols is None else y[:, cols]
-    assert_close(got, ref, bnd, name)
+    assert_close(y[:, :N], ref, bnd, name)
     assert (y[:, N:].view(np.uint32) == 0).all()
     assert np.isfinite(y).all()
 

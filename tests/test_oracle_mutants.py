@@ -10,6 +10,7 @@ import inspect
 import itertools
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -80,6 +81,12 @@ MUTANTS = [
     ("two-word bound drops the second word",
      "dot_abs += fabs(((double)hi[r * K + k] + (double)lo[r * K + k] / 128.0) * (double)w);",
      "dot_abs += fabs((double)hi[r * K + k] * (double)w);"),
+    ("epilogue takes the neighbouring column's bias",
+     "v += (double)bias[n];", "v += (double)bias[(n + 1) % ncols];"),
+    ("epilogue reads the residual with the output's row stride",
+     "v += (double)residual[r * res_stride + n];", "v += (double)residual[r * ncols + n];"),
+    ("epilogue bound drops the residual",
+     "b += fabs((double)residual[r * res_stride + n]);", "b += 0.0;"),
     ("view rows drop the K tail",
      "return m * ((K + chunk - 1) / chunk) * Q8O_BLOCK;", "return m * (K / chunk) * Q8O_BLOCK;"),
     ("byte model counts 2-byte scales",
@@ -141,3 +148,64 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new):
     finally:
         oracle._lib = prev
     assert failed, f"no pin caught: {label}"
+
+
+# Planted mistakes in the numpy packed-layout reference (oracle.repack_ref):
+# each replaces the function with a plausible wrong permutation, and some pin
+# of the layout must then fail.
+def _swap_halves(q, s):
+    K, N = q.shape
+    NB, Np = K // 32, (N + 63) // 64 * 64
+    qp = np.zeros((K, Np), np.int8)
+    qp[:, :N] = q
+    v = qp.reshape(NB, 2, 16, Np // 64, 64).transpose(3, 0, 1, 4, 2)[:, :, ::-1]
+    return np.ascontiguousarray(v).ravel(), _REPACK(q, s)[1]
+
+
+def _block_major(q, s):
+    K, N = q.shape
+    NB, Np = K // 32, (N + 63) // 64 * 64
+    qp = np.zeros((K, Np), np.int8)
+    qp[:, :N] = q
+    v = qp.reshape(NB, 2, 16, Np // 64, 64).transpose(0, 3, 1, 4, 2)
+    return np.ascontiguousarray(v).ravel(), _REPACK(q, s)[1]
+
+
+def _scales_in_column_order(q, s):
+    K, N = q.shape
+    NB, Np = K // 32, (N + 63) // 64 * 64
+    sp = np.zeros((NB, Np), np.float32)
+    sp[:, :N] = s
+    w = sp.reshape(NB, Np // 64, 64).transpose(1, 0, 2)
+    return _REPACK(q, s)[0], np.ascontiguousarray(w).ravel()
+
+
+def _k_reversed(q, s):
+    K, N = q.shape
+    NB, Np = K // 32, (N + 63) // 64 * 64
+    qp = np.zeros((K, Np), np.int8)
+    qp[:, :N] = q
+    v = qp.reshape(NB, 2, 16, Np // 64, 64).transpose(3, 0, 1, 4, 2)[..., ::-1]
+    return np.ascontiguousarray(v).ravel(), _REPACK(q, s)[1]
+
+
+_REPACK = oracle.repack_ref
+LAYOUT_MUTANTS = [("halves swapped", _swap_halves), ("block-major chunks", _block_major),
+                  ("scales in column order", _scales_in_column_order),
+                  ("k reversed inside a half", _k_reversed)]
+
+
+@pytest.mark.parametrize("label,fn", LAYOUT_MUTANTS, ids=[m[0] for m in LAYOUT_MUTANTS])
+def test_planted_layout_mistake_is_caught(monkeypatch, label, fn):
+    monkeypatch.setattr(oracle, "repack_ref", fn)
+    failed = [name for name, f, kw in _pin_calls() if "packed_layout" in name
+              and not _passes(f, kw)]
+    assert failed, f"no layout pin caught: {label}"
+
+
+def _passes(fn, kw):
+    try:
+        fn(**kw)
+        return True
+    except Exception:
+        return False

@@ -523,3 +523,105 @@ def test_gated_pair_brute_force(m, K, N, seed):
     cols = [N - 1, 0, 2]
     sub, _, _, _, _ = oracle.gemv_glu_bf16(x, qg, sg, qu, su, bg, bu, cols)
     np.testing.assert_array_equal(sub, out[:, cols])
+
+
+# --------------------------------------------------------------------------
+# the library's packed layout (from_q8.rs, enum Q8Part: the host repacks the
+# checkpoint's blocks; the device placement is the library's), pinned to
+# hand-worked byte offsets and to its invariants
+# --------------------------------------------------------------------------
+
+def test_packed_layout_hand_worked_offsets():
+    g = json.load(open(os.path.join(GOLDEN, "packed_layout.json")))
+    K, N = g["K"], g["N"]
+    for e in g["values"]:
+        q = np.zeros((K, N), np.int8)
+        q[e["k"], e["n"]] = -77
+        v, w = oracle.repack_ref(q, np.zeros((K // 32, N), np.float32))
+        assert v.size == g["values_bytes"] and w.size == g["scales_floats"]
+        np.testing.assert_array_equal(np.flatnonzero(v), [e["offset"]], err_msg=e["work"])
+        assert v[e["offset"]] == -77
+        assert not w.any()
+    for e in g["scales"]:
+        s = np.zeros((K // 32, N), np.float32)
+        s[e["b"], e["n"]] = 0.375
+        v, w = oracle.repack_ref(np.zeros((K, N), np.int8), s)
+        np.testing.assert_array_equal(np.flatnonzero(w), [e["index"]], err_msg=e["work"])
+        assert w[e["index"]] == np.float32(0.375) and not v.any()
+
+
+@pytest.mark.parametrize("K,N,seed", [(32, 1, 1), (64, 130, 2), (1056, 200, 3), (96, 64, 4)])
+def test_packed_layout_round_trip_and_pad(K, N, seed):
+    _, q, s = inputs.random_case(1, K, N, seed)
+    v, w = oracle.repack_ref(q, s)
+    Np = (N + 63) // 64 * 64
+    assert v.dtype == np.int8 and v.size == K * Np and w.size == (K // 32) * Np
+    q2, s2 = oracle.unpack_ref(v, w, K, N)
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(s2.view(np.uint32), s.view(np.uint32))
+    # the values are permuted, never changed; the pad adds only zeros
+    np.testing.assert_array_equal(np.sort(v), np.sort(np.concatenate(
+        [q.ravel(), np.zeros(K * (Np - N), np.int8)])))
+    # one tile over all K is one contiguous run of K*64 bytes holding exactly
+    # its 64 columns' values
+    NB = K // 32
+    for t in range(Np // 64):
+        run = np.sort(v[t * NB * 2048:(t + 1) * NB * 2048])
+        cols = np.zeros((K, 64), np.int8)
+        hi = min(N, 64 * t + 64)
+        cols[:, :hi - 64 * t] = q[:, 64 * t:hi]
+        np.testing.assert_array_equal(run, np.sort(cols.ravel()))
+
+
+def test_packed_layout_column_block_is_sixteen_bytes_in_k_order():
+    # column n's values of block b are two 16-byte runs (k ascending), the
+    # second 1024 bytes after the first
+    K, N = 96, 70
+    q = np.zeros((K, N), np.int8)
+    q[32:64, 66] = np.arange(1, 33, dtype=np.int8)
+    v, _ = oracle.repack_ref(q, np.zeros((K // 32, N), np.float32))
+    base = (1 * (K // 32) + 1) * 2048 + 2 * 16     # t=1, b=1, c=2
+    np.testing.assert_array_equal(v[base:base + 16], np.arange(1, 17))
+    np.testing.assert_array_equal(v[base + 1024:base + 1040], np.arange(17, 33))
+    assert np.count_nonzero(v) == 32
+
+
+# --------------------------------------------------------------------------
+# plan.rs, enum Launch, variant Gemv: bias, then the residual, after x.w
+# --------------------------------------------------------------------------
+
+def test_epilogue_closed_forms():
+    m, n = 3, 5
+    y = np.zeros((m, n))
+    bnd = np.zeros((m, n))
+    bias = np.array([1.0, -2.0, 0.5, 8.0, -0.25, 99.0], np.float32)    # one extra column
+    res = (np.arange(m)[:, None] * 100 + np.arange(7)[None, :]).astype(np.float32)
+    z, zb = oracle.epilogue(y, bnd, bias, res)
+    np.testing.assert_array_equal(z, bias[None, :n] + res[:, :n])
+    np.testing.assert_array_equal(zb, np.abs(bias[None, :n]) + np.abs(res[:, :n]))
+    # no bias and no residual: the product unchanged
+    y2 = np.random.default_rng(90).standard_normal((m, n))
+    z2, b2 = oracle.epilogue(y2, np.abs(y2), None, None)
+    np.testing.assert_array_equal(z2, y2)
+    np.testing.assert_array_equal(b2, np.abs(y2))
+    # listed columns pick their own bias and residual columns
+    cols = [6, 0, 3]
+    z3, _ = oracle.epilogue(np.zeros((m, 3)), np.zeros((m, 3)), np.zeros(7, np.float32), res, cols)
+    np.testing.assert_array_equal(z3, res[:, cols])
+    z4, _ = oracle.epilogue(np.zeros((m, 3)), np.zeros((m, 3)), bias, None, [5, 1, 2])
+    np.testing.assert_array_equal(z4, np.broadcast_to(bias[[5, 1, 2]], (m, 3)))
+
+
+@pytest.mark.parametrize("m,K,N,seed", [(2, 96, 7, 93), (3, 1056, 70, 94)])
+def test_epilogue_brute_force(m, K, N, seed):
+    x, q, s = inputs.random_case(m, K, N, seed)
+    Np = (N + 63) // 64 * 64
+    bias = inputs.gen_bias(N, seed)
+    res = inputs.gen_residual(m, Np, seed)
+    y, bnd = oracle.gemv_bf16(x, q, s)
+    z, zb = oracle.epilogue(y, bnd, bias, res)
+    xd = xval(x)
+    ref = xd @ dense_w(q, s) + bias.astype(np.float64)[None, :] + res[:, :N].astype(np.float64)
+    babs = np.abs(xd) @ np.abs(dense_w(q, s)) + np.abs(bias)[None, :] + np.abs(res[:, :N])
+    assert np.all(np.abs(z - ref) <= 1e-13 * babs + 1e-300)
+    np.testing.assert_allclose(zb, babs, rtol=1e-13)

@@ -119,6 +119,8 @@ _SIGS = {
     "q8_last_error": (ctypes.c_char_p, []),
     "q8_release_workspaces": (_int, []),
     "q8_stream_read": (_int, [_p, _sz, _int, _int, _int, _p, _p]),
+    "q8_gemv_noalloc": (_int, [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p]),
+    "q8_noalloc_scratch_bytes": (_sz, []),
     "q8_layout_version": (_int, []),
 }
 
@@ -395,3 +397,11 @@ def q8_stream_read(src, nbytes, workgroups, waves, depth, sink, stream=None) -> 
     _check(lib().q8_stream_read(_addr(src), nbytes, workgroups, waves, depth, _addr(sink),
                                 _stream(stream)))
 
+
+def q8_gemv_noalloc(x, W_q8, W_q8_scale, y, m, K, N, act_fmt, stream=None) -> None:
+    _check(lib().q8_gemv_noalloc(_addr(x), _addr(W_q8), _addr(W_q8_scale), _addr(y), m, K, N,
+                                 act_fmt, _stream(stream)))
+
+
+def q8_noalloc_scratch_bytes() -> int:
+    return int(lib().q8_noalloc_scratch_bytes())

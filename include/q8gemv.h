@@ -430,6 +430,33 @@ int q8_layout_version(void);
 int q8_stream_read(const void *src, size_t bytes, int workgroups, int waves, int depth,
                    void *sink, hipStream_t stream);
 
+/* ---- the product without allocation ------------------------------------------ */
+
+/* Bytes of the device scratch array q8_gemv_noalloc takes its split-K
+ * workspace from (one array per GPU, held until the process ends). */
+#define Q8_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * q8_gemv_noalloc: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Computes exactly what q8_gemv computes (same default plan, same kernels,
+ * bit-identical y), but its split-K workspace is a fixed device array of
+ * Q8_NOALLOC_SCRATCH_BYTES per GPU inside the library instead of an
+ * allocation: the call allocates nothing and frees nothing.  Arguments,
+ * layouts and errors as q8_gemv; in addition Q8_ERR_WORKSPACE when the shape's
+ * plan needs more workspace than the array holds
+ * (q8_gemv_workspace_bytes(m, K, N, act_fmt) > Q8_NOALLOC_SCRATCH_BYTES).
+ * The first call on each GPU looks up that GPU's copy of the array and clears
+ * it with a kernel on `stream`.  Every call on one GPU shares its array and
+ * leaves its counters zero for the next: calls that overlap on one GPU
+ * (unordered streams or threads) race.
+ */
+int q8_gemv_noalloc(const void *x, const int8_t *W_q8, const float *W_q8_scale,
+                    float *y, int64_t m, int64_t K, int64_t N, int act_fmt,
+                    hipStream_t stream);
+/* Q8_NOALLOC_SCRATCH_BYTES, as the library was built. */
+size_t q8_noalloc_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -198,6 +198,27 @@ def _hold_cycles_per_ms():
     return _HOLD["cycles_per_ms"]
 
 
+PREHEAT_MS = 100.0
+
+
+def preheat(fn, ms=PREHEAT_MS):
+    """Untimed launches of `fn` for about `ms` milliseconds of host time before
+    a measurement: an idle GPU runs its first launches slower (measured on
+    MI355X: the first 20-launch loop of a process 13.2-13.7 us per launch of
+    the m=1 product, every later one 11.5-11.7 us, and 11.5-11.7 us for the
+    first one after 50 ms of launches), and a decode loop keeps it busy."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < ms * 1e-3:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
 def time_loop(fn, steps, info=None):
     """Milliseconds per step of exactly `steps` steps run back to back on the
     launch stream.
@@ -241,6 +262,7 @@ def measure(w, steps, warmup, rotate=True):
     b = algorithmic_bytes(w)
     log(f"[bench] {w.name}: m={w.m} K={w.K} N={w.N} act={w.act} copies={st.copies} "
         f"plan={st.plan} bytes/step={b['total']}")
+    preheat(st.gemv_only)
     for i in range(warmup):
         st.step(i)
     torch.cuda.synchronize()
@@ -261,6 +283,7 @@ def measure(w, steps, warmup, rotate=True):
         "macs_per_s": w.m * weights / (ms * 1e-3),
         "kernel_us_mean": gemv_ms * 1e3,
         "launches_timed": steps, "back_to_back": info["back_to_back"],
+        "preheat_ms": PREHEAT_MS,
         "bytes": b, "copies": st.copies, "wall_s": wall,
         "plan": {"kernel": st.plan.kernel, "rows": st.plan.rows,
                  "split_k": st.plan.split_k, "waves": st.plan.waves, "kslices": st.plan.kslices},
@@ -305,12 +328,28 @@ def read_ceiling(torch, nbytes, steps):
                 ms = time_loop(call, steps)
                 rows.append({"workgroups": wgs, "waves": waves, "depth": depth,
                              "us": ms * 1e3, "gbs": n / (ms * 1e-3) / 1e9})
+    # the sweep's maximum is biased upward by run-to-run noise: the five
+    # fastest shapes are timed three more times and ranked by their median
+    top = sorted(rows, key=lambda r: -r["gbs"])[:5]
+    for r in top:
+        def call(i, r=r):
+            rc = lib.q8_stream_read(base + offs[i % nwin], n, r["workgroups"], r["waves"],
+                                    r["depth"], sink_p, sp)
+            if rc:
+                raise RuntimeError(q8.q8_last_error())
+        reps = [r["us"]] + [time_loop(call, steps) * 1e3 for _ in range(3)]
+        r["us_repeats"] = reps
+        r["us_median"] = float(np.median(reps))
+        r["gbs_median"] = n / (r["us_median"] * 1e-6) / 1e9
     del buf, sink
     torch.cuda.empty_cache()
-    best = max(rows, key=lambda r: r["gbs"])
+    best = max(top, key=lambda r: r["gbs_median"])
+    best = dict(best, us=best["us_median"], gbs=best["gbs_median"])
+    same = [r for r in rows if (r["workgroups"], r["waves"], r["depth"]) == (224, 8, 4)]
     log(f"[bench] read ceiling over {n} B: {best['us']:.2f} us, {best['gbs']:.0f} GB/s "
         f"({best['workgroups']} x {best['waves']} waves, depth {best['depth']})")
-    return {"bytes": n, "launches_per_shape": steps, "best": best, "sweep": rows}
+    return {"bytes": n, "launches_per_shape": steps, "best": best,
+            "product_grid_shape": same[0] if same else None, "sweep": rows}
 
 
 def measure_fused(w, steps, warmup, rotate=True):

@@ -131,6 +131,10 @@ size_t act_scales_offset_of(int act_fmt, int64_t m, int64_t K) {
   return act_scales_offset(act_fmt == Q8_ACT_Q8_0_TWO_WORDS ? 2 * m : m, K);
 }
 
+// Most K splits of a plan (the splits are the launch grid's second
+// dimension).
+constexpr int kMaxSplits = 65535;
+
 // LDS per workgroup kept free for the kernels' static shared variables.
 constexpr size_t kStaticLdsReserve = 1024;
 
@@ -294,9 +298,9 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
   if (p->rows < m || p->rows > Q8_MAX_ROWS || (p->rows & (p->rows - 1)) != 0)
     return fail(Q8_ERR_PLAN, "plan rows = %d: need a power of two in [m = %lld, %d]",
                 p->rows, (long long)m, Q8_MAX_ROWS);
-  if (p->split_k < 1 || p->split_k > NB)
-    return fail(Q8_ERR_PLAN, "plan split_k = %d: need 1 <= split_k <= K/32 = %lld",
-                p->split_k, (long long)NB);
+  if (p->split_k < 1 || p->split_k > NB || p->split_k > kMaxSplits)
+    return fail(Q8_ERR_PLAN, "plan split_k = %d: need 1 <= split_k <= min(K/32 = %lld, %d)",
+                p->split_k, (long long)NB, kMaxSplits);
   if (!q8::gemv_instantiated(p->kernel, p->rows, act, dots, p->waves, p->kslices))
     return fail(Q8_ERR_PLAN,
                 "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d kslices=%d",

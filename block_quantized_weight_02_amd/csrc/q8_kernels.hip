@@ -143,10 +143,12 @@ quantize_act_two_words_kernel(const uint16_t *__restrict__ x, int8_t *__restrict
 // the product: shared pieces
 // ---------------------------------------------------------------------------
 
-// The workgroup's row range of blocks [b_lo, b_hi) of split s of S.
-__device__ __forceinline__ void split_range(int NB, int s, int S, int &b_lo, int &b_hi) {
-  b_lo = (int)(((long long)NB * s) / S);
-  b_hi = (int)(((long long)NB * (s + 1)) / S);
+// The workgroup's range of blocks [b_lo, b_hi) of split s: NB = S*q + r
+// blocks, the first r splits one block longer (q and r come from the host,
+// so a workgroup starts its stream without an integer division).
+__device__ __forceinline__ void split_range(int s, int q, int r, int &b_lo, int &b_hi) {
+  b_lo = s * q + min(s, r);
+  b_hi = b_lo + q + (s < r ? 1 : 0);
 }
 
 // SiLU, g * sigmoid(g), in fp32 (the gate of the pages' GemvGlu launch).
@@ -550,13 +552,14 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
                  float *__restrict__ partial, unsigned *__restrict__ counters,
                  int32_t *__restrict__ dots, int m, int K, int NB, int Npad,
-                 int S, unsigned act_scale_off, Epi ep) {
+                 int S, int split_q, int split_r, unsigned act_scale_off, Epi ep) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // unit tv: a tile of the product, of a gated pair's weight (the pair's two
-  // weights are adjacent units), or of one part of a parts launch
-  const int tv = blockIdx.x / S;
-  const int s = blockIdx.x - tv * S;
+  // weights are adjacent units), or of one part of a parts launch; the grid
+  // is units x splits
+  const int tv = blockIdx.x;
+  const int s = blockIdx.y;
   const int wsel = PAIR ? (tv & 1) : 0;
   int t = PAIR ? (tv >> 1) : tv;
   const int8_t *wbase = wsel ? ep.wq_u : wq;
@@ -564,7 +567,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   TileOut out{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t};
   Epi uep = ep;
   if constexpr (PARTS) {
-    const PartUnit u = part_unit(ep, tv, (int)(gridDim.x / S));
+    const PartUnit u = part_unit(ep, tv, (int)gridDim.x);
     t = u.t;
     wbase = u.wq;
     sbase = u.wsc;
@@ -572,7 +575,7 @@ gemv_valu_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     uep = u.ep;
   }
   int b_lo, b_hi;
-  split_range(NB, s, S, b_lo, b_hi);
+  split_range(s, split_q, split_r, b_lo, b_hi);
 
   // the tile's values and scales; each lane adds its own byte offset
   ValuSrc<MR> src;
@@ -922,7 +925,8 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
                       const float *__restrict__ wsc, float *__restrict__ y,
                       float *__restrict__ partial, unsigned *__restrict__ counters,
                       int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
-                      int S, int G, int nblk_max, unsigned act_scale_off, Epi ep) {
+                      int S, int split_q, int split_r, int G, int nblk_max,
+                      unsigned act_scale_off, Epi ep) {
   constexpr int W = 4 * KW * P;
   constexpr int RG = MR / 16;
   constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;   // one row of one block in LDS
@@ -934,10 +938,10 @@ gemv_mfma_cols_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq
   const int g = wave & 3;
   const int kw = (wave >> 2) % KW;
   const int slot = wave / (4 * KW);
-  const int s = blockIdx.x % S;
-  const int jwg = blockIdx.x / S;
+  const int s = blockIdx.y;
+  const int jwg = blockIdx.x;
   int b_lo, b_hi;
-  split_range(NB, s, S, b_lo, b_hi);
+  split_range(s, split_q, split_r, b_lo, b_hi);
   const int nblk = b_hi - b_lo;
   const int col_in_tile = 16 * g + li;
   // lane's bytes in a chunk: half j/2, column 16g+i, k offset 8*(j%2)
@@ -1153,8 +1157,8 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                  const float *__restrict__ wsc, float *__restrict__ y,
                  float *__restrict__ partial, unsigned *__restrict__ counters,
                  int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T,
-                 int S, int G, int nblk_max, int red_on_stage, unsigned act_scale_off,
-                 Epi ep) {
+                 int S, int split_q, int split_r, int G, int nblk_max, int red_on_stage,
+                 unsigned act_scale_off, Epi ep) {
   constexpr int RG = MR / 16;
   constexpr int kRowBytes = (ACT == kActBf16) ? 64 : 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -1162,10 +1166,10 @@ gemv_mfma_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lj = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int s = blockIdx.x % S;
-  const int jwg = blockIdx.x / S;
+  const int s = blockIdx.y;
+  const int jwg = blockIdx.x;
   int b_lo, b_hi;
-  split_range(NB, s, S, b_lo, b_hi);
+  split_range(s, split_q, split_r, b_lo, b_hi);
   const int nblk = b_hi - b_lo;
   // lane's bytes in a chunk: half j/2, column i (+16g), k offset 8*(j%2)
   const size_t lane_off = (size_t)(lj >> 1) * kHalfBytes + li * 16 + (lj & 1) * 8;
@@ -1382,10 +1386,10 @@ size_t cols_lds_bytes_of(int rows, int act, int kslices, int NB, int S) {
 
 template <int MR, int ACT, bool DOTS, int W, bool PAIR, bool PARTS>
 hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.tiles() * a.split_k));
+  const dim3 grid((unsigned)a.tiles(), (unsigned)a.split_k);
   gemv_valu_kernel<MR, ACT, DOTS, W, PAIR, PARTS><<<grid, dim3(64 * W), 0, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB,
-      a.Npad, a.split_k, a.act_scale_off, a.ep);
+      a.Npad, a.split_k, a.NB / a.split_k, a.NB % a.split_k, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
@@ -1468,9 +1472,10 @@ hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
     lds = lds_sep;
   }
   (void)hipGetLastError();
-  kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
+  kern<<<dim3((unsigned)G, (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, units,
-      a.split_k, G, nblk_max, red_on_stage, a.act_scale_off, a.ep);
+      a.split_k, a.NB / a.split_k, a.NB % a.split_k, G, nblk_max, red_on_stage,
+      a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 
@@ -1496,9 +1501,9 @@ hipError_t launch_cols_k(const GemvArgs &a, hipStream_t stream) {
   const int want = (a.tiles() + P - 1) / P;
   const int G = balanced_grid(resident_workgroups(kern, 64 * W, lds) / a.split_k, want);
   (void)hipGetLastError();
-  kern<<<dim3((unsigned)(G * a.split_k)), dim3(64 * W), lds, stream>>>(
+  kern<<<dim3((unsigned)G, (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.tiles(),
-      a.split_k, G, nblk_max, a.act_scale_off, a.ep);
+      a.split_k, a.NB / a.split_k, a.NB % a.split_k, G, nblk_max, a.act_scale_off, a.ep);
   return hipGetLastError();
 }
 

@@ -84,6 +84,8 @@ def kernel_name(plan: dict, w) -> str:
         return f"gemv_valu_kernel<{r}, {act}, false, {wv}, false, false>"
     if plan["kernel"] == 1:
         return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false, false>"
+    if plan["kernel"] == 5:
+        return f"gemv_mfma32w_kernel<{wv}, false>"
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
 
 
@@ -720,11 +722,15 @@ def summarize_kernel_trace(path):
             t0, t1 = row.get("Start_Timestamp"), row.get("End_Timestamp")
             if not name or t0 is None or t1 is None:
                 continue
-            durs.setdefault(name, []).append((int(t1) - int(t0)) / 1e3)
+            # one kernel serves several shapes: the launch's grid tells them apart
+            grid = "x".join(str(int(row.get(f"Grid_Size_{a}", 1) or 1)) for a in "XYZ")
+            key = (name, grid, int(row.get("Workgroup_Size_X", 0) or 0))
+            durs.setdefault(key, []).append((int(t1) - int(t0)) / 1e3)
     out = []
-    for name, d in durs.items():
+    for (name, grid, wg), d in durs.items():
         a = np.array(d)
-        out.append({"kernel": name, "dispatches": int(a.size), "total_us": float(a.sum()),
+        out.append({"kernel": name, "grid_threads": grid, "workgroup": wg,
+                    "dispatches": int(a.size), "total_us": float(a.sum()),
                     "mean_us": float(a.mean()), "median_us": float(np.median(a)),
                     "p10_us": float(np.percentile(a, 10)), "p90_us": float(np.percentile(a, 90))})
     out.sort(key=lambda r: -r["total_us"])
@@ -743,6 +749,8 @@ def main():
     ap.add_argument("--no-fused", action="store_true", help="skip the fused-epilogue lines")
     ap.add_argument("--no-prefill", action="store_true", help="skip the many-row (prefill) lines")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the read-ceiling sweep")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the cache-hot headline and the 1 GiB copy")
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy (for profiler counter calibration)")
@@ -823,7 +831,7 @@ def main():
         context["read_ceiling"] = read_ceiling(torch, head["bytes"]["total"], 200)
         best = context["read_ceiling"]["best"]["gbs"]
         context["product_frac_of_read_ceiling"] = head["kernel_gbs"] / best
-    if not args.no_rows:
+    if not args.no_rows and not args.no_context:
         context.update(bandwidth_context(torch, w, 200))
         log(f"[bench] context: one weight copy {context['mall_hot_us']:.2f} us; 1 GiB copy "
             f"{context['copy_1gib_gbs_read_plus_write']:.0f} GB/s read+write")

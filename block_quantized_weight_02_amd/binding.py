@@ -23,6 +23,9 @@ Q8_ACT_Q8_0_TWO_WORDS = 2
 Q8_KERNEL_VALU = 0
 Q8_KERNEL_MFMA = 1
 Q8_KERNEL_MFMA_COLS = 2
+Q8_KERNEL_MFMA32 = 3
+Q8_KERNEL_MFMA32_DIRECT = 4
+Q8_KERNEL_MFMA32_TILE = 5
 Q8_MAX_ROWS = 32
 Q8_MAX_GEMM_ROWS = 8192
 Q8_MAX_PARTS = 4
@@ -75,6 +78,7 @@ _SIGS = {
     "q8_packed_values_bytes": (_sz, [_i64, _i64]),
     "q8_packed_scales_bytes": (_sz, [_i64, _i64]),
     "q8_act_scales_offset": (_sz, [_i64, _i64]),
+    "q8_act_view_offset": (_sz, [_i64, _i64]),
     "q8_act_bytes": (_sz, [_i64, _i64]),
     "q8_act_two_words_scales_offset": (_sz, [_i64, _i64]),
     "q8_act_two_words_bytes": (_sz, [_i64, _i64]),
@@ -190,6 +194,10 @@ def q8_packed_scales_bytes(K: int, N: int) -> int:
 
 def q8_act_scales_offset(m: int, K: int) -> int:
     return int(lib().q8_act_scales_offset(m, K))
+
+
+def q8_act_view_offset(m: int, K: int) -> int:
+    return int(lib().q8_act_view_offset(m, K))
 
 
 def q8_act_bytes(m: int, K: int) -> int:

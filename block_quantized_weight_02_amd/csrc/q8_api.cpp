@@ -125,6 +125,11 @@ size_t act_scales_offset(int64_t m, int64_t K) {
   return (size_t)round_up(m * K, 256);
 }
 
+// Offset of the one-word buffer's block-interleaved view of the codes.
+size_t act_view_offset(int64_t m, int64_t K) {
+  return (size_t)round_up((int64_t)act_scales_offset(m, K) + m * (K / Q8_BLOCK) * 4, 256);
+}
+
 // Offset of the scales in the activation buffer of a format: the two-word
 // form holds 2m rows of words before its scales.
 size_t act_scales_offset_of(int act_fmt, int64_t m, int64_t K) {
@@ -193,11 +198,41 @@ int rows_for(int64_t m) {
 // holds both words of up to 16 rows).
 constexpr int64_t kValuTwoWordRows = 2;
 
-q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
+// One-word Q8_0 activations of 17-32 rows take the tile-per-workgroup
+// 32x32x32 kernel (MFMA32_TILE; a product of one weight only, so the gated
+// pair and the parts pass tile32 = false).  Measured on MI355X against the
+// block-interleaved and column-group kernels (us, rows 17 / 24 / 32):
+// K=5120, N=32000: 36.6 / 37.5 / 39.2 against 45.7 / 47.2 / 48.8 (column-
+// group, 2 splits); K=4096, N=14336: 16.9 / 17.4 / 18.0 against 18.1 / 19.4 /
+// 20.1; N=4096: 11.1 / 11.3 / 11.6 against 12.9 / 13.1 / 13.3; N=1024: 10.3 /
+// 10.6 / 10.9 against 11.7 / 11.9 / 12.0; K=5120, N=40: 10.4 / 10.3 / 10.6
+// against 11.2 / 11.4 / 11.6.  8 waves from 384 tiles (N=32000: 39.2 against
+// 44.2 us with 16), else 16 (N=14336: 18.0 against 21.1); K split only below
+// 128 tiles: 3 ways from 8 tiles (N=4096: 11.5 against 11.8 with 4 and 12.4
+// with 2; N=1024: 10.9 against 11.0 with 4), 4 ways below (N=40: 10.6 against
+// 11.4 with 5).  Up to 16 rows the block-interleaved 16-row kernel stays
+// ahead (m=16, N=32000: 34.4 against 36.3 us; N=14336: 16.0 against 16.9).
+q8_plan tile32_plan(int64_t K, int64_t N) {
+  const int64_t NB = K / Q8_BLOCK;
+  const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
+  q8_plan p;
+  p.kernel = Q8_KERNEL_MFMA32_TILE;
+  p.rows = 32;
+  p.kslices = 1;
+  p.waves = T >= 384 ? 8 : 16;
+  int64_t S = T >= 128 ? 1 : (T >= 8 ? 3 : 4);
+  const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
+  if (S > smax) S = smax;
+  p.split_k = (int32_t)S;
+  return p;
+}
+
+q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tile32 = true) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   const DeviceFacts dev = device_facts();
   const int64_t smax = NB / 40 > 0 ? NB / 40 : 1;
+  if (tile32 && act_fmt == Q8_ACT_Q8_0 && m > 16) return tile32_plan(K, N);
   q8_plan p;
   p.kslices = 1;
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && m <= kValuTwoWordRows) {
@@ -329,8 +364,9 @@ constexpr size_t kCounterBytes = (size_t)(kMaxN / Q8_TILE_COLS) * 4 * 4;
 size_t plan_ws_bytes(const q8_plan &p, int64_t m, int64_t N, int nw = 1) {
   if (p.split_k * nw <= 1) return 0;
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
-  // the column-group kernel keeps whole 16-column records of its tile rows
-  const int64_t rows = p.kernel == Q8_KERNEL_MFMA_COLS ? p.rows : m;
+  // the column-group and 32x32 kernels keep whole records of their tile rows
+  const int64_t rows =
+      (p.kernel == Q8_KERNEL_MFMA_COLS || p.kernel >= Q8_KERNEL_MFMA32) ? p.rows : m;
   return kCounterBytes + (size_t)round_up((int64_t)nw * p.split_k * rows * Npad * 4, 256);
 }
 
@@ -415,6 +451,9 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   const int nw = pair ? 2 : 1;
   if (pair && act_fmt == Q8_ACT_Q8_0_TWO_WORDS)
     return fail(Q8_ERR_ACT_FMT, "the gated pair takes no two-word activation (act_fmt 2)");
+  if (pair && plan.kernel >= Q8_KERNEL_MFMA32)
+    return fail(Q8_ERR_PLAN, "the MFMA32 kernels do not run the gated pair: "
+                "use the VALU, MFMA or MFMA_COLS kernel");
   if (ep && ep->y_q8 && plan.kernel == Q8_KERNEL_MFMA_COLS && plan.split_k * nw < 2)
     return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel quantizes its output in the split-K "
                 "finish: y_q8 needs split_k >= 2 (or the MFMA or VALU kernel)");
@@ -434,8 +473,9 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
   a.T = (int)(Npad / Q8_TILE_COLS);
   a.split_k = plan.split_k;
   a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
+  if (act_fmt != Q8_ACT_BF16 && act_view_offset(m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "activation too large");
+  a.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
   a.ep.N = (int)N;
   a.ep.write_y = 1;
   a.ep.nw = nw;
@@ -452,6 +492,7 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
       a.ep.yq = static_cast<int8_t *>(ep->y_q8);
       a.ep.yq_scale = reinterpret_cast<float *>(static_cast<char *>(ep->y_q8) +
                                                 act_scales_offset(m, Npad));
+      a.ep.yq_view = static_cast<int8_t *>(ep->y_q8) + act_view_offset(m, Npad);
     }
   }
   if (!write_dots && plan.split_k * nw > 1) {
@@ -520,7 +561,7 @@ q8_plan fused_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt,
 // single product (measured on MI355X, m = 1, K = 4096, N = 14336: 4 waves
 // 23.0 us, 8 waves 24.2 us).
 q8_plan glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
-  q8_plan p = default_plan(m, K, 2 * round_up(N, Q8_TILE_COLS), act_fmt);
+  q8_plan p = default_plan(m, K, 2 * round_up(N, Q8_TILE_COLS), act_fmt, false);
   const int64_t units = 2 * round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   if (p.kernel == Q8_KERNEL_VALU && units * p.split_k > device_facts().cus) p.waves /= 2;
   return p;
@@ -619,7 +660,7 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
 // MI355X, m = 16, K = 4096, N = 4096 + 1024 + 1024: one split 14.7 us, two
 // 12.1 us, three 16.0 us).
 q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
-  q8_plan p = default_plan(m, K, cols, act_fmt);
+  q8_plan p = default_plan(m, K, cols, act_fmt, false);
   const int64_t NB = K / Q8_BLOCK;
   const int64_t units = cols / Q8_TILE_COLS;
   const DeviceFacts dev = device_facts();
@@ -646,8 +687,8 @@ q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
 int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
               int64_t cols, int act_fmt, const q8_plan &plan, hipStream_t stream,
               void *workspace, size_t ws_bytes) {
-  if (plan.kernel == Q8_KERNEL_MFMA_COLS)
-    return fail(Q8_ERR_PLAN, "the MFMA_COLS kernel does not run parts: "
+  if (plan.kernel == Q8_KERNEL_MFMA_COLS || plan.kernel >= Q8_KERNEL_MFMA32)
+    return fail(Q8_ERR_PLAN, "the MFMA_COLS and MFMA32 kernels do not run parts: "
                 "use the VALU or MFMA kernel");
   int st = check_plan(&plan, m, K, act_fmt, false);
   if (st) return st;
@@ -723,9 +764,14 @@ size_t q8_act_scales_offset(int64_t m, int64_t K) {
   return act_scales_offset(m, K);
 }
 
+size_t q8_act_view_offset(int64_t m, int64_t K) {
+  if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
+  return act_view_offset(m, K);
+}
+
 size_t q8_act_bytes(int64_t m, int64_t K) {
   if (m < 1 || K <= 0 || K % Q8_BLOCK) return 0;
-  return act_scales_offset(m, K) + (size_t)(m * (K / Q8_BLOCK)) * 4;
+  return act_view_offset(m, K) + (size_t)(m * K);
 }
 
 size_t q8_gemv_workspace_bytes(int64_t m, int64_t K, int64_t N, int act_fmt) {
@@ -764,13 +810,13 @@ int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
   int st;
   if ((st = check_m(m, Q8_MAX_GEMM_ROWS))) return st;
   if ((st = check_kn(K, 1))) return st;
-  if (act_scales_offset(m, K) > 0xffffffffull)
+  if (act_view_offset(m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
   if ((st = check_ptr(x_bf16, "x_bf16")) || (st = check_ptr(x_q8, "x_q8"))) return st;
   (void)hipGetLastError();
-  hipError_t e = q8::launch_quantize_act(x_bf16, x_q8, (int)m, (int)K,
-                                         (unsigned)act_scales_offset(m, K), stream);
+  hipError_t e = q8::launch_quantize_act(x_bf16, x_q8, (int)m, (int)K, act_scales_offset(m, K),
+                                         act_view_offset(m, K), stream);
   if (e != hipSuccess) return hip_fail(e, "quantize_act launch");
   return ok();
 }

@@ -28,6 +28,11 @@ constexpr int kChunkBytes = 2048;   // one tile x one block of values
 constexpr int kHalfBytes = 1024;    // 16 k-values of each of the 64 columns
 constexpr int kLayoutVersion = 2;
 
+// The one-word quantized activation buffer: int8 m x K row-major at 0, fp32
+// scales m x K/32 row-major at the scale offset, and the same int8 values in
+// the block-interleaved view at the view offset: block b of row r at
+// ((b * m + r) * 32), so one block's m rows are m*32 consecutive bytes.
+//
 // Activation forms: bf16; int8 with one scale per 32 (one word); and two
 // int8 words per value with one scale per 32, the second word the first's
 // rounding residual in steps of 1/128 of the scale (a buffer laid out as
@@ -60,6 +65,7 @@ struct Epi {
   const float *residual;
   int8_t *yq;
   float *yq_scale;
+  int8_t *yq_view;       // the quantized output's block-interleaved view (with yq)
   int N;
   int write_y;
   int nw;                // weights: 1, or 2 for the gated pair
@@ -82,6 +88,7 @@ struct GemvArgs {
   int m, K, NB, Npad, T;
   int split_k;
   unsigned act_scale_off; // byte offset of the activation scales (Q8 mode)
+  unsigned act_view_off;  // byte offset of the block-interleaved view (one-word Q8)
   Epi ep;                 // epilogue (plain product: N set, write_y 1, nw 1, rest null)
   // Output tiles times weights: the launch's units of work.
   int tiles() const { return T * ep.nw; }
@@ -93,12 +100,13 @@ hipError_t launch_repack(const int8_t *q_kn, const float *s_kn, int K, int N,
 hipError_t launch_unpack(const int8_t *wq, const float *wsc, int K, int N,
                          int8_t *q_kn, float *s_kn, hipStream_t stream);
 hipError_t launch_quantize_act(const uint16_t *x, void *x_q8, int m, int K,
-                               unsigned scale_off, hipStream_t stream);
+                               size_t scale_off, size_t view_off, hipStream_t stream);
 hipError_t launch_quantize_act_two_words(const uint16_t *x, void *x_q8x2, int m, int K,
                                          unsigned scale_off, hipStream_t stream);
 // kernel: 0 VALU, 1 MFMA (waves split K, each over all 64 columns), 2 MFMA
-// (waves own 16-column groups); rows: 1,2,4,8,16,32; act: Act; waves: 4, 8
-// or 16; kslices: waves sharing one column group's K range (kernel 2 only).
+// (waves own 16-column groups), 3 MFMA 32x32x32 int8 (waves split K, each
+// over all 64 columns); rows: 1,2,4,8,16,32; act: Act; waves: 4, 8 or 16;
+// kslices: waves sharing one column group's K range (kernel 2 only).
 // Returns hipErrorInvalidValue for a combination that is not instantiated.
 hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots, int waves, int kslices,
                        const GemvArgs &a, hipStream_t stream);
@@ -106,6 +114,19 @@ bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves
 // Dynamic LDS bytes a launch needs (activation stage plus carries; 0 for VALU).
 size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int NB,
                       int split_k);
+
+// The 32x32x32 int8 matrix-core product (q8_mfma32.hip, kernel 3): 32 rows of
+// a one-word Q8_0 activation; waves = kslices (waves splitting one tile's K
+// range) x tiles side by side; one weight (no pair, no parts).
+// kernel 4 is its direct form: the activation fragments loaded from memory
+// with each weight stage, only the activation scales staged; kernel 5 the
+// tile-per-workgroup form (the VALU kernel's weight stream, operands moved
+// into place with lane swaps).
+bool mfma32_instantiated(int kernel, int rows, int act, bool write_dots, int waves,
+                         int kslices);
+size_t mfma32_lds_bytes(int kernel, int waves, int kslices, int NB, int split_k);
+hipError_t launch_gemv_mfma32(int kernel, int waves, int kslices, bool write_dots,
+                              const GemvArgs &a, hipStream_t stream);
 
 // The many-row product (q8_gemm.hip): no split, no workspace.
 struct GemmArgs {

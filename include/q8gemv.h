@@ -36,7 +36,13 @@
  *   bf16 activation   x    : m x K bf16 (uint16 bit patterns), row-major
  *   quantized act.    x_q8 : one buffer of q8_act_bytes(m, K) bytes: int8
  *                            values m x K row-major at offset 0, fp32 scales
- *                            m x K/32 row-major at q8_act_scales_offset(m, K)
+ *                            m x K/32 row-major at q8_act_scales_offset(m, K),
+ *                            and the same int8 values again in the pages'
+ *                            block-interleaved view of the rows (from_q8.rs,
+ *                            fn relayout_rows_to_q8_view: each 32-value block
+ *                            of every row side by side) at
+ *                            q8_act_view_offset(m, K): value (r, k) at byte
+ *                            ((k/32) * m + r) * 32 + k % 32
  *   output            y    : m x N_pad fp32 row-major, N_pad = q8_padded_cols(N);
  *                            columns N..N_pad-1 are written and are exactly +0
  *                            (pad values and scales are zero: from_q8.rs,
@@ -90,7 +96,11 @@ size_t q8_packed_scales_bytes(int64_t K, int64_t N);
 /* Byte offset of the fp32 scales inside a quantized activation buffer:
  * m*K rounded up to 256. */
 size_t q8_act_scales_offset(int64_t m, int64_t K);
-/* Total bytes of a quantized activation buffer. 0 on a bad shape. */
+/* Byte offset of the block-interleaved view inside a quantized activation
+ * buffer: the scales' end rounded up to 256. */
+size_t q8_act_view_offset(int64_t m, int64_t K);
+/* Total bytes of a quantized activation buffer (values, scales and view).
+ * 0 on a bad shape. */
 size_t q8_act_bytes(int64_t m, int64_t K);
 /* The same two for the two-word form: its 2*m*K bytes of words, then the
  * scales at 2*m*K rounded up to 256 (m rows of K/32 fp32). */
@@ -128,7 +138,9 @@ int q8_unpack(const int8_t *W_q8, const float *W_q8_scale, int64_t K,
  *     amax = max|x|,  d = fp32(amax / 127)  (amax == 0: d = 0, xq = 0),
  *     xq   = clamp(round_half_away_from_zero(fp32(x / d)), -127, 127)
  * with correctly rounded divisions.  Requires 1 <= m <= Q8_MAX_GEMM_ROWS,
- * K > 0, K % 32 == 0.  x_q8 receives q8_act_bytes(m, K) bytes.
+ * K > 0, K % 32 == 0.  x_q8 receives q8_act_bytes(m, K) bytes: the codes
+ * row-major, the scales, and the codes' block-interleaved view (the
+ * MFMA32_TILE kernel reads one block's rows from it as one run).
  */
 int q8_quantize_act(const uint16_t *x_bf16, void *x_q8, int64_t m, int64_t K,
                     hipStream_t stream);
@@ -201,7 +213,20 @@ typedef enum {
   Q8_KERNEL_VALU = 0,     /* lane per column, activation broadcast from SGPRs     */
   Q8_KERNEL_MFMA = 1,     /* 16x16x32 matrix-core block dots, activation in LDS;
                              waves split K, each over all 64 columns of a tile    */
-  Q8_KERNEL_MFMA_COLS = 2 /* as MFMA, but each wave owns one 16-column group      */
+  Q8_KERNEL_MFMA_COLS = 2, /* as MFMA, but each wave owns one 16-column group     */
+  Q8_KERNEL_MFMA32 = 3,    /* 32x32x32 int8 matrix-core block dots, 32 rows of a
+                              one-word Q8_0 activation in LDS; each wave covers all
+                              64 columns of a tile, kslices waves split a tile's K
+                              range, waves / kslices tiles side by side; one weight
+                              (no gated pair, no parts)                             */
+  Q8_KERNEL_MFMA32_DIRECT = 4, /* as MFMA32, but the activation fragments are loaded
+                              from memory with each weight stage and only the
+                              activation scales are staged in LDS, so a workgroup's
+                              K range is not bounded by the LDS                    */
+  Q8_KERNEL_MFMA32_TILE = 5 /* the 32x32x32 block dots with the VALU kernel's weight
+                              stream: one workgroup per (tile, K split), waves (4, 8
+                              or 16) split K, the activation fragments loaded with
+                              the weights, kslices ignored                          */
 } q8_kernel;
 
 typedef struct q8_plan {
@@ -213,7 +238,10 @@ typedef struct q8_plan {
   int32_t waves;   /* waves (64 lanes) per workgroup: 4, 8 or 16               */
   int32_t kslices; /* MFMA_COLS: waves that split one 16-column group's K range
                       (1, 2 or 4; waves = 4 * kslices * tiles side by side);
-                      other kernels: ignored (all their waves split K)         */
+                      MFMA32(_DIRECT): waves that split one tile's K range (waves 4:
+                      1, 2, 4; waves 8: 1, 2, 4, 8; waves = kslices * tiles
+                      side by side); VALU, MFMA: ignored (all their waves
+                      split K)                                                 */
 } q8_plan;
 
 /* The plan q8_gemv would launch for this shape on the current device. */
@@ -247,8 +275,9 @@ int q8_gemv_block_dots_planned(const void *x_q8, const int8_t *W_q8,
  *   - when y_q8 is given, z's quantized form per row and per 32 columns, by
  *     exactly the q8_quantize_act arithmetic applied to fp32 z, in the
  *     activation layout of q8_act_bytes(m, N_pad): int8 m x N_pad at y_q8,
- *     fp32 scales m x N_pad/32 at y_q8 + q8_act_scales_offset(m, N_pad) --
- *     the input of the next product with act_fmt Q8_ACT_Q8_0 and K = N_pad.
+ *     fp32 scales m x N_pad/32 at y_q8 + q8_act_scales_offset(m, N_pad), the
+ *     view at y_q8 + q8_act_view_offset(m, N_pad) -- the input of the next
+ *     product with act_fmt Q8_ACT_Q8_0 and K = N_pad.
  * All pointers are device pointers, 16-byte aligned.  bias holds N fp32;
  * residual is m x N_pad fp32 like y and may be y itself (each element is read
  * before it is written, by the same thread).  The MFMA_COLS kernel quantizes

@@ -387,6 +387,19 @@ def unpack_ref(values: np.ndarray, scales: np.ndarray, K: int, N: int
     return np.ascontiguousarray(q[:, :N]), np.ascontiguousarray(s[:, :N])
 
 
+def act_view_ref(xq: np.ndarray) -> np.ndarray:
+    """The block-interleaved view of an ``m x K`` int8 activation, flat: every
+    row's 32-value block b side by side, value ``(r, k)`` at
+    ``((k // 32) * m + r) * 32 + k % 32`` (from_q8.rs, fn
+    relayout_rows_to_q8_view: the rows' blocks of one K range brought
+    together so that one block of every row is read as one piece)."""
+    xq = _c(xq, np.int8)
+    m, K = xq.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    return np.ascontiguousarray(xq.reshape(m, K // BLOCK, BLOCK).transpose(1, 0, 2)).ravel()
+
+
 def view_rows(m: int, K: int) -> int:
     """Rows of the ``K/32 x 32`` activation view (from_q8.rs, fn q8_view_rows)."""
     return int(_load().q8o_view_rows(m, K))

@@ -38,7 +38,15 @@ def quantize(x_bits: np.ndarray):
     np.testing.assert_array_equal(xq, rq, err_msg="HIP quantizer codes differ from the oracle's")
     np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32),
                                   err_msg="HIP quantizer scales differ from the oracle's")
+    np.testing.assert_array_equal(act_view(buf, m, K), oracle.act_view_ref(rq),
+                                  err_msg="HIP quantizer view differs from the oracle's layout")
     return buf
+
+
+def act_view(buf: torch.Tensor, m: int, K: int) -> np.ndarray:
+    """The block-interleaved view region of a quantized activation buffer."""
+    off = q8.q8_act_view_offset(m, K)
+    return buf.cpu().numpy()[off: off + m * K].view(np.int8)
 
 
 def act_host(buf: torch.Tensor, m: int, K: int):

@@ -43,7 +43,10 @@ def test_sizes():
     assert q8.q8_packed_values_bytes(4096, 14336) == 4096 * 14336
     assert q8.q8_packed_values_bytes(33, 14) == 0
     assert q8.q8_act_scales_offset(32, 5120) == 163840
-    assert q8.q8_act_bytes(32, 5120) == 163840 + 32 * 160 * 4
+    assert q8.q8_act_view_offset(32, 5120) == 163840 + 32 * 160 * 4
+    assert q8.q8_act_bytes(32, 5120) == 163840 + 32 * 160 * 4 + 163840
+    assert q8.q8_act_view_offset(3, 96) == 768          # scales at 512, 36 bytes, rounded to 768
+    assert q8.q8_act_bytes(3, 96) == q8.q8_act_view_offset(3, 96) + 288
     assert q8.q8_act_scales_offset(1, 32) == 256
     assert q8.q8_layout_version() == 2
 
@@ -225,17 +228,18 @@ def test_parts_validation():
 
 def test_parts_plan_is_the_side_by_side_product():
     # the parts' columns side by side are one product's work; the column-group
-    # kernel (which does not walk parts) is replaced by the MFMA kernel
+    # and 32x32 tile kernels (which do not walk parts) are replaced by the
+    # MFMA kernel
     for (m, K, Ns, act) in ((1, 4096, (4096, 1024, 1024), 0), (8, 4096, (4096, 1024, 1024), 1),
                             (16, 4096, (4096, 1024, 1024), 0), (32, 4096, (100, 30), 1),
                             (4, 2048, (200,), 1)):
         parts = [_part(N) for N in Ns]
         got = q8.q8_gemv_parts_default_plan(parts, m, K, act)
         wide = q8.q8_gemv_default_plan(m, K, sum(q8.q8_padded_cols(N) for N in Ns), act)
-        if wide.kernel != q8.Q8_KERNEL_MFMA_COLS:
+        if wide.kernel not in (q8.Q8_KERNEL_MFMA_COLS, q8.Q8_KERNEL_MFMA32_TILE):
             assert (got.kernel, got.rows, got.split_k) == (wide.kernel, wide.rows, wide.split_k)
         else:
-            # the column-group kernel walks no parts: the MFMA kernel instead
+            # these kernels walk no parts: the MFMA kernel instead
             assert got.kernel == q8.Q8_KERNEL_MFMA and got.waves == 16 and got.rows == wide.rows
             assert 1 <= got.split_k <= K // 32
 

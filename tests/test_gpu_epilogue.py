@@ -59,6 +59,8 @@ def run_fused(xin, Wq, Ws, m, K, N, act, bias=None, residual=None, quant=False,
     yh = y.cpu().numpy() if y is not None else None
     if quant:
         codes, scales = g.act_host(yq, m, Npad)
+        np.testing.assert_array_equal(g.act_view(yq, m, Npad), oracle.act_view_ref(codes),
+                                      err_msg="quantized output's view")
         return yh, codes, scales
     return yh, None, None
 
@@ -113,13 +115,18 @@ EXACT_PLANS = [None,
                (q8.Q8_KERNEL_VALU, 4, 1, 8, 1), (q8.Q8_KERNEL_VALU, 4, 3, 16, 1),
                (q8.Q8_KERNEL_VALU, 32, 2, 4, 1),
                (q8.Q8_KERNEL_MFMA, 16, 1, 16, 1), (q8.Q8_KERNEL_MFMA, 32, 4, 8, 1),
-               (q8.Q8_KERNEL_MFMA_COLS, 32, 2, 16, 1), (q8.Q8_KERNEL_MFMA_COLS, 16, 5, 8, 2)]
+               (q8.Q8_KERNEL_MFMA_COLS, 32, 2, 16, 1), (q8.Q8_KERNEL_MFMA_COLS, 16, 5, 8, 2),
+               (q8.Q8_KERNEL_MFMA32, 32, 1, 8, 2), (q8.Q8_KERNEL_MFMA32, 32, 3, 4, 1),
+               (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 1, 8, 4), (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 2, 8, 8),
+               (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1), (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 16, 1)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8])
 @pytest.mark.parametrize("pl", EXACT_PLANS, ids=lambda p: "default" if p is None else
                          "k{}r{}s{}w{}".format(*p[:4]))
 def test_exact_case_bit_exact(act, pl):
+    if pl is not None and pl[0] >= q8.Q8_KERNEL_MFMA32 and act != Q8:
+        pytest.skip("the MFMA32 kernel takes Q8_0 activations only")
     m, K, N = 3, 512, 100
     x, q, s, bias, res = inputs.exact_case(m, K, N, seed=31)
     Wq, Ws = g.pack(q, s)
@@ -153,6 +160,13 @@ RANDOM_PLANS = [
     (32, Q8, (q8.Q8_KERNEL_MFMA_COLS, 32, 2, 16, 1)),
     (16, BF16, (q8.Q8_KERNEL_MFMA_COLS, 16, 3, 8, 2)),
     (20, Q8, (q8.Q8_KERNEL_MFMA_COLS, 32, 68, 16, 4)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA32, 32, 2, 8, 2)),
+    (17, Q8, (q8.Q8_KERNEL_MFMA32, 32, 5, 4, 4)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA32, 32, 1, 8, 1)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 1, 8, 4)),
+    (19, Q8, (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 3, 4, 2)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1)),
+    (25, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 4, 16, 1)),
 ]
 
 

@@ -64,6 +64,8 @@ def run_glu(xin, W, m, K, N, act, bg=None, bu=None, quant=False, write_y=True, p
     yh = y.cpu().numpy() if y is not None else None
     if quant:
         codes, scales = g.act_host(yq, m, Npad)
+        np.testing.assert_array_equal(g.act_view(yq, m, Npad), oracle.act_view_ref(codes),
+                                      err_msg="quantized output's view")
         return yh, codes, scales
     return yh, None, None
 

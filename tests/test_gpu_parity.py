@@ -207,6 +207,16 @@ def _plans(m, NB):
             for split in splits:
                 if split <= NB:
                     out.append((q8.Q8_KERNEL_MFMA_COLS, rows, split, waves, ks))
+    if m <= 32:
+        for kernel in (q8.Q8_KERNEL_MFMA32, q8.Q8_KERNEL_MFMA32_DIRECT):
+            for (waves, ks) in ((4, 1), (4, 2), (4, 4), (8, 1), (8, 2), (8, 4), (8, 8)):
+                for split in splits:
+                    if split <= NB:
+                        out.append((kernel, 32, split, waves, ks))
+        for waves in (4, 8, 16):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_MFMA32_TILE, 32, split, waves, 1))
     return out
 
 

@@ -189,6 +189,11 @@ def _k_reversed(q, s):
     return np.ascontiguousarray(v).ravel(), _REPACK(q, s)[1]
 
 
+def _view_row_major_blocks(xq):
+    xq = np.asarray(xq, np.int8)
+    return np.ascontiguousarray(xq).ravel()
+
+
 _REPACK = oracle.repack_ref
 LAYOUT_MUTANTS = [("halves swapped", _swap_halves), ("block-major chunks", _block_major),
                   ("scales in column order", _scales_in_column_order),
@@ -209,3 +214,10 @@ def _passes(fn, kw):
         return True
     except Exception:
         return False
+
+
+def test_planted_view_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "act_view_ref", _view_row_major_blocks)
+    failed = [name for name, f, kw in _pin_calls() if "activation_view" in name
+              and not _passes(f, kw)]
+    assert failed

@@ -625,3 +625,19 @@ def test_epilogue_brute_force(m, K, N, seed):
     babs = np.abs(xd) @ np.abs(dense_w(q, s)) + np.abs(bias)[None, :] + np.abs(res[:, :N])
     assert np.all(np.abs(z - ref) <= 1e-13 * babs + 1e-300)
     np.testing.assert_allclose(zb, babs, rtol=1e-13)
+
+
+def test_activation_view_hand_worked():
+    # m = 3, K = 96: value (r=2, k=37) is block 1, place 5: (1*3 + 2)*32 + 5 = 165;
+    # (0, 0) -> 0; (1, 95) -> (2*3 + 1)*32 + 31 = 255; (2, 31) -> (0*3 + 2)*32 + 31 = 95
+    xq = np.zeros((3, 96), np.int8)
+    for (r, k, at) in ((2, 37, 165), (0, 0, 0), (1, 95, 255), (2, 31, 95)):
+        xq[:] = 0
+        xq[r, k] = -5
+        v = oracle.act_view_ref(xq)
+        assert v.size == 288
+        np.testing.assert_array_equal(np.flatnonzero(v), [at])
+    # a block of every row is one contiguous run of m*32 bytes
+    xq = np.random.default_rng(5).integers(-127, 128, (3, 96)).astype(np.int8)
+    v = oracle.act_view_ref(xq)
+    np.testing.assert_array_equal(v[96:192].reshape(3, 32), xq[:, 32:64])

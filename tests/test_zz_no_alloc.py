@@ -43,7 +43,8 @@ def _both(m, K, N, act, seed):
 # so the scratch array carries split-K counters and partials between them.
 PAIRS = [
     ((1, 14336, 4096, BF16), (1, 4096, 1024, BF16)),       # VALU, 4 then 3 splits
-    ((32, 5120, 32000, Q8), (32, 5120, 40, Q8)),           # column-group MFMA, then 5 splits
+    ((32, 5120, 4096, Q8), (32, 5120, 40, Q8)),            # 32x32 tile kernel, 3 then 4 splits
+    ((20, 4096, 4096, BF16), (17, 2176, 200, BF16)),       # block-interleaved MFMA, 32 rows
     ((16, 4096, 4096, BF16), (3, 2176, 200, Q8)),          # block-interleaved MFMA, 2 splits
 ]
 
@@ -72,10 +73,12 @@ def test_noalloc_without_split_and_repeated():
 
 
 def test_noalloc_rejects_a_workspace_beyond_the_scratch():
-    m, K, N = 32, 5120, 200000          # column-group plan: 2 splits x 32 rows x N fp32
-    need = q8.q8_gemv_workspace_bytes(m, K, N, Q8)
+    # a long K of 32 bf16 rows: the MFMA plan splits K in ~26 for the LDS,
+    # ~27 MB of partial carries
+    m, K, N = 32, 65536, 8192
+    need = q8.q8_gemv_workspace_bytes(m, K, N, BF16)
     assert need > q8.q8_noalloc_scratch_bytes()
     A = 1 << 20                           # host-side refusal: never dereferenced
     with pytest.raises(q8.Q8Error) as e:
-        q8.q8_gemv_noalloc(A, A, A, A, m, K, N, Q8, 0)
+        q8.q8_gemv_noalloc(A, A, A, A, m, K, N, BF16, 0)
     assert e.value.status == 5 and "scratch" in e.value.message

@@ -26,6 +26,7 @@ Q8_KERNEL_MFMA_COLS = 2
 Q8_KERNEL_MFMA32 = 3
 Q8_KERNEL_MFMA32_DIRECT = 4
 Q8_KERNEL_MFMA32_TILE = 5
+Q8_KERNEL_MFMA16_TILE = 6
 Q8_MAX_ROWS = 32
 Q8_MAX_GEMM_ROWS = 8192
 Q8_MAX_PARTS = 4

@@ -17,8 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libq8gemv.so")
-SOURCES = ["q8_kernels.hip", "q8_mfma32.hip", "q8_gemm.hip", "q8_measure.hip", "q8_noalloc.hip",
-           "q8_api.cpp"]
+SOURCES = ["q8_kernels.hip", "q8_mfma32.hip", "q8_tile16.hip", "q8_gemm.hip", "q8_measure.hip",
+           "q8_noalloc.hip", "q8_api.cpp"]
 # Per-source device flags.  The GEMM writes its MFMA results to VGPRs (by
 # default the compiler routes them through one AGPR quad and serialises the
 # matrix core behind its reads).

@@ -199,8 +199,7 @@ int rows_for(int64_t m) {
 constexpr int64_t kValuTwoWordRows = 2;
 
 // One-word Q8_0 activations of 17-32 rows take the tile-per-workgroup
-// 32x32x32 kernel (MFMA32_TILE; a product of one weight only, so the gated
-// pair and the parts pass tile32 = false).  Measured on MI355X against the
+// 32x32x32 kernel (MFMA32_TILE; a product of one weight only).  Measured on MI355X against the
 // block-interleaved and column-group kernels (us, rows 17 / 24 / 32):
 // K=5120, N=32000: 36.6 / 37.5 / 39.2 against 45.7 / 47.2 / 48.8 (column-
 // group, 2 splits); K=4096, N=14336: 16.9 / 17.4 / 18.0 against 18.1 / 19.4 /
@@ -212,6 +211,17 @@ constexpr int64_t kValuTwoWordRows = 2;
 // with 2; N=1024: 10.9 against 11.0 with 4), 4 ways below (N=40: 10.6 against
 // 11.4 with 5).  Up to 16 rows the block-interleaved 16-row kernel stays
 // ahead (m=16, N=32000: 34.4 against 36.3 us; N=14336: 16.0 against 16.9).
+// Raises a tile plan's K split until its LDS (the split's activation scales
+// and the carries) fits a workgroup.
+void fit_tile_lds(q8_plan &p, int64_t NB, int act_fmt) {
+  const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
+  int64_t S = p.split_k;
+  while (S < NB && q8::gemv_lds_bytes(p.kernel, p.rows, act_fmt, p.waves, p.kslices, (int)NB,
+                                      (int)S) > budget)
+    ++S;
+  p.split_k = (int32_t)S;
+}
+
 q8_plan tile32_plan(int64_t K, int64_t N) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
@@ -224,15 +234,47 @@ q8_plan tile32_plan(int64_t K, int64_t N) {
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
   if (S > smax) S = smax;
   p.split_k = (int32_t)S;
+  fit_tile_lds(p, NB, Q8_ACT_Q8_0);
   return p;
 }
 
-q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tile32 = true) {
+// 3-16 rows (bf16 or one-word Q8_0) take the tile-per-workgroup 16x16x32
+// kernel (MFMA16_TILE), 16 waves, K split only below 128 tiles (256 / tiles
+// ways, at most 8).  Measured on MI355X against the block-interleaved MFMA
+// kernel (us, rows 3 / 8 / 16): bf16, K=4096, N=14336: 13.2 / 13.5 / 15.5
+// against 14.8 / 14.9 / 15.7; K=5120, N=32000: 30.9 / 30.7 / 35.1 against
+// 37.1 / 38.9 / 40.7; K=4096, N=4096 (4 splits): 8.2 / 8.2 / 8.4 against 9.3 /
+// 9.3 / 9.5; N=1024 (8 splits): 6.7 / 6.9 / 7.1 against 8.4 / 8.5 / 8.6.
+// Q8_0, K=4096, N=14336: 13.6 / 13.9 / 14.1 against 15.2 / 15.6 / 16.1;
+// K=5120, N=32000: 31.5 / 31.8 / 32.1 against 31.9 / 33.2 / 34.4.
+q8_plan tile16_plan(int64_t K, int64_t N, int act_fmt) {
+  const int64_t NB = K / Q8_BLOCK;
+  const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
+  q8_plan p;
+  p.kernel = Q8_KERNEL_MFMA16_TILE;
+  p.rows = 16;
+  p.kslices = 1;
+  p.waves = 16;
+  int64_t S = T >= 128 ? 1 : 256 / T;
+  if (S > 8) S = 8;
+  const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
+  if (S > smax) S = smax;
+  if (S < 1) S = 1;
+  p.split_k = (int32_t)S;
+  fit_tile_lds(p, NB, act_fmt);
+  return p;
+}
+
+// tiles: the tile-per-workgroup kernels may be chosen (they run one weight:
+// the gated pair and the parts pass false).
+q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tiles = true) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   const DeviceFacts dev = device_facts();
   const int64_t smax = NB / 40 > 0 ? NB / 40 : 1;
-  if (tile32 && act_fmt == Q8_ACT_Q8_0 && m > 16) return tile32_plan(K, N);
+  if (tiles && act_fmt == Q8_ACT_Q8_0 && m > 16) return tile32_plan(K, N);
+  if (tiles && act_fmt != Q8_ACT_Q8_0_TWO_WORDS && m > 2 && m <= 16)
+    return tile16_plan(K, N, act_fmt);
   q8_plan p;
   p.kslices = 1;
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && m <= kValuTwoWordRows) {

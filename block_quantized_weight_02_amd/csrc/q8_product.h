@@ -339,7 +339,7 @@ int resident_workgroups(Kern kern, int threads, size_t lds) {
 // `fit` are resident: the fewest rounds, then the fewest workgroups that
 // finish in that many rounds, so every workgroup walks the same number of
 // units (448 units on 256 resident: 224 workgroups of 2, not 256 of 1 or 2).
-int balanced_grid(int fit, int units) {
+inline int balanced_grid(int fit, int units) {
   if (fit < 1) fit = 1;
   if (units < 1) return 1;
   const int rounds = (units + fit - 1) / fit;

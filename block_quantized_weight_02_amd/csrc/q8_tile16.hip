@@ -1,0 +1,267 @@
+// q8_tile16.hip -- the product for up to 16 activation rows (bf16, or the
+// Q8_0 form) on the 16x16x32 matrix core, one workgroup per column tile.
+//
+// The product (docs.logicaffeine.com, logicaffeine_compile/spatial/passes/
+// from_q8.rs, module doc and fn q8_fold): per Q8_0 block b the dot
+// D[r,n] = sum_i x[r,32b+i] * q[32b+i,n], scaled once by the block's scale
+// and folded into an fp32 carry.  One 16x16x32 MFMA is exactly that dot for
+// 16 rows and 16 columns of one block (its K of 32 is one block), in bf16
+// (an int8 weight is exact in bf16 and every product exact in the fp32
+// accumulator) or in int8 (exact int32).
+//
+// The weight stream is the VALU kernel's: lane c loads column c's two
+// 16-byte halves of a block, so each load instruction reads one contiguous
+// KiB.  The MFMA's B operand of 16-column group g wants, in quarter q of the
+// wave (lanes 16q .. 16q+15), the 8 values k = 8q .. 8q+7 of column 16g + i
+// (i = lane % 16): a 4 x 4 transpose of (quarter, 8-byte piece), done in
+// registers with two v_permlane32_swap and two v_permlane16_swap per dword
+// pair.  The scale row's place 4i .. 4i+3 holds the scales of columns i,
+// i+16, i+32, i+48 -- the four groups of the lane -- as one 16-byte load.
+// The activation fragment (row i, k = 8q .. 8q+7) is loaded with the weights:
+// bf16 from the rows (16 rows of a block touch 16 cache lines), int8 from the
+// quantized activation's block-interleaved view (a block's rows are one
+// run); rows past m are zero.  W waves take blocks w, w+W, ... of the
+// workgroup's K split; their carries meet by halves in LDS and every wave
+// takes a share of the finish (epilogue, stores, split-K combine).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "q8_device.h"
+#include "q8_internal.h"
+#include "q8_product.h"
+
+namespace q8 {
+namespace {
+
+using namespace dev;
+
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2v_t;
+
+template <int ACT, int W>
+constexpr size_t t16_lds_bytes(int nblk) {
+  return (ACT == kActQ8 ? (size_t)nblk * 16 * 4 : 0) + (size_t)(W / 2) * 1024 * 4;
+}
+
+// A 16-byte load of the scale row with the default cache policy.
+__device__ __forceinline__ float4 buf_ld16f(buf_t r, unsigned voff, unsigned soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
+template <int ACT, int W, bool DOTS>
+__global__ void __launch_bounds__(64 * W)
+gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
+                   const float *__restrict__ wsc, float *__restrict__ y,
+                   float *__restrict__ partial, unsigned *__restrict__ counters,
+                   int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T, int S,
+                   int split_q, int split_r, unsigned act_scale_off, unsigned act_view_off,
+                   Epi ep) {
+  constexpr int MR = 16;
+  constexpr bool kQ8 = ACT == kActQ8;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, i = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = blockIdx.x, s = blockIdx.y;
+  int b_lo, b_hi;
+  split_range(s, split_q, split_r, b_lo, b_hi);
+  const int nblk = b_hi - b_lo;
+  const int nblk_max = split_q + (split_r > 0 ? 1 : 0);
+
+  const buf_t wr = make_buf(wq + (size_t)t * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
+  const buf_t sr = DOTS ? wr : make_buf(wsc + (size_t)t * NB * kTile, (unsigned)NB * kTile * 4);
+  const unsigned lw = (unsigned)lane * 16u, ls = (unsigned)i * 16u;
+  // the activation: bf16 rows, or the int8 view (block b's m rows at b*m*32)
+  const bool row_live = i < m;
+  const int ri = row_live ? i : 0;
+  const buf_t xr = kQ8 ? make_buf(static_cast<const char *>(xv) + act_view_off,
+                                  (unsigned)m * (unsigned)K)
+                       : make_buf(xv, (unsigned)m * (unsigned)K * 2u);
+  const unsigned xoff = kQ8 ? (unsigned)ri * 32u + (unsigned)q * 8u
+                            : (unsigned)ri * (unsigned)K * 2u + (unsigned)q * 16u;
+
+  struct Stage {
+    uint4 lo, hi;   // column `lane`'s k = 0..15 and 16..31 of the block
+    float4 sc;      // scales of columns i, i+16, i+32, i+48
+    uint4 a;        // activation row i, k = 8q .. 8q+7 (bf16: 16 bytes; int8: x, y)
+  };
+  auto load = [&](Stage &st, int b) {
+    const unsigned wb = (unsigned)b * kChunkBytes;
+    st.lo = buf_ld16(wr, lw, wb);
+    st.hi = buf_ld16(wr, lw + kHalfBytes, wb);
+    if constexpr (!DOTS) st.sc = buf_ld16f(sr, ls, (unsigned)b * (kTile * 4));
+    if constexpr (kQ8) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, xoff, (unsigned)b * (unsigned)m * 32u, 0);
+      st.a = make_uint4(row_live ? v.x : 0u, row_live ? v.y : 0u, 0u, 0u);
+    } else {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (unsigned)b * 64u, 0);
+      st.a = row_live ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  Stage A, B;
+  if (b_lo + wave < b_hi) load(A, b_lo + wave);
+  float *dxs = reinterpret_cast<float *>(lds);
+  float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4 : 0));
+  if constexpr (kQ8 && !DOTS) {
+    // the split's activation scales, [block][row], rows past m zero
+    const float *dxp =
+        reinterpret_cast<const float *>(static_cast<const char *>(xv) + act_scale_off);
+    for (int p = threadIdx.x; p < nblk * MR; p += 64 * W) {
+      const int r = p / nblk, bb = p - r * nblk;
+      dxs[bb * MR + r] = (r < m) ? dxp[(size_t)r * NB + b_lo + bb] : 0.0f;
+    }
+    __syncthreads();
+  }
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) acc[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](const Stage &st, int bb) {
+    // pieces: quarter Q holds column 16Q + i, piece p = k 8p .. 8p+7; after
+    // the transpose R[g] holds, in quarter q, column 16g + i's piece q
+    uint32_t R[4][2] = {{st.lo.x, st.lo.y}, {st.lo.z, st.lo.w}, {st.hi.x, st.hi.y},
+                        {st.hi.z, st.hi.w}};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const auto a02 = __builtin_amdgcn_permlane32_swap(R[0][d], R[2][d], false, false);
+      const auto a13 = __builtin_amdgcn_permlane32_swap(R[1][d], R[3][d], false, false);
+      const auto b01 = __builtin_amdgcn_permlane16_swap(a02[0], a13[0], false, false);
+      const auto b23 = __builtin_amdgcn_permlane16_swap(a02[1], a13[1], false, false);
+      R[0][d] = b01[0];
+      R[1][d] = b01[1];
+      R[2][d] = b23[0];
+      R[3][d] = b23[1];
+    }
+    const float scs[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
+    if constexpr (kQ8) {
+      const long a = __builtin_bit_cast(long, make_uint2(st.a.x, st.a.y));
+      float4 dx4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if constexpr (!DOTS) dx4 = *reinterpret_cast<const float4 *>(dxs + (bb - b_lo) * MR + 4 * q);
+      const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const long bw = __builtin_bit_cast(long, make_uint2(R[g][0], R[g][1]));
+        const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+        if constexpr (DOTS) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            if (r < m) dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + 16 * g + i] = d[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[g][e] = fmaf(dxv[e] * scs[g], (float)d[e], acc[g][e]);
+        }
+      }
+    } else {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, st.a);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const bf16x8_t bw = i8x8_to_bf16(make_uint2(R[g][0], R[g][1]));
+        const f32x4_t d =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[g][e] = fmaf(scs[g], d[e], acc[g][e]);
+      }
+    }
+  };
+
+  int b = b_lo + wave;
+  if (b < b_hi) {
+    while (true) {
+      if (b + W >= b_hi) {
+        compute(A, b);
+        break;
+      }
+      load(B, b + W);
+      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
+      compute(A, b);
+      A = B;
+      b += W;
+    }
+  }
+  if constexpr (DOTS) return;
+
+  // carries meet by halves: wave w + half adds into wave w
+#pragma unroll
+  for (int half = W / 2; half >= 1; half /= 2) {
+    if (wave >= half && wave < 2 * half) {
+      float *rw = red + (size_t)(wave - half) * 1024;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *reinterpret_cast<f32x4_t *>(rw + g * 256 + lane * 4) = acc[g];
+    }
+    __syncthreads();
+    if (wave < half) {
+      const float *rw = red + (size_t)wave * 1024;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[g] += *reinterpret_cast<const f32x4_t *>(rw + g * 256 + lane * 4);
+    }
+    __syncthreads();
+  }
+  // wave 0 holds the tile's sums: into LDS row-major, then every wave takes a
+  // share of the finish
+  if (wave == 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(4 * q + e) * 64 + 16 * g + i] = acc[g][e];
+  }
+  __syncthreads();
+  finish_tile<MR, 1, false, 64 * W>(
+      red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t}, partial,
+      counters, m, s, S, 0, ep);
+}
+
+template <int ACT, int W, bool DOTS>
+hipError_t launch_t16(const GemvArgs &a, hipStream_t stream) {
+  const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
+  const size_t lds = t16_lds_bytes<ACT, W>(nblk_max);
+  auto kern = gemv_tile16_kernel<ACT, W, DOTS>;
+  static size_t granted = 64 * 1024;
+  hipError_t e = grant_lds(kern, lds, granted);
+  if (e != hipSuccess) return e;
+  (void)hipGetLastError();
+  kern<<<dim3((unsigned)a.T, (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
+      a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
+      a.split_k, a.NB / a.split_k, a.NB % a.split_k, a.act_scale_off, a.act_view_off, a.ep);
+  return hipGetLastError();
+}
+
+template <int ACT, bool DOTS>
+hipError_t launch_t16_w(int waves, const GemvArgs &a, hipStream_t stream) {
+  switch (waves) {
+    case 4: return launch_t16<ACT, 4, DOTS>(a, stream);
+    case 8: return launch_t16<ACT, 8, DOTS>(a, stream);
+    case 16: return launch_t16<ACT, 16, DOTS>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+bool tile16_instantiated(int rows, int act, bool write_dots, int waves) {
+  if (rows != 16 || (waves != 4 && waves != 8 && waves != 16)) return false;
+  if (act == kActQ8) return true;
+  return act == kActBf16 && !write_dots;
+}
+
+size_t tile16_lds_bytes(int act, int waves, int NB, int split_k) {
+  const int nblk = (NB + split_k - 1) / split_k;
+  const size_t dx = act == kActQ8 ? (size_t)nblk * 16 * 4 : 0;
+  return dx + (size_t)(waves / 2) * 1024 * 4;
+}
+
+hipError_t launch_gemv_tile16(int act, int waves, bool write_dots, const GemvArgs &a,
+                              hipStream_t stream) {
+  if (a.ep.nw != 1 || a.ep.parts.n > 0) return hipErrorInvalidValue;
+  if (act == kActQ8)
+    return write_dots ? launch_t16_w<kActQ8, true>(waves, a, stream)
+                      : launch_t16_w<kActQ8, false>(waves, a, stream);
+  if (act == kActBf16 && !write_dots) return launch_t16_w<kActBf16, false>(waves, a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace q8

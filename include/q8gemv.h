@@ -223,10 +223,14 @@ typedef enum {
                               from memory with each weight stage and only the
                               activation scales are staged in LDS, so a workgroup's
                               K range is not bounded by the LDS                    */
-  Q8_KERNEL_MFMA32_TILE = 5 /* the 32x32x32 block dots with the VALU kernel's weight
+  Q8_KERNEL_MFMA32_TILE = 5, /* the 32x32x32 block dots with the VALU kernel's weight
                               stream: one workgroup per (tile, K split), waves (4, 8
                               or 16) split K, the activation fragments loaded with
                               the weights, kslices ignored                          */
+  Q8_KERNEL_MFMA16_TILE = 6 /* 16x16x32 block dots of up to 16 rows (bf16 or one-word
+                              Q8_0) with the VALU kernel's weight stream: one
+                              workgroup per (tile, K split), waves (4, 8 or 16)
+                              split K, kslices ignored; one weight                  */
 } q8_kernel;
 
 typedef struct q8_plan {

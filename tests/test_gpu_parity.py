@@ -217,6 +217,11 @@ def _plans(m, NB):
             for split in splits:
                 if split <= NB:
                     out.append((q8.Q8_KERNEL_MFMA32_TILE, 32, split, waves, 1))
+    if m <= 16:
+        for waves in (4, 8, 16):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_MFMA16_TILE, 16, split, waves, 1))
     return out
 
 

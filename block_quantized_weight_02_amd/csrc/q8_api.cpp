@@ -247,14 +247,19 @@ q8_plan tile32_plan(int64_t K, int64_t N) {
 // 9.3 / 9.5; N=1024 (8 splits): 6.7 / 6.9 / 7.1 against 8.4 / 8.5 / 8.6.
 // Q8_0, K=4096, N=14336: 13.6 / 13.9 / 14.1 against 15.2 / 15.6 / 16.1;
 // K=5120, N=32000: 31.5 / 31.8 / 32.1 against 31.9 / 33.2 / 34.4.
-q8_plan tile16_plan(int64_t K, int64_t N, int act_fmt) {
+q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   q8_plan p;
   p.kernel = Q8_KERNEL_MFMA16_TILE;
   p.rows = 16;
-  p.kslices = 1;
-  p.waves = 16;
+  // bf16, measured on MI355X: two-block stages pay only for many rows on
+  // mid-width weights (K = 4096, N = 14336: m = 16 14.8 against 15.2 us; m = 12
+  // 14.6 against 14.1); 8 waves on wide weights (K = 5120, N = 32000, m = 3 .. 16:
+  // 30.8 .. 34.8 us, within 1% of the best).
+  const bool bf16 = act_fmt == Q8_ACT_BF16;
+  p.kslices = bf16 && m >= 13 && T >= 128 && T < 384 ? 2 : 1;
+  p.waves = bf16 && T >= 384 ? 8 : 16;
   int64_t S = T >= 128 ? 1 : 256 / T;
   if (S > 8) S = 8;
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;
@@ -274,7 +279,7 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tiles = 
   const int64_t smax = NB / 40 > 0 ? NB / 40 : 1;
   if (tiles && act_fmt == Q8_ACT_Q8_0 && m > 16) return tile32_plan(K, N);
   if (tiles && act_fmt != Q8_ACT_Q8_0_TWO_WORDS && m > 2 && m <= 16)
-    return tile16_plan(K, N, act_fmt);
+    return tile16_plan(m, K, N, act_fmt);
   q8_plan p;
   p.kslices = 1;
   if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS && m <= kValuTwoWordRows) {

@@ -1349,7 +1349,7 @@ size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int
 bool gemv_instantiated(int kernel, int rows, int act, bool write_dots, int waves, int kslices) {
   if (kernel >= 3 && kernel <= 5)
     return mfma32_instantiated(kernel, rows, act, write_dots, waves, kslices);
-  if (kernel == 6) return tile16_instantiated(rows, act, write_dots, waves);
+  if (kernel == 6) return tile16_instantiated(rows, act, write_dots, waves, kslices);
   return pick(kernel, rows, act, write_dots, waves, kslices) != nullptr;
 }
 
@@ -1361,8 +1361,8 @@ hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots, int waves
     return launch_gemv_mfma32(kernel, waves, kslices, write_dots, a, stream);
   }
   if (kernel == 6) {
-    if (!tile16_instantiated(rows, act, write_dots, waves)) return hipErrorInvalidValue;
-    return launch_gemv_tile16(act, waves, write_dots, a, stream);
+    if (!tile16_instantiated(rows, act, write_dots, waves, kslices)) return hipErrorInvalidValue;
+    return launch_gemv_tile16(act, waves, kslices, write_dots, a, stream);
   }
   Launcher f = pick(kernel, rows, act, write_dots, waves, kslices);
   if (!f) return hipErrorInvalidValue;

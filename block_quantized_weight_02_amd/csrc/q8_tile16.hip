@@ -18,11 +18,14 @@
 // pair.  The scale row's place 4i .. 4i+3 holds the scales of columns i,
 // i+16, i+32, i+48 -- the four groups of the lane -- as one 16-byte load.
 // The activation fragment (row i, k = 8q .. 8q+7) is loaded with the weights:
-// bf16 from the rows (16 rows of a block touch 16 cache lines), int8 from the
-// quantized activation's block-interleaved view (a block's rows are one
-// run); rows past m are zero.  W waves take blocks w, w+W, ... of the
-// workgroup's K split; their carries meet by halves in LDS and every wave
-// takes a share of the finish (epilogue, stores, split-K combine).
+// int8 from the quantized activation's block-interleaved view (a block's
+// rows are one run; W waves take blocks w, w+W, ...); bf16 either straight
+// from the rows, one block a stage, or two blocks a stage (a wave takes pairs
+// 2w, 2w+1, then 2w+2W, ...) with the rows' 128 bytes of the pair read as
+// whole cache lines and handed to the MFMA layout through a per-wave LDS
+// scratch (one block of 16 rows touches 16 half-used lines a load); rows
+// past m are zero.  The waves' carries meet by halves in LDS and every
+// wave takes a share of the finish (epilogue, stores, split-K combine).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,10 +40,13 @@ using namespace dev;
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2v_t;
 
+// LDS: int8, the split's activation scales; bf16, a 2 KiB scratch per wave
+// (the activation transpose); then the carries' halves.
 template <int ACT, int W>
 constexpr size_t t16_lds_bytes(int nblk) {
-  return (ACT == kActQ8 ? (size_t)nblk * 16 * 4 : 0) + (size_t)(W / 2) * 1024 * 4;
+  return (ACT == kActQ8 ? (size_t)nblk * 16 * 4 : (size_t)W * 2048) + (size_t)(W / 2) * 1024 * 4;
 }
+
 
 // A 16-byte load of the scale row with the default cache policy.
 __device__ __forceinline__ float4 buf_ld16f(buf_t r, unsigned voff, unsigned soff) {
@@ -49,7 +55,7 @@ __device__ __forceinline__ float4 buf_ld16f(buf_t r, unsigned voff, unsigned sof
                      __uint_as_float(v.w));
 }
 
-template <int ACT, int W, bool DOTS>
+template <int ACT, int W, bool DOTS, bool PAIRS>
 __global__ void __launch_bounds__(64 * W)
 gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                    const float *__restrict__ wsc, float *__restrict__ y,
@@ -78,32 +84,54 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const buf_t xr = kQ8 ? make_buf(static_cast<const char *>(xv) + act_view_off,
                                   (unsigned)m * (unsigned)K)
                        : make_buf(xv, (unsigned)m * (unsigned)K * 2u);
-  const unsigned xoff = kQ8 ? (unsigned)ri * 32u + (unsigned)q * 8u
-                            : (unsigned)ri * (unsigned)K * 2u + (unsigned)q * 16u;
+  // int8: the view, 8 bytes a lane (row i, k = 8q ..).  bf16 single blocks:
+  // 16 bytes a lane (row i, k = 8q ..) from the rows.  bf16 pairs: a stage
+  // holds two consecutive blocks; its activation is read as whole cache lines
+  // (lane L of load v: row 8v + L/8, bytes 16 (L%8) of the two blocks' 128)
+  // and handed to the MFMA layout through the wave's LDS scratch.
+  constexpr int U = PAIRS ? 2 : 1;
+  const int lrow = lane >> 3;
+  const unsigned xoff = kQ8      ? (unsigned)ri * 32u + (unsigned)q * 8u
+                        : PAIRS ? (unsigned)lrow * (unsigned)K * 2u + (unsigned)(lane & 7) * 16u
+                                : (unsigned)ri * (unsigned)K * 2u + (unsigned)q * 16u;
+  const unsigned xoff8 = (unsigned)8 * (unsigned)K * 2u;   // rows 8 .. 15
 
   struct Stage {
-    uint4 lo, hi;   // column `lane`'s k = 0..15 and 16..31 of the block
-    float4 sc;      // scales of columns i, i+16, i+32, i+48
-    uint4 a;        // activation row i, k = 8q .. 8q+7 (bf16: 16 bytes; int8: x, y)
+    uint4 lo[U], hi[U];   // column `lane`'s k = 0..15 and 16..31 of each block
+    float4 sc[U];         // scales of columns i, i+16, i+32, i+48
+    uint4 a[2];           // int8: a[0].xy; bf16: the two loads of the pair
   };
   auto load = [&](Stage &st, int b) {
-    const unsigned wb = (unsigned)b * kChunkBytes;
-    st.lo = buf_ld16(wr, lw, wb);
-    st.hi = buf_ld16(wr, lw + kHalfBytes, wb);
-    if constexpr (!DOTS) st.sc = buf_ld16f(sr, ls, (unsigned)b * (kTile * 4));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int bu = min(b + u, b_hi - 1);
+      const unsigned wb = (unsigned)bu * kChunkBytes;
+      st.lo[u] = buf_ld16(wr, lw, wb);
+      st.hi[u] = buf_ld16(wr, lw + kHalfBytes, wb);
+      if constexpr (!DOTS) st.sc[u] = buf_ld16f(sr, ls, (unsigned)bu * (kTile * 4));
+    }
     if constexpr (kQ8) {
       const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, xoff, (unsigned)b * (unsigned)m * 32u, 0);
-      st.a = make_uint4(row_live ? v.x : 0u, row_live ? v.y : 0u, 0u, 0u);
-    } else {
+      st.a[0] = make_uint4(row_live ? v.x : 0u, row_live ? v.y : 0u, 0u, 0u);
+    } else if constexpr (!PAIRS) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (unsigned)b * 64u, 0);
-      st.a = row_live ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+      st.a[0] = row_live ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      // bytes past the activation's end (a last unpaired block) read as zero
+#pragma unroll
+      for (int v2 = 0; v2 < 2; ++v2) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, xoff + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
+        st.a[v2] = (8 * v2 + lrow < m) ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
 
   Stage A, B;
-  if (b_lo + wave < b_hi) load(A, b_lo + wave);
+  if (b_lo + U * wave < b_hi) load(A, b_lo + U * wave);
   float *dxs = reinterpret_cast<float *>(lds);
-  float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4 : 0));
+  char *scr = lds + (size_t)wave * 2048;   // bf16: this wave's transpose scratch
+  float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4 : (size_t)W * 2048));
   if constexpr (kQ8 && !DOTS) {
     // the split's activation scales, [block][row], rows past m zero
     const float *dxp =
@@ -119,11 +147,13 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int g = 0; g < 4; ++g) acc[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](const Stage &st, int bb) {
+  // one block of a stage: u its place in the stage, bb the block, a the
+  // activation fragment
+  auto compute1 = [&](const Stage &st, int u, int bb, uint4 afrag) {
     // pieces: quarter Q holds column 16Q + i, piece p = k 8p .. 8p+7; after
     // the transpose R[g] holds, in quarter q, column 16g + i's piece q
-    uint32_t R[4][2] = {{st.lo.x, st.lo.y}, {st.lo.z, st.lo.w}, {st.hi.x, st.hi.y},
-                        {st.hi.z, st.hi.w}};
+    uint32_t R[4][2] = {{st.lo[u].x, st.lo[u].y}, {st.lo[u].z, st.lo[u].w},
+                        {st.hi[u].x, st.hi[u].y}, {st.hi[u].z, st.hi[u].w}};
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const auto a02 = __builtin_amdgcn_permlane32_swap(R[0][d], R[2][d], false, false);
@@ -135,9 +165,9 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       R[2][d] = b23[0];
       R[3][d] = b23[1];
     }
-    const float scs[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
+    const float scs[4] = {st.sc[u].x, st.sc[u].y, st.sc[u].z, st.sc[u].w};
     if constexpr (kQ8) {
-      const long a = __builtin_bit_cast(long, make_uint2(st.a.x, st.a.y));
+      const long a = __builtin_bit_cast(long, make_uint2(afrag.x, afrag.y));
       float4 dx4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if constexpr (!DOTS) dx4 = *reinterpret_cast<const float4 *>(dxs + (bb - b_lo) * MR + 4 * q);
       const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
@@ -157,7 +187,7 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         }
       }
     } else {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, st.a);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, afrag);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const bf16x8_t bw = i8x8_to_bf16(make_uint2(R[g][0], R[g][1]));
@@ -169,18 +199,38 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     }
   };
 
-  int b = b_lo + wave;
+  auto compute = [&](const Stage &st, int b0) {
+    if constexpr (!PAIRS) {
+      compute1(st, 0, b0, st.a[0]);
+    } else {
+      // the pair's rows through LDS: row r's 128 bytes at r * 128, then the
+      // MFMA fragment of block u (row i, k = 8q ..) at i * 128 + 64u + 16q
+#pragma unroll
+      for (int v2 = 0; v2 < 2; ++v2)
+        *reinterpret_cast<uint4 *>(scr + (8 * v2 + lrow) * 128 + (lane & 7) * 16) = st.a[v2];
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes are done
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b0 + u >= b_hi) break;
+        const uint4 af = *reinterpret_cast<const uint4 *>(scr + i * 128 + 64 * u + 16 * q);
+        compute1(st, u, b0 + u, af);
+      }
+    }
+  };
+
+  constexpr int step = W * U;
+  int b = b_lo + U * wave;
   if (b < b_hi) {
     while (true) {
-      if (b + W >= b_hi) {
+      if (b + step >= b_hi) {
         compute(A, b);
         break;
       }
-      load(B, b + W);
+      load(B, b + step);
       __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
       compute(A, b);
       A = B;
-      b += W;
+      b += step;
     }
   }
   if constexpr (DOTS) return;
@@ -215,11 +265,11 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       counters, m, s, S, 0, ep);
 }
 
-template <int ACT, int W, bool DOTS>
-hipError_t launch_t16(const GemvArgs &a, hipStream_t stream) {
+template <int ACT, int W, bool DOTS, bool PAIRS>
+hipError_t launch_t16_k(const GemvArgs &a, hipStream_t stream) {
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t lds = t16_lds_bytes<ACT, W>(nblk_max);
-  auto kern = gemv_tile16_kernel<ACT, W, DOTS>;
+  auto kern = gemv_tile16_kernel<ACT, W, DOTS, PAIRS>;
   static size_t granted = 64 * 1024;
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
@@ -230,37 +280,46 @@ hipError_t launch_t16(const GemvArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int ACT, int W, bool DOTS>
+hipError_t launch_t16(bool pairs, const GemvArgs &a, hipStream_t stream) {
+  if constexpr (ACT == kActBf16) {
+    if (pairs) return launch_t16_k<ACT, W, DOTS, true>(a, stream);
+  }
+  return launch_t16_k<ACT, W, DOTS, false>(a, stream);
+}
+
 template <int ACT, bool DOTS>
-hipError_t launch_t16_w(int waves, const GemvArgs &a, hipStream_t stream) {
+hipError_t launch_t16_w(int waves, bool pairs, const GemvArgs &a, hipStream_t stream) {
   switch (waves) {
-    case 4: return launch_t16<ACT, 4, DOTS>(a, stream);
-    case 8: return launch_t16<ACT, 8, DOTS>(a, stream);
-    case 16: return launch_t16<ACT, 16, DOTS>(a, stream);
+    case 4: return launch_t16<ACT, 4, DOTS>(pairs, a, stream);
+    case 8: return launch_t16<ACT, 8, DOTS>(pairs, a, stream);
+    case 16: return launch_t16<ACT, 16, DOTS>(pairs, a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-bool tile16_instantiated(int rows, int act, bool write_dots, int waves) {
+bool tile16_instantiated(int rows, int act, bool write_dots, int waves, int kslices) {
   if (rows != 16 || (waves != 4 && waves != 8 && waves != 16)) return false;
-  if (act == kActQ8) return true;
-  return act == kActBf16 && !write_dots;
+  if (act == kActQ8) return kslices == 1;
+  return act == kActBf16 && !write_dots && (kslices == 1 || kslices == 2);
 }
 
 size_t tile16_lds_bytes(int act, int waves, int NB, int split_k) {
   const int nblk = (NB + split_k - 1) / split_k;
-  const size_t dx = act == kActQ8 ? (size_t)nblk * 16 * 4 : 0;
-  return dx + (size_t)(waves / 2) * 1024 * 4;
+  const size_t first = act == kActQ8 ? (size_t)nblk * 16 * 4 : (size_t)waves * 2048;
+  return first + (size_t)(waves / 2) * 1024 * 4;
 }
 
-hipError_t launch_gemv_tile16(int act, int waves, bool write_dots, const GemvArgs &a,
-                              hipStream_t stream) {
+hipError_t launch_gemv_tile16(int act, int waves, int kslices, bool write_dots,
+                              const GemvArgs &a, hipStream_t stream) {
   if (a.ep.nw != 1 || a.ep.parts.n > 0) return hipErrorInvalidValue;
-  if (act == kActQ8)
-    return write_dots ? launch_t16_w<kActQ8, true>(waves, a, stream)
-                      : launch_t16_w<kActQ8, false>(waves, a, stream);
-  if (act == kActBf16 && !write_dots) return launch_t16_w<kActBf16, false>(waves, a, stream);
+  if (act == kActQ8 && kslices == 1)
+    return write_dots ? launch_t16_w<kActQ8, true>(waves, false, a, stream)
+                      : launch_t16_w<kActQ8, false>(waves, false, a, stream);
+  if (act == kActBf16 && !write_dots && (kslices == 1 || kslices == 2))
+    return launch_t16_w<kActBf16, false>(waves, kslices == 2, a, stream);
   return hipErrorInvalidValue;
 }
 

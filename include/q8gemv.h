@@ -230,7 +230,10 @@ typedef enum {
   Q8_KERNEL_MFMA16_TILE = 6 /* 16x16x32 block dots of up to 16 rows (bf16 or one-word
                               Q8_0) with the VALU kernel's weight stream: one
                               workgroup per (tile, K split), waves (4, 8 or 16)
-                              split K, kslices ignored; one weight                  */
+                              split K, kslices = blocks a wave's stage holds (bf16:
+                              1, or 2 with the activation read as whole lines and
+                              moved into place through the LDS; Q8_0: 1); one
+                              weight                                                */
 } q8_kernel;
 
 typedef struct q8_plan {
@@ -244,8 +247,9 @@ typedef struct q8_plan {
                       (1, 2 or 4; waves = 4 * kslices * tiles side by side);
                       MFMA32(_DIRECT): waves that split one tile's K range (waves 4:
                       1, 2, 4; waves 8: 1, 2, 4, 8; waves = kslices * tiles
-                      side by side); VALU, MFMA: ignored (all their waves
-                      split K)                                                 */
+                      side by side); MFMA16_TILE: blocks per stage (above);
+                      VALU, MFMA, MFMA32_TILE: ignored (all their waves split
+                      K)                                                       */
 } q8_plan;
 
 /* The plan q8_gemv would launch for this shape on the current device. */

@@ -119,16 +119,19 @@ EXACT_PLANS = [None,
                (q8.Q8_KERNEL_MFMA32, 32, 1, 8, 2), (q8.Q8_KERNEL_MFMA32, 32, 3, 4, 1),
                (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 1, 8, 4), (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 2, 8, 8),
                (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1), (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 16, 1),
-               (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1), (q8.Q8_KERNEL_MFMA16_TILE, 16, 4, 4, 1)]
+               (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1), (q8.Q8_KERNEL_MFMA16_TILE, 16, 4, 4, 1),
+               (q8.Q8_KERNEL_MFMA16_TILE, 16, 2, 16, 2)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8])
 @pytest.mark.parametrize("pl", EXACT_PLANS, ids=lambda p: "default" if p is None else
-                         "k{}r{}s{}w{}".format(*p[:4]))
+                         "k{}r{}s{}w{}ks{}".format(*p))
 def test_exact_case_bit_exact(act, pl):
     if pl is not None and pl[0] in (q8.Q8_KERNEL_MFMA32, q8.Q8_KERNEL_MFMA32_DIRECT,
                                     q8.Q8_KERNEL_MFMA32_TILE) and act != Q8:
         pytest.skip("the MFMA32 kernel takes Q8_0 activations only")
+    if pl is not None and pl[0] == q8.Q8_KERNEL_MFMA16_TILE and pl[4] == 2 and act != BF16:
+        pytest.skip("two-block stages are a bf16 form")
     m, K, N = 3, 512, 100
     x, q, s, bias, res = inputs.exact_case(m, K, N, seed=31)
     Wq, Ws = g.pack(q, s)
@@ -172,6 +175,9 @@ RANDOM_PLANS = [
     (16, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1)),
     (5, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 16, 3, 16, 1)),
     (11, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 7, 4, 1)),
+    (16, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 2)),
+    (9, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 3, 4, 2)),
+    (3, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 16, 2)),
 ]
 
 

@@ -239,7 +239,7 @@ q8_plan tile32_plan(int64_t K, int64_t N) {
 }
 
 // 3-16 rows (bf16 or one-word Q8_0) take the tile-per-workgroup 16x16x32
-// kernel (MFMA16_TILE), 16 waves, K split only below 128 tiles (256 / tiles
+// kernel (MFMA16_TILE) (Q8_0: 16 waves; bf16: below), K split only below 128 tiles (256 / tiles
 // ways, at most 8).  Measured on MI355X against the block-interleaved MFMA
 // kernel (us, rows 3 / 8 / 16): bf16, K=4096, N=14336: 13.2 / 13.5 / 15.5
 // against 14.8 / 14.9 / 15.7; K=5120, N=32000: 30.9 / 30.7 / 35.1 against
@@ -253,13 +253,28 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   q8_plan p;
   p.kernel = Q8_KERNEL_MFMA16_TILE;
   p.rows = 16;
-  // bf16, measured on MI355X: two-block stages pay only for many rows on
-  // mid-width weights (K = 4096, N = 14336: m = 16 14.8 against 15.2 us; m = 12
-  // 14.6 against 14.1); 8 waves on wide weights (K = 5120, N = 32000, m = 3 .. 16:
-  // 30.8 .. 34.8 us, within 1% of the best).
-  const bool bf16 = act_fmt == Q8_ACT_BF16;
-  p.kslices = bf16 && m >= 13 && T >= 128 && T < 384 ? 2 : 1;
-  p.waves = bf16 && T >= 384 ? 8 : 16;
+  p.kslices = 1;
+  p.waves = 16;
+  // bf16, swept on MI355X (loop us, best plan against the next form):
+  //   K = 4096, N = 14336: m <= 12 one-block stages of 8 waves (m = 3, 6, 12:
+  //     12.8, 13.0, 13.5); m = 16 two-block stages of 16 waves (14.1, one-block
+  //     14.4);
+  //   K = 5120, N = 32000: m <= 9 one-block stages of 8 waves (30.9, 31.1, 31.6
+  //     at m = 3, 6, 9); m = 12, 16 two-block stages of 4 waves (32.0, 33.3
+  //     against 32.8, 34.3);
+  //   K = 4096, N = 4096 (4 splits): one-block stages, 8 waves up to 8 rows
+  //     (m = 3: 8.0 against 8.2), 16 above (m = 16: 8.4 against 8.8).
+  if (act_fmt == Q8_ACT_BF16) {
+    if (T >= 384) {
+      p.kslices = m >= 12 ? 2 : 1;
+      p.waves = m >= 12 ? 4 : 8;
+    } else if (T >= 128) {
+      p.kslices = m >= 13 ? 2 : 1;
+      p.waves = m >= 13 ? 16 : 8;
+    } else {
+      p.waves = m <= 8 ? 8 : 16;
+    }
+  }
   int64_t S = T >= 128 ? 1 : 256 / T;
   if (S > 8) S = 8;
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;

@@ -124,5 +124,18 @@ __device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint2 v) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3]));
 }
 
+// Copies words of a weight stage into fresh registers before lane swaps
+// (v_permlane16/32_swap overwrite both of their operands).  Without the copy
+// the register allocator of a two-stage loop can tie the swaps to registers
+// that the next stage's load (still in flight) is given, and the loop then
+// waits for that load too; the copy is a move the compiler cannot fold.
+template <int N, int D>
+__device__ __forceinline__ void opaque_copy(uint32_t (&r)[N][D]) {
+#pragma unroll
+  for (int a = 0; a < N; ++a)
+#pragma unroll
+    for (int d = 0; d < D; ++d) asm volatile("v_mov_b32 %0, %1" : "=v"(r[a][d]) : "v"(r[a][d]));
+}
+
 }  // namespace dev
 }  // namespace q8

@@ -78,9 +78,11 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const buf_t wr = make_buf(wq + (size_t)t * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
   const buf_t sr = DOTS ? wr : make_buf(wsc + (size_t)t * NB * kTile, (unsigned)NB * kTile * 4);
   const unsigned lw = (unsigned)lane * 16u, ls = (unsigned)i * 16u;
-  // the activation: bf16 rows, or the int8 view (block b's m rows at b*m*32)
-  const bool row_live = i < m;
-  const int ri = row_live ? i : 0;
+  // the activation: bf16 rows, or the int8 view (block b's m rows at b*m*32).
+  // Lanes of rows past m load row 0 (or, for the pair's whole lines, read
+  // zero past the buffer's extent): those rows of D are never read, and an
+  // unconditional load keeps the stage's loads out of branches.
+  const int ri = i < m ? i : 0;
   const buf_t xr = kQ8 ? make_buf(static_cast<const char *>(xv) + act_view_off,
                                   (unsigned)m * (unsigned)K)
                        : make_buf(xv, (unsigned)m * (unsigned)K * 2u);
@@ -101,7 +103,8 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     float4 sc[U];         // scales of columns i, i+16, i+32, i+48
     uint4 a[2];           // int8: a[0].xy; bf16: the two loads of the pair
   };
-  auto load = [&](Stage &st, int b) {
+  auto load = [&](Stage &st, int bv) {
+    const int b = __builtin_amdgcn_readfirstlane(bv);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int bu = min(b + u, b_hi - 1);
@@ -112,17 +115,16 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     }
     if constexpr (kQ8) {
       const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, xoff, (unsigned)b * (unsigned)m * 32u, 0);
-      st.a[0] = make_uint4(row_live ? v.x : 0u, row_live ? v.y : 0u, 0u, 0u);
+      st.a[0] = make_uint4(v.x, v.y, 0u, 0u);
     } else if constexpr (!PAIRS) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (unsigned)b * 64u, 0);
-      st.a[0] = row_live ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+      st.a[0] = make_uint4(v.x, v.y, v.z, v.w);
     } else {
-      // bytes past the activation's end (a last unpaired block) read as zero
 #pragma unroll
       for (int v2 = 0; v2 < 2; ++v2) {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
             xr, xoff + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
-        st.a[v2] = (8 * v2 + lrow < m) ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
+        st.a[v2] = make_uint4(v.x, v.y, v.z, v.w);
       }
     }
   };
@@ -154,6 +156,7 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     // the transpose R[g] holds, in quarter q, column 16g + i's piece q
     uint32_t R[4][2] = {{st.lo[u].x, st.lo[u].y}, {st.lo[u].z, st.lo[u].w},
                         {st.hi[u].x, st.hi[u].y}, {st.hi[u].z, st.hi[u].w}};
+    opaque_copy(R);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const auto a02 = __builtin_amdgcn_permlane32_swap(R[0][d], R[2][d], false, false);
@@ -218,6 +221,9 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     }
   };
 
+  // Two stages in flight, taking turns: each path issues the next stage's
+  // loads just before computing the older one, and no registers are copied
+  // between stages, so the compiler waits only for the older stage.
   constexpr int step = W * U;
   int b = b_lo + U * wave;
   if (b < b_hi) {
@@ -227,9 +233,14 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         break;
       }
       load(B, b + step);
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the compute
       compute(A, b);
-      A = B;
+      b += step;
+      if (b + step >= b_hi) {
+        compute(B, b);
+        break;
+      }
+      load(A, b + step);
+      compute(B, b);
       b += step;
     }
   }

@@ -86,7 +86,16 @@ def kernel_name(plan: dict, w) -> str:
         return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false, false>"
     if plan["kernel"] == 5:
         return f"gemv_mfma32w_kernel<{wv}, false>"
+    if plan["kernel"] == 6:
+        return f"gemv_tile16_kernel<{act}, {wv}, false, {'true' if ks == 2 else 'false'}>"
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
+
+
+def plan_grid(plan: dict, w) -> str:
+    """rocprofv3's Grid_Size X x Y x Z (threads) of a tile-per-workgroup
+    product launch (kernels 0, 5 and 6: one workgroup per tile and K split)."""
+    tiles = (w.N + 63) // 64
+    return f"{tiles * 64 * plan['waves']}x{plan['split_k']}x1"
 
 
 def _code_only(text: str) -> str:
@@ -710,11 +719,23 @@ CONFIG_IDS = {"decode_k1024_n1024": "C1", "decode_k4096_n4096": "C2",
               "decode_k4096_n14336": "T"}
 
 
-def summarize_kernel_trace(path):
+def summarize_kernel_trace(path, bench_json=None):
     """Per-kernel dispatch statistics of a rocprofv3 kernel-trace CSV: count,
     mean, median, p10 and p90 of the dispatch durations (us), in order of
-    total time.  Prints one JSON line."""
+    total time.  Given the JSON line that the traced bench.py run printed, each
+    configuration's product launches (kernel name and grid from its plan) are
+    labelled with the configuration.  Prints one JSON line."""
     import csv
+    from block_quantized_weight_02_amd import inputs
+    labels = {}
+    if bench_json:
+        line = [l for l in open(bench_json).read().splitlines() if l.startswith('{"metric"')][-1]
+        rec = json.loads(line)
+        cfgs = dict(rec.get("by_config", {}))
+        cfgs["T"] = {"workload": rec["config"]["workload"], "plan": rec["config"]["plan"]}
+        for cid, c in cfgs.items():
+            w = inputs.WORKLOADS[c["workload"]]
+            labels.setdefault((kernel_name(c["plan"], w), plan_grid(c["plan"], w)), []).append(cid)
     durs = {}
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
@@ -729,12 +750,75 @@ def summarize_kernel_trace(path):
     out = []
     for (name, grid, wg), d in durs.items():
         a = np.array(d)
-        out.append({"kernel": name, "grid_threads": grid, "workgroup": wg,
+        cfg = [c for (k, g), cs in labels.items() if g == grid and k in name for c in cs]
+        out.append({"kernel": name, "configs": cfg, "grid_threads": grid, "workgroup": wg,
                     "dispatches": int(a.size), "total_us": float(a.sum()),
                     "mean_us": float(a.mean()), "median_us": float(np.median(a)),
                     "p10_us": float(np.percentile(a, 10)), "p90_us": float(np.percentile(a, 90))})
     out.sort(key=lambda r: -r["total_us"])
     print(json.dumps({"trace": os.path.basename(path), "kernels": out}), flush=True)
+
+
+def summarize_pmc(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM traffic of one workload's product kernel from four rocprofv3
+    counter-collection CSVs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of a
+    `--workload` run, each scaled by what the same counter reads for the
+    `--copy-calibration` copy (256 MiB read and written).  The product kernel
+    is the gemv kernel (name and grid) with the most dispatches.  Prints one
+    JSON record (the `profiles/pmc_<workload>.json` format)."""
+    import csv
+    from block_quantized_weight_02_amd import inputs
+    w = inputs.WORKLOADS[workload]
+
+    def rows(path, cname):
+        out = []
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == cname:
+                    out.append((r["Kernel_Name"], r.get("Grid_Size", ""), float(r["Counter_Value"])))
+        return out
+
+    def product(path, cname):
+        groups = {}
+        for name, grid, v in rows(path, cname):
+            if "gemv_" in name:
+                groups.setdefault((name, grid), []).append(v)
+        (name, grid), vals = max(groups.items(), key=lambda kv: len(kv[1]))
+        return name, grid, vals
+
+    def copy(path, cname):
+        return [v for name, _, v in rows(path, cname) if "copyBuffer" in name]
+
+    kname, grid, g_f = product(fetch_csv, "FETCH_SIZE")
+    _, _, g_w = product(write_csv, "WRITE_SIZE")
+    c_f, c_w = copy(copy_fetch_csv, "FETCH_SIZE"), copy(copy_write_csv, "WRITE_SIZE")
+    copy_bytes = 256 * 2 ** 20
+    ff = copy_bytes / (float(np.median(c_f)) * 1024)
+    wf = copy_bytes / (float(np.median(c_w)) * 1024)
+    rd = float(np.mean(g_f)) * 1024 * ff
+    wr = float(np.mean(g_w)) * 1024 * wf
+    alg = algorithmic_bytes(w)["total"]
+    run = (f"python3 bench.py --workload {workload} --no-rows --no-cpu --no-fused --no-prefill "
+           "--no-ceiling --no-context --steps 100 --warmup 10")
+    rec = {
+        "workload": f"{workload} (m={w.m}, K={w.K}, N={w.N}, {w.act} activations)",
+        "kernel": kname, "grid_threads": grid,
+        "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o bench -- {run}",
+                     f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o bench -- {run}",
+                     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o copy -- python3 bench.py --copy-calibration",
+                     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o copy -- python3 bench.py --copy-calibration",
+                     f"python3 bench.py --summarize-pmc {workload} <fetch csv> <write csv> <copy fetch csv> <copy write csv>"],
+        "dispatches": {"gemv": len(g_f), "copy": len(c_f)},
+        "FETCH_SIZE_KiB_per_dispatch": {"gemv_mean": float(np.mean(g_f)), "copy_median": float(np.median(c_f))},
+        "WRITE_SIZE_KiB_per_dispatch": {"gemv_mean": float(np.mean(g_w)), "copy_median": float(np.median(c_w))},
+        "calibration": {"copy_bytes_each_way": copy_bytes, "fetch_factor": ff, "write_factor": wf,
+                        "note": "a plain 256 MiB device copy reads and writes 256 MiB; the factors turn each counter's KiB into bytes"},
+        "traffic_read_bytes_per_launch": rd, "traffic_write_bytes_per_launch": wr,
+        "traffic_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": (rd + wr) / alg,
+        "csrc_hash": csrc_hash(),
+    }
+    print(json.dumps(rec, indent=2), flush=True)
 
 
 def main():
@@ -754,12 +838,19 @@ def main():
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (cache-hot number)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 256 MiB device copy (for profiler counter calibration)")
-    ap.add_argument("--summarize-kernel-trace", metavar="CSV", default=None,
-                    help="print per-kernel dispatch statistics of a rocprofv3 kernel trace")
+    ap.add_argument("--summarize-kernel-trace", metavar="CSV", nargs="+", default=None,
+                    help="print per-kernel dispatch statistics of a rocprofv3 kernel trace "
+                         "(optionally followed by the traced run's output, to label configurations)")
+    ap.add_argument("--summarize-pmc", metavar="ARG", nargs=5, default=None,
+                    help="WORKLOAD FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV: HBM traffic "
+                         "of the workload's product kernel from rocprofv3 counter CSVs")
     args = ap.parse_args()
 
     if args.summarize_kernel_trace:
-        summarize_kernel_trace(args.summarize_kernel_trace)
+        summarize_kernel_trace(*args.summarize_kernel_trace[:2])
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -796,6 +887,9 @@ def main():
                                   "pct_hbm_peak", "weights_per_s", "macs_per_s",
                                   "kernel_us_mean", "kernel_gbs", "kernel_pct_hbm_peak",
                                   "launches_timed", "back_to_back", "plan")}
+            # HBM bytes per launch from the committed counter record, while the
+            # kernel sources are the ones it was taken on
+            by_config[cid]["traffic"] = traffic_from_profile(other)
 
     fused = {}
     if not args.no_fused:

@@ -209,8 +209,10 @@ constexpr int64_t kValuTwoWordRows = 2;
 // 44.2 us with 16), else 16 (N=14336: 18.0 against 21.1); K split only below
 // 128 tiles: 3 ways from 8 tiles (N=4096: 11.5 against 11.8 with 4 and 12.4
 // with 2; N=1024: 10.9 against 11.0 with 4), 4 ways below (N=40: 10.6 against
-// 11.4 with 5).  Up to 16 rows the block-interleaved 16-row kernel stays
-// ahead (m=16, N=32000: 34.4 against 36.3 us; N=14336: 16.0 against 16.9).
+// 11.4 with 5).  Up to 16 rows the 16-row kernels stay ahead (the
+// block-interleaved one at m=16, N=32000: 34.4 against 36.3 us; N=14336: 16.0
+// against 16.9), and the 16-row tile kernel below is faster still.
+
 // Raises a tile plan's K split until its LDS (the split's activation scales
 // and the carries) fits a workgroup.
 void fit_tile_lds(q8_plan &p, int64_t NB, int act_fmt) {

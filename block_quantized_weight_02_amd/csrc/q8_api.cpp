@@ -102,11 +102,11 @@ int check_m_act(int64_t m, int act_fmt) {
 }
 
 // The products that take no two-word activation.
-int check_one_word_act(int act_fmt, const char *what) {
+// The format, and the row limit of two-word activations.
+int check_act_rows(int act_fmt, int64_t m) {
   int st = check_act(act_fmt);
   if (st) return st;
-  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS)
-    return fail(Q8_ERR_ACT_FMT, "%s takes no two-word activation (act_fmt 2)", what);
+  if (act_fmt == Q8_ACT_Q8_0_TWO_WORDS) return check_m(m, Q8_MAX_TWO_WORD_ROWS);
   return Q8_OK;
 }
 
@@ -513,8 +513,6 @@ int run_gemv(const void *x, const int8_t *W_q8, const float *W_q8_scale,
              const PairArgs *pair = nullptr) {
   const bool write_dots = dots != nullptr;
   const int nw = pair ? 2 : 1;
-  if (pair && act_fmt == Q8_ACT_Q8_0_TWO_WORDS)
-    return fail(Q8_ERR_ACT_FMT, "the gated pair takes no two-word activation (act_fmt 2)");
   if (pair && plan.kernel >= Q8_KERNEL_MFMA32)
     return fail(Q8_ERR_PLAN, "the MFMA32 kernels do not run the gated pair: "
                 "use the VALU, MFMA or MFMA_COLS kernel");
@@ -664,7 +662,6 @@ int check_glu_args(const void *x, const int8_t *Wg, const float *Wg_s, const int
                    int act_fmt, const q8_glu_epilogue *ep) {
   int st = check_gemv_args(x, Wg, Wg_s, y, "y", m, K, N, act_fmt, true, false);
   if (st) return st;
-  if ((st = check_one_word_act(act_fmt, "the gated pair"))) return st;
   if ((st = check_ptr(Wu, "Wu_q8")) || (st = check_ptr(Wu_s, "Wu_q8_scale"))) return st;
   return check_glu_epilogue(ep, y);
 }
@@ -699,8 +696,7 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
                      int act_fmt, int64_t *cols) {
   int st;
   if ((st = check_parts(parts, n_parts, cols))) return st;
-  if ((st = check_m(m)) || (st = check_kn(K, *cols)) ||
-      (st = check_one_word_act(act_fmt, "the product in parts")))
+  if ((st = check_m(m)) || (st = check_kn(K, *cols)) || (st = check_act_rows(act_fmt, m)))
     return st;
   if ((st = check_ptr(x, "x"))) return st;
   for (int i = 0; i < n_parts; ++i) {
@@ -756,7 +752,7 @@ int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64
                 "use the VALU or MFMA kernel");
   int st = check_plan(&plan, m, K, act_fmt, false);
   if (st) return st;
-  if (act_fmt == Q8_ACT_Q8_0 && act_scales_offset(m, K) > 0xffffffffull)
+  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "activation too large");
   q8::GemvArgs a{};
   a.x = x;
@@ -769,7 +765,7 @@ int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64
   a.Npad = (int)cols;
   a.T = (int)(cols / Q8_TILE_COLS);
   a.split_k = plan.split_k;
-  a.act_scale_off = (unsigned)act_scales_offset(m, K);
+  a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
   a.ep.N = (int)parts[0].N;
   a.ep.write_y = 1;
   a.ep.nw = 1;
@@ -1027,7 +1023,7 @@ size_t q8_glu_workspace_bytes(const q8_plan *plan, int64_t m, int64_t K, int64_t
 int q8_gemv_glu_default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, q8_plan *plan) {
   int st;
   if ((st = check_m(m)) || (st = check_kn(K, N)) ||
-      (st = check_one_word_act(act_fmt, "the gated pair")))
+      (st = check_act_rows(act_fmt, m)))
     return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = glu_default_plan(m, K, N, act_fmt);
@@ -1182,7 +1178,7 @@ int q8_gemv_parts_default_plan(const q8_part *parts, int n_parts, int64_t m, int
   int64_t cols = 0;
   if ((st = check_parts(parts, n_parts, &cols))) return st;
   if ((st = check_m(m)) || (st = check_kn(K, cols)) ||
-      (st = check_one_word_act(act_fmt, "the product in parts")))
+      (st = check_act_rows(act_fmt, m)))
     return st;
   if (!plan) return fail(Q8_ERR_NULL, "plan is NULL");
   *plan = parts_default_plan(m, K, cols, act_fmt);

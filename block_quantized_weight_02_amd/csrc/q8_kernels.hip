@@ -1104,7 +1104,7 @@ hipError_t launch_valu_k(const GemvArgs &a, hipStream_t stream) {
 // product carries none of the pair's code.
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_valu(const GemvArgs &a, hipStream_t stream) {
-  if constexpr (!DOTS && ACT != kActQ8x2) {
+  if constexpr (!DOTS) {
     if (a.ep.nw == 2) return launch_valu_k<MR, ACT, DOTS, W, true, false>(a, stream);
     if (a.ep.parts.n > 0) return launch_valu_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }
@@ -1151,7 +1151,7 @@ hipError_t launch_mfma_k(const GemvArgs &a, hipStream_t stream) {
 
 template <int MR, int ACT, bool DOTS, int W>
 hipError_t launch_mfma(const GemvArgs &a, hipStream_t stream) {
-  if constexpr (!DOTS && ACT != kActQ8x2) {
+  if constexpr (!DOTS) {
     if (a.ep.nw == 2) return launch_mfma_k<MR, ACT, DOTS, W, true, false>(a, stream);
     if (a.ep.parts.n > 0) return launch_mfma_k<MR, ACT, DOTS, W, false, true>(a, stream);
   }

@@ -169,11 +169,12 @@ int q8_quantize_act_two_words(const uint16_t *x_bf16, void *x_q8x2, int64_t m,
  * q8_gemv: y = x . W over the packed Q8_0 weight (from_q8.rs, module doc and
  * fn q8_fold).  x per act_fmt; y is m x N_pad fp32.  Requires 1 <= m <= 32
  * (two-word activations: m <= Q8_MAX_TWO_WORD_ROWS), K > 0, K % 32 == 0,
- * N >= 1.  Two-word activations run each block's two int8 passes on the
- * matrix cores and join them exactly in int32 before the block's scale
- * (128 * D_hi + D_lo, then times dx * s / 128); only the MFMA kernel takes
- * them (plans naming another kernel are Q8_ERR_PLAN), and the gated pair
- * and the parts do not (Q8_ERR_ACT_FMT).  When the chosen plan splits K across
+ * N >= 1.  Two-word activations run each block's two int8 passes (v_dot4
+ * or the matrix cores) and join them exactly in int32 before the block's
+ * scale (128 * D_hi + D_lo, then times dx * s / 128); the VALU kernel (up to
+ * 4 rows) and the block-interleaved MFMA kernel take them (plans naming
+ * another kernel are Q8_ERR_PLAN), also for the gated pair and the parts.
+ * When the chosen plan splits K across
  * workgroups it uses a workspace the library allocates on first need and
  * keeps per (device, stream) until q8_release_workspaces(); a call that would
  * allocate while its stream is being captured returns Q8_ERR_WORKSPACE

@@ -210,7 +210,7 @@ def test_parts_validation():
     expect(1, q8.q8_gemv_parts, A, [_part(64), _part(0)], 1, 4096, 0, S0)
     expect(1, q8.q8_gemv_parts, A, three, 33, 4096, 0, S0)
     expect(1, q8.q8_gemv_parts, A, three, 1, 48, 0, S0)
-    expect(2, q8.q8_gemv_parts, A, three, 1, 4096, 2, S0)
+    expect(2, q8.q8_gemv_parts, A, three, 1, 4096, 3, S0)
     expect(3, q8.q8_gemv_parts, None, three, 1, 4096, 0, S0)
     expect(3, q8.q8_gemv_parts, A, [_part(64), _part(64, y=None)], 1, 4096, 0, S0)
     assert "part 1" in q8.q8_last_error()
@@ -278,9 +278,11 @@ def test_two_word_rules():
         bad = q8.q8_plan()
         bad.kernel, bad.rows, bad.split_k, bad.waves, bad.kslices = kernel, rows, 2, waves, 1
         expect(7, q8.q8_gemv_planned, A, A, A, A, 1, 64, 8, TW, bad, S0, A, 1 << 30)
-    expect(2, q8.q8_gemv_glu, A, A, A, A, A, A, 1, 64, 8, TW, None, S0)
-    expect(2, q8.q8_gemv_glu_default_plan, 1, 64, 8, TW)
-    expect(2, q8.q8_gemv_parts, A, [q8.make_part(A, A, A, 64)], 1, 64, TW, S0)
+    # the pair and the parts take two words, within the same row limit
+    expect(1, q8.q8_gemv_glu, A, A, A, A, A, A, 17, 64, 8, TW, None, S0)
+    expect(1, q8.q8_gemv_glu_default_plan, 17, 64, 8, TW)
+    expect(1, q8.q8_gemv_parts, A, [q8.make_part(A, A, A, 64)], 17, 64, TW, S0)
+    expect(1, q8.q8_gemv_parts_default_plan, [q8.make_part(A, A, A, 64)], 17, 64, TW)
     expect(3, q8.q8_gemm, None, A, A, A, 64, 64, 8, TW, S0)   # the GEMM takes it
 
 

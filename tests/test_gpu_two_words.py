@@ -264,3 +264,95 @@ def test_gemm_two_words_prefill_full_size():
     z, bnd = oracle.gemv_q8_two_words(*words_host(buf, m, K), q, s, cols)
     err = np.abs(y[:, cols].astype(np.float64) - z)
     assert np.all(err <= REL * bnd + ABS), np.max(err / (REL * bnd + ABS))
+
+
+# ------------------------------------------------------------------------------
+# the gated pair and the parts over two-word activations
+# ------------------------------------------------------------------------------
+
+def _words_checked(x):
+    """The device two-word buffer of x, its words checked bit for bit against
+    the oracle's quantizer, and the oracle's words (the references use them)."""
+    m, K = x.shape
+    buf = quantize2(x)
+    hi, lo, dx = words_host(buf, m, K)
+    rh, rl, rd = oracle.quantize_act_two_words(x)
+    np.testing.assert_array_equal(hi, rh)
+    np.testing.assert_array_equal(lo, rl)
+    np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32))
+    return buf, (rh, rl, rd)
+
+
+PAIR_PLANS = [(1, None), (2, None), (3, None), (16, None),
+              (1, (q8.Q8_KERNEL_VALU, 1, 2, 8, 1)),
+              (4, (q8.Q8_KERNEL_VALU, 4, 1, 16, 1)),
+              (8, (q8.Q8_KERNEL_MFMA, 32, 1, 8, 1)),
+              (16, (q8.Q8_KERNEL_MFMA, 32, 3, 16, 1))]
+
+
+@pytest.mark.parametrize("m,pl", PAIR_PLANS)
+@pytest.mark.parametrize("N", [200, 40])
+def test_gated_pair_two_words(m, pl, N):
+    from tests.test_gpu_glu import glu_tolerance, run_glu
+    from tests.test_gpu_epilogue import check_quant
+    K = 2176
+    x, qg, sg = inputs.random_case(m, K, N, seed=900 + m + N)
+    _, qu, su = inputs.random_case(m, K, N, seed=950 + m + N)
+    bg = inputs.gen_bias(N, seed=901)
+    bu = inputs.gen_bias(N, seed=902)
+    buf, (rh, rl, rd) = _words_checked(x)
+    W = (*g.pack(qg, sg), *g.pack(qu, su))
+    plan = None if pl is None else g.plan(*pl)
+    y, codes, scales = run_glu(buf, W, m, K, N, TW, bg, bu, quant=True, plan=plan)
+    gg, bnd_g = oracle.gemv_q8_two_words(rh, rl, rd, qg, sg)
+    uu, bnd_u = oracle.gemv_q8_two_words(rh, rl, rd, qu, su)
+    out = oracle.swiglu(gg, uu, bg, bu)
+    tol = glu_tolerance(gg, uu, bnd_g, bnd_u, bg, bu, out)
+    err = np.abs(y[:, :N].astype(np.float64) - out)
+    what = f"pair m={m} plan={pl} N={N}"
+    assert np.all(err <= tol), f"{what}: max err/tol {np.max(err / tol):.3g}"
+    assert (y[:, N:].view(np.uint32) == 0).all(), f"{what}: pad columns not zero"
+    check_quant(codes, scales, out, (tol - ABS) / REL, N, what)
+
+
+PARTS_PLANS = [(1, None), (2, None), (5, None), (16, None),
+               (2, (q8.Q8_KERNEL_VALU, 2, 1, 8, 1)),
+               (4, (q8.Q8_KERNEL_VALU, 4, 3, 4, 1)),
+               (16, (q8.Q8_KERNEL_MFMA, 32, 2, 16, 1))]
+
+
+@pytest.mark.parametrize("m,pl", PARTS_PLANS)
+@pytest.mark.parametrize("Ns", [(200, 40, 64, 130), (96,)])
+def test_parts_two_words(m, pl, Ns):
+    from tests.test_gpu_parts import run_parts, check_part
+    K = 2176
+    seed = 980 + m + sum(Ns)
+    x = inputs.gen_x(m, K, seed)
+    ws = [(inputs.gen_q(K, N, seed + 10 * i + 1), inputs.gen_scales(K, N, seed + 10 * i + 1))
+          for i, N in enumerate(Ns)]
+    biases = [inputs.gen_bias(N, seed=seed + i) if i % 2 == 0 else None
+              for i, N in enumerate(Ns)]
+    buf, (rh, rl, rd) = _words_checked(x)
+    packed = [g.pack(q, s) for q, s in ws]
+    plan = None if pl is None else g.plan(*pl)
+    ys = run_parts(buf, packed, Ns, biases, m, K, TW, plan)
+    for i, ((q, s), N, b, y) in enumerate(zip(ws, Ns, biases, ys)):
+        z, bnd = oracle.gemv_q8_two_words(rh, rl, rd, q, s)
+        z, bnd = oracle.epilogue(z, bnd, b)
+        check_part(y, z, bnd, N, f"part {i} m={m} plan={pl} Ns={Ns}")
+
+
+def test_parts_two_words_match_single_products():
+    """Each part equals the single two-word product under the same plan, bit
+    for bit (the parts launch walks the same units)."""
+    m, K, Ns = 3, 1024, (130, 64)
+    x = inputs.gen_x(m, K, 991)
+    ws = [(inputs.gen_q(K, N, 992 + i), inputs.gen_scales(K, N, 992 + i)) for i, N in enumerate(Ns)]
+    buf, _ = _words_checked(x)
+    packed = [g.pack(q, s) for q, s in ws]
+    from tests.test_gpu_parts import run_parts
+    for pl in ((q8.Q8_KERNEL_VALU, 4, 1, 8, 1), (q8.Q8_KERNEL_MFMA, 32, 1, 16, 1)):
+        ys = run_parts(buf, packed, Ns, [None] * len(Ns), m, K, TW, g.plan(*pl))
+        for (W, Ws), N, y in zip(packed, Ns, ys):
+            y1 = g.gemv(buf, W, Ws, m, K, N, TW, g.plan(*pl))
+            np.testing.assert_array_equal(y.view(np.uint32), y1.view(np.uint32))

@@ -455,9 +455,10 @@ def measure_glu(w, steps, warmup, rotate=True):
                      "waves": plan.waves, "kslices": plan.kslices}}
 
 
-def measure_parts(pw, steps, warmup, rotate=True):
+def measure_parts(pw, steps, warmup, rotate=True, gemm=False):
     """The product in parts (several projections of one activation, one
-    launch) against the same products launched one by one."""
+    launch) against the same products launched one by one; with gemm, the
+    many-row forms (q8_gemm_parts against q8_gemm per part)."""
     import torch
     import block_quantized_weight_02_amd as q8
     from block_quantized_weight_02_amd import inputs
@@ -492,17 +493,19 @@ def measure_parts(pw, steps, warmup, rotate=True):
         arrs.append((q8.q8_part * len(parts))(*parts))
     singles = [[(xin, Wd[i][c][0].data_ptr(), Wd[i][c][1].data_ptr(), ys[i].data_ptr(), m, K, N,
                  act, sp) for i, N in enumerate(Ns)] for c in range(copies)]
-    plan = q8.q8_gemv_parts_default_plan(list(arrs[0]), m, K, act)
+    plan = None if gemm else q8.q8_gemv_parts_default_plan(list(arrs[0]), m, K, act)
+    parts_fn = lib.q8_gemm_parts if gemm else lib.q8_gemv_parts
+    single_fn = lib.q8_gemm if gemm else lib.q8_gemv
     torch.cuda.synchronize()
 
     def call(i):
-        rc = lib.q8_gemv_parts(xin, arrs[i % copies], len(Ns), m, K, act, sp)
+        rc = parts_fn(xin, arrs[i % copies], len(Ns), m, K, act, sp)
         if rc:
             raise RuntimeError(q8.q8_last_error())
 
     def one_by_one(i):
         for a in singles[i % copies]:
-            rc = lib.q8_gemv(*a)
+            rc = single_fn(*a)
             if rc:
                 raise RuntimeError(q8.q8_last_error())
 
@@ -516,12 +519,18 @@ def measure_parts(pw, steps, warmup, rotate=True):
     del Wd, arrs, singles
     torch.cuda.empty_cache()
     log(f"[bench] parts {pw.name}: {parts_ms * 1e3:.2f} us vs one by one {sep_ms * 1e3:.2f} us, "
-        f"plan={plan}")
-    return {"workload": pw.name, "Ns": list(Ns), "parts_us": parts_ms * 1e3,
-            "one_by_one_us": sep_ms * 1e3, "bytes": nbytes,
-            "parts_gbs": nbytes / (parts_ms * 1e-3) / 1e9,
-            "plan": {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
-                     "waves": plan.waves, "kslices": plan.kslices}}
+        f"plan={plan if plan is not None else 'q8_gemm_parts'}")
+    out = {"workload": pw.name, "Ns": list(Ns), "parts_us": parts_ms * 1e3,
+           "one_by_one_us": sep_ms * 1e3, "bytes": nbytes,
+           "parts_gbs": nbytes / (parts_ms * 1e-3) / 1e9}
+    if gemm:
+        flops = 2.0 * m * K * sum(Ns)
+        out["tflops"] = flops / (parts_ms * 1e-3) / 1e12
+        out["frac_of_mfma_peak"] = out["tflops"] / MFMA_PEAK_TFLOPS[pw.act]
+    else:
+        out["plan"] = {"kernel": plan.kernel, "rows": plan.rows, "split_k": plan.split_k,
+                       "waves": plan.waves, "kslices": plan.kslices}
+    return out
 
 
 def measure_two_words(w, steps, warmup, rotate=True):
@@ -919,6 +928,9 @@ def main():
         prefill["q8_0_two_words"] = measure_gemm(
             inputs.WORKLOADS["prefill_q8act_m512_k4096_n14336"], max(100, args.steps // 10),
             max(10, args.warmup // 10), rotate=not args.no_rotate, two_words=True)
+        prefill["parts_m512"] = measure_parts(
+            inputs.PARTS_WORKLOADS["qkv_prefill_m512_k4096"], max(100, args.steps // 10),
+            max(10, args.warmup // 10), rotate=not args.no_rotate, gemm=True)
 
     context = {}
     if not args.no_ceiling:

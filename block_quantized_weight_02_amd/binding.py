@@ -112,6 +112,7 @@ _SIGS = {
     "q8_gemv_glu_default_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(q8_plan)]),
     "q8_glu_workspace_bytes": (_sz, [ctypes.POINTER(q8_plan), _i64, _i64, _i64]),
     "q8_gemv_parts": (_int, [_p, ctypes.POINTER(q8_part), _int, _i64, _i64, _int, _p]),
+    "q8_gemm_parts": (_int, [_p, ctypes.POINTER(q8_part), _int, _i64, _i64, _int, _p]),
     "q8_gemv_parts_planned": (_int, [_p, ctypes.POINTER(q8_part), _int, _i64, _i64, _int,
                                      ctypes.POINTER(q8_plan), _p, _p, _sz]),
     "q8_gemv_parts_default_plan": (_int, [ctypes.POINTER(q8_part), _int, _i64, _i64, _int,
@@ -355,6 +356,11 @@ def _parts_ref(parts):
 def q8_gemv_parts(x, parts, m, K, act_fmt, stream=None) -> None:
     arr, n = _parts_ref(parts)
     _check(lib().q8_gemv_parts(_addr(x), arr, n, m, K, act_fmt, _stream(stream)))
+
+
+def q8_gemm_parts(x, parts, m, K, act_fmt, stream=None) -> None:
+    arr, n = _parts_ref(parts)
+    _check(lib().q8_gemm_parts(_addr(x), arr, n, m, K, act_fmt, _stream(stream)))
 
 
 def q8_gemv_parts_planned(x, parts, m, K, act_fmt, plan: q8_plan, stream=None,

@@ -1093,7 +1093,61 @@ int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *
   return ok();
 }
 
+// The GEMM in parts: the parts' column tiles side by side in one launch.
+int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
+                   int act_fmt, hipStream_t stream) {
+  int st;
+  int64_t cols = 0;
+  if ((st = check_parts(parts, n_parts, &cols))) return st;
+  if ((st = check_m(m, Q8_MAX_GEMM_ROWS)) || (st = check_kn(K, cols)) ||
+      (st = check_act(act_fmt)))
+    return st;
+  if ((st = check_ptr(x, "x"))) return st;
+  for (int i = 0; i < n_parts; ++i) {
+    const q8_part &pt = parts[i];
+    if ((st = check_ptr(pt.W_q8, "W_q8")) || (st = check_ptr(pt.W_q8_scale, "W_q8_scale")) ||
+        (st = check_ptr(pt.y, "y")) || (pt.bias && (st = check_ptr(pt.bias, "bias")))) {
+      const std::string what = g_last_error;
+      return fail(st, "part %d: %s", i, what.c_str());
+    }
+  }
+  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
+    return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
+                (long long)(m * K));
+  q8::GemmArgs a{};
+  a.x = x;
+  a.m = (int)m;
+  a.K = (int)K;
+  a.NB = (int)(K / Q8_BLOCK);
+  a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+  q8::Parts &pp = a.parts;
+  pp.n = n_parts;
+  pp.cum[0] = 0;
+  for (int i = 0; i < q8::kMaxParts; ++i) {
+    const bool on = i < n_parts;
+    pp.wq[i] = on ? parts[i].W_q8 : nullptr;
+    pp.wsc[i] = on ? parts[i].W_q8_scale : nullptr;
+    pp.y[i] = on ? parts[i].y : nullptr;
+    pp.bias[i] = on ? parts[i].bias : nullptr;
+    pp.N[i] = on ? (int)parts[i].N : 0;
+    pp.cum[i + 1] =
+        pp.cum[i] + (on ? (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS) : 0);
+  }
+  (void)hipGetLastError();
+  hipError_t e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return hip_fail(e, "gemm launch");
+  }
+  return ok();
+}
+
 }  // namespace
+
+int q8_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
+                  int act_fmt, hipStream_t stream) {
+  return run_gemm_parts(x, parts, n_parts, m, K, act_fmt, stream);
+}
 
 int q8_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *y, int64_t m,
             int64_t K, int64_t N, int act_fmt, hipStream_t stream) {

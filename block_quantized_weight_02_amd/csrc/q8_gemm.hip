@@ -275,11 +275,16 @@ __device__ __forceinline__ void gemm_store(const GemmStaging<ACT, BM> &st,
 
 // Two workgroups per CU (8 waves): the register budget is then 256 per lane,
 // which the accumulators, the in-flight stage and its descriptors need.
-template <int ACT, int BM, bool DOTS>
+// PARTS: several weights of one activation (the pages' GemmParts above the
+// GEMV's rows, plan.rs merged_projections): the column blocks of part p are
+// blocks cum[p] .. cum[p+1]-1 of the grid, and a workgroup takes its part's
+// weight, output, width and bias; y = x.W_p + bias_p, pad columns 0.
+template <int ACT, int BM, bool DOTS, bool PARTS>
 __global__ void __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
             const float *__restrict__ wsc, float *__restrict__ y, int32_t *__restrict__ dots,
-            int m, int K, int NB, int Npad, int T, int MB, int NBN, unsigned act_scale_off) {
+            int m, int K, int NB, int Npad, int T, int MB, int NBN, unsigned act_scale_off,
+            Parts parts) {
   using S = GemmShape<ACT, BM>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -288,7 +293,24 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int G = MB * NBN;
   const int bid = (int)blockIdx.x;
   const int logical = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int mb = logical % MB, nb = logical / MB;
+  const int mb = logical % MB;
+  int nb = logical / MB;
+  const float *bias = nullptr;
+  int N = Npad;
+  if constexpr (PARTS) {
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxParts; ++i)
+      if (i < parts.n && nb >= parts.cum[i]) p = i;
+    nb -= parts.cum[p];
+    wq = parts.wq[p];
+    wsc = parts.wsc[p];
+    y = parts.y[p];
+    bias = parts.bias[p];
+    N = parts.N[p];
+    Npad = (N + kTile - 1) / kTile * kTile;
+    T = Npad / kTile;
+  }
   const int row0 = mb * BM, t0 = nb * S::WN;
 
   const int lane = threadIdx.x & 63;
@@ -453,6 +475,16 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   if constexpr (DOTS) return;
 
   if (t >= T) return;
+  // the part's bias on its real columns (pad columns stay the exact zero of
+  // zero values and scales)
+  float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (PARTS) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = t * kTile + g * 16 + li;
+      if (bias && c < N) bv[g] = bias[c];
+    }
+  }
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -460,19 +492,35 @@ gemm_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       const int r = row0 + wm * 64 + rt * 16 + lj * 4 + e;
       if (r < m) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          y[(size_t)r * Npad + (size_t)t * kTile + g * 16 + li] = acc[rt][g][e];
+        for (int g = 0; g < 4; ++g) {
+          float v = acc[rt][g][e];
+          if constexpr (PARTS) {
+            if (t * kTile + g * 16 + li < N) v += bv[g];
+          }
+          y[(size_t)r * Npad + (size_t)t * kTile + g * 16 + li] = v;
+        }
       }
     }
 }
 
-template <int ACT, int BM, bool DOTS>
-hipError_t launch_gemm_k(const GemmArgs &a, hipStream_t stream) {
+template <int ACT, int BM, bool DOTS, bool PARTS>
+hipError_t launch_gemm_kp(const GemmArgs &a, hipStream_t stream) {
   using S = GemmShape<ACT, BM>;
   const int MB = (a.m + BM - 1) / BM;
-  const int NBN = (a.T + S::WN - 1) / S::WN;
+  // parts: each part's tiles start a new column block
+  Parts parts = a.parts;
+  int NBN = (a.T + S::WN - 1) / S::WN;
+  if constexpr (PARTS) {
+    NBN = 0;
+    for (int i = 0; i < parts.n; ++i) {
+      const int tiles = a.parts.cum[i + 1] - a.parts.cum[i];
+      parts.cum[i] = NBN;
+      NBN += (tiles + S::WN - 1) / S::WN;
+    }
+    parts.cum[parts.n] = NBN;
+  }
   const size_t lds = 2 * (size_t)S::kStage;
-  auto kern = gemm_kernel<ACT, BM, DOTS>;
+  auto kern = gemm_kernel<ACT, BM, DOTS, PARTS>;
   static bool granted = false;
   if (!granted && lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -482,8 +530,18 @@ hipError_t launch_gemm_k(const GemmArgs &a, hipStream_t stream) {
   }
   (void)hipGetLastError();
   kern<<<dim3((unsigned)(MB * NBN)), dim3(kGemmThreads), lds, stream>>>(
-      a.x, a.wq, a.wsc, a.y, a.dots, a.m, a.K, a.NB, a.Npad, a.T, MB, NBN, a.act_scale_off);
+      a.x, a.wq, a.wsc, a.y, a.dots, a.m, a.K, a.NB, a.Npad, a.T, MB, NBN, a.act_scale_off,
+      parts);
   return hipGetLastError();
+}
+
+// One weight, or (a.parts.n > 0, no dots) the parts.
+template <int ACT, int BM, bool DOTS>
+hipError_t launch_gemm_k(const GemmArgs &a, hipStream_t stream) {
+  if constexpr (!DOTS) {
+    if (a.parts.n > 0) return launch_gemm_kp<ACT, BM, false, true>(a, stream);
+  }
+  return launch_gemm_kp<ACT, BM, DOTS, false>(a, stream);
 }
 
 }  // namespace

@@ -144,6 +144,10 @@ struct GemmArgs {
   int32_t *dots;           // non-null: write the int32 block dots instead of y
   int m, K, NB, Npad, T;
   unsigned act_scale_off;
+  // n > 0: several weights of one activation side by side (the GEMM in
+  // parts); cum[] counts 64-column tiles, each part's tiles starting a new
+  // column block; wq, wsc, y, Npad, T above are then unused
+  Parts parts;
 };
 // Output rows per workgroup the GEMM takes for m rows (64 or 128).
 int gemm_rows_per_block(int64_t m);

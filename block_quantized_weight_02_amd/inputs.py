@@ -89,6 +89,9 @@ PARTS_WORKLOADS: Dict[str, PartsWorkload] = {
     "qkv_q8act_m32_k4096": PartsWorkload("qkv_q8act_m32_k4096", 32, 4096, (4096, 1024, 1024),
                                          "q8_0", 1011, 1011,
                                          note="m=32 Q8_0 activations, q/k/v projections"),
+    "qkv_prefill_m512_k4096": PartsWorkload("qkv_prefill_m512_k4096", 512, 4096,
+                                            (4096, 1024, 1024), "bf16", 1012, 1012,
+                                            note="m=512 prefill chunk, q/k/v projections"),
 }
 
 

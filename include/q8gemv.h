@@ -437,6 +437,22 @@ int q8_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale,
 int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
                        int64_t m, int64_t K, int64_t N, hipStream_t stream);
 
+/*
+ * q8_gemm_parts: the product in parts above the GEMV's rows, as one launch:
+ * the pages' codegen_cuda/lane/plan.rs, enum Launch, variant GemmParts, whose
+ * parts run at more rows as one tensor-core GEMM over the parts' tiles side
+ * by side (merged_projections).  Part i computes
+ *     y_i[r, n] = (x . W_i)[r, n] + bias_i[n]        n < N_i (pad columns 0)
+ * with q8_gemm's arithmetic; the parts (a host array, 1 <= n_parts <=
+ * Q8_MAX_PARTS, padded widths summing to at most 2^24), x and act_fmt as in
+ * q8_gemv_parts, for 1 <= m <= Q8_MAX_GEMM_ROWS.  Each part's columns start a
+ * new column block of the GEMM, so a part's outputs are bit-identical to
+ * q8_gemm on that part alone (before the bias).  No workspace; allocates
+ * nothing.  Errors as q8_gemv_parts.
+ */
+int q8_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m,
+                  int64_t K, int act_fmt, hipStream_t stream);
+
 /* ---- errors and resources ------------------------------------------------ */
 
 /* Static name of a status code. */

@@ -202,6 +202,21 @@ def _part(N, w=A, s=A, y=A, bias=None):
     return q8.make_part(w, s, y, N, bias=bias)
 
 
+def test_gemm_parts_validation():
+    three = [_part(4096), _part(1024), _part(1024)]
+    expect(3, q8.q8_gemm_parts, A, None, 64, 4096, 0, S0)
+    expect(1, q8.q8_gemm_parts, A, [], 64, 4096, 0, S0)
+    expect(1, q8.q8_gemm_parts, A, [_part(64)] * 5, 64, 4096, 0, S0)
+    expect(1, q8.q8_gemm_parts, A, three, 0, 4096, 0, S0)
+    expect(1, q8.q8_gemm_parts, A, three, q8.Q8_MAX_GEMM_ROWS + 1, 4096, 0, S0)
+    expect(1, q8.q8_gemm_parts, A, three, 64, 48, 0, S0)
+    expect(2, q8.q8_gemm_parts, A, three, 64, 4096, 3, S0)
+    expect(3, q8.q8_gemm_parts, None, three, 64, 4096, 0, S0)
+    expect(4, q8.q8_gemm_parts, A + 2, three, 64, 4096, 0, S0)
+    expect(3, q8.q8_gemm_parts, A, [_part(64), _part(64, y=None)], 64, 4096, 0, S0)
+    assert "part 1" in q8.q8_last_error()
+
+
 def test_parts_validation():
     three = [_part(4096), _part(1024), _part(1024)]
     expect(3, q8.q8_gemv_parts, A, None, 1, 4096, 0, S0)

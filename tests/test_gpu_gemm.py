@@ -166,3 +166,76 @@ def test_gemm_most_rows():
     y = gemm(buf, Wq, Ws, m, K, N, Q8)
     ref, bnd = oracle.gemv_q8(xq, dx, q, s)
     assert_close(y[:, :N], ref, bnd, "gemm int8 m=8192")
+
+
+# ------------------------------------------------------------------------------
+# the GEMM in parts (plan.rs, GemmParts above the GEMV's rows)
+# ------------------------------------------------------------------------------
+
+def gemm_parts(xin, packed, Ns, biases, m, K, act):
+    ys = [torch.full((m, q8.q8_padded_cols(N)), float("nan"), dtype=torch.float32,
+                     device=g.DEV) for N in Ns]
+    bdev = [None if b is None else g.dev(b) for b in biases]
+    parts = [q8.make_part(W, Ws, y, N, bias=b)
+             for (W, Ws), y, N, b in zip(packed, ys, Ns, bdev)]
+    q8.q8_gemm_parts(xin, parts, m, K, act)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys]
+
+
+PART_SETS = [(200, 40, 64, 130), (4096, 1024, 1024), (96,), (320, 260)]
+
+
+@pytest.mark.parametrize("act", [BF16, Q8, q8.Q8_ACT_Q8_0_TWO_WORDS])
+@pytest.mark.parametrize("m", [1, 33, 100, 200])
+@pytest.mark.parametrize("Ns", PART_SETS)
+def test_gemm_parts(act, m, Ns):
+    K = 1056 if max(Ns) < 4096 else 512
+    seed = 5000 + m + sum(Ns) + act
+    x = inputs.gen_x(m, K, seed)
+    ws = [(inputs.gen_q(K, N, seed + 10 * i + 1), inputs.gen_scales(K, N, seed + 10 * i + 1))
+          for i, N in enumerate(Ns)]
+    biases = [inputs.gen_bias(N, seed=seed + i) if i % 2 == 0 else None
+              for i, N in enumerate(Ns)]
+    packed = [g.pack(q, s) for q, s in ws]
+    if act == BF16:
+        xin = xdev(x)
+    elif act == Q8:
+        xin = g.quantize(x)
+        rq, rd = oracle.quantize_act(x)
+        xq, dx = g.act_host(xin, m, K)
+        np.testing.assert_array_equal(xq, rq)
+        np.testing.assert_array_equal(dx.view(np.uint32), rd.view(np.uint32))
+    else:
+        from tests.test_gpu_two_words import _words_checked
+        xin, (rh, rl, rd2) = _words_checked(x)
+    ys = gemm_parts(xin, packed, Ns, biases, m, K, act)
+    for i, ((q, s), N, b, y) in enumerate(zip(ws, Ns, biases, ys)):
+        if act == BF16:
+            z, bnd = oracle.gemv_bf16(x, q, s)
+        elif act == Q8:
+            z, bnd = oracle.gemv_q8(rq, rd, q, s)
+        else:
+            z, bnd = oracle.gemv_q8_two_words(rh, rl, rd2, q, s)
+        z, bnd = oracle.epilogue(z, bnd, b)
+        assert_close(y[:, :N], z, bnd, f"gemm part {i} act={act} m={m} Ns={Ns}")
+        assert (y[:, N:].view(np.uint32) == 0).all(), f"part {i}: pad columns not zero"
+        if b is None:
+            y1 = gemm(xin, *packed[i], m, K, N, act)
+            np.testing.assert_array_equal(y.view(np.uint32), y1.view(np.uint32),
+                                          err_msg=f"part {i} differs from q8_gemm alone")
+
+
+def test_gemm_parts_qkv_prefill_full_size():
+    """The attention's query, key and value projections of a 512-row prefill
+    chunk, one launch, every column against the oracle."""
+    m, K, Ns = 512, 4096, (4096, 1024, 1024)
+    x = inputs.gen_x(m, K, 5100)
+    ws = [(inputs.gen_q(K, N, 5101 + i), inputs.gen_scales(K, N, 5101 + i)) for i, N in enumerate(Ns)]
+    biases = [inputs.gen_bias(N, seed=5110 + i) for i, N in enumerate(Ns)]
+    packed = [g.pack(q, s) for q, s in ws]
+    ys = gemm_parts(xdev(x), packed, Ns, biases, m, K, BF16)
+    for i, ((q, s), N, b, y) in enumerate(zip(ws, Ns, biases, ys)):
+        z, bnd = oracle.gemv_bf16(x, q, s)
+        z, bnd = oracle.epilogue(z, bnd, b)
+        assert_close(y[:, :N], z, bnd, f"qkv part {i}")

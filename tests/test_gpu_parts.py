@@ -154,7 +154,7 @@ def test_exact_products_parts():
             np.testing.assert_array_equal(y[:, :N].astype(np.float64), z)
 
 
-@pytest.mark.parametrize("name", sorted(inputs.PARTS_WORKLOADS))
+@pytest.mark.parametrize("name", sorted(n for n, w in inputs.PARTS_WORKLOADS.items() if w.m <= 32))
 def test_full_size_parts(name):
     w = inputs.PARTS_WORKLOADS[name]
     act = BF16 if w.act == "bf16" else Q8

@@ -467,3 +467,49 @@ def test_widest_n():
     assert_close(y[:, cols], ref, bnd, "N=2^24-5")
     assert (y[:, N:].view(np.uint32) == 0).all()
     assert y.shape[1] == 1 << 24
+
+
+def test_long_k_tile_kernels():
+    """K = 2^20 on the tile kernels' default plans (their LDS of the split's
+    activation scales raises the K split): 20 int8 rows (32x32x32 kernel) and
+    16 bf16 rows (16x16x32 kernel, both stage sizes)."""
+    K, N = 1 << 20, 70
+    for m, act in ((20, Q8), (16, BF16)):
+        x, q, s = inputs.random_case(m, K, N, seed=99 + m)
+        Wq, Ws = g.pack(q, s)
+        if act == BF16:
+            ref, bnd = oracle.gemv_bf16(x, q, s)
+            for plan in (None, g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 16, 2),
+                         g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 8, 1)):
+                y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16, plan)
+                assert_close(y[:, :N], ref, bnd, f"K=2^20 bf16 m={m} plan={plan}")
+                assert (y[:, N:].view(np.uint32) == 0).all()
+        else:
+            buf = g.quantize(x)
+            xq, dx = oracle.quantize_act(x)
+            ref, bnd = oracle.gemv_q8(xq, dx, q, s)
+            p = q8.q8_gemv_default_plan(m, K, N, Q8)
+            assert p.kernel == q8.Q8_KERNEL_MFMA32_TILE
+            y = g.gemv(buf, Wq, Ws, m, K, N, Q8)
+            assert_close(y[:, :N], ref, bnd, f"K=2^20 int8 m={m}")
+            assert (y[:, N:].view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("m,act", [(3, BF16), (17, Q8)])
+def test_widest_n_tile_kernels(m, act):
+    """N = 2^24 - 5 on the tile kernels (2^18 workgroups, the last tile
+    ragged), one block of K; sampled columns and the tile edges."""
+    K, N = 32, (1 << 24) - 5
+    x, q, s = inputs.random_case(m, K, N, seed=200 + m)
+    Wq, Ws = g.pack(q, s)
+    cols = _sample_cols(N, n=2048, seed=200 + m)
+    if act == BF16:
+        y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16)
+        ref, bnd = oracle.gemv_bf16(x, q, s, cols)
+    else:
+        buf = g.quantize(x)
+        xq, dx = oracle.quantize_act(x)
+        y = g.gemv(buf, Wq, Ws, m, K, N, Q8)
+        ref, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
+    assert_close(y[:, cols], ref, bnd, f"N=2^24-5 m={m}")
+    assert (y[:, N:].view(np.uint32) == 0).all()

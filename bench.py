@@ -85,7 +85,7 @@ def kernel_name(plan: dict, w) -> str:
     if plan["kernel"] == 1:
         return f"gemv_mfma_kernel<{r}, {act}, false, {wv}, false, false>"
     if plan["kernel"] == 5:
-        return f"gemv_mfma32w_kernel<{wv}, false>"
+        return f"gemv_mfma32w_kernel<{wv}, false, {ks}>"
     if plan["kernel"] == 6:
         return f"gemv_tile16_kernel<{act}, {wv}, false, {'true' if ks == 2 else 'false'}>"
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
@@ -95,6 +95,9 @@ def plan_grid(plan: dict, w) -> str:
     """rocprofv3's Grid_Size X x Y x Z (threads) of a tile-per-workgroup
     product launch (kernels 0, 5 and 6: one workgroup per tile and K split)."""
     tiles = (w.N + 63) // 64
+    if plan["kernel"] == 5:   # kslices column tiles a workgroup
+        ks = plan.get("kslices", 1)
+        tiles = (tiles + ks - 1) // ks
     return f"{tiles * 64 * plan['waves']}x{plan['split_k']}x1"
 
 

@@ -230,7 +230,13 @@ q8_plan tile32_plan(int64_t K, int64_t N) {
   q8_plan p;
   p.kernel = Q8_KERNEL_MFMA32_TILE;
   p.rows = 32;
-  p.kslices = 1;
+  // From 384 tiles each wave covers two column tiles (one activation load
+  // serves four MFMAs; half the workgroups still cover the CUs).  Measured on
+  // MI355X (loop us, two tiles against one, 8 waves): K=5120, N=32000: m=17
+  // 35.6 against 37.3, m=24 36.4 against 38.3-38.8, m=32 39.6 against 39.4;
+  // K=8192, N=32000, m=32: 57.7 against 61.3.  Below 384 tiles one (m=32,
+  // K=4096, N=14336: 24.2 against 17.6-17.7 with 16 waves).
+  p.kslices = T >= 384 ? 2 : 1;
   p.waves = T >= 384 ? 8 : 16;
   int64_t S = T >= 128 ? 1 : (T >= 8 ? 3 : 4);
   const int64_t smax = NB / 8 > 0 ? NB / 8 : 1;

@@ -457,7 +457,11 @@ constexpr size_t m32w_lds_bytes(int nblk) {
   return (size_t)nblk * 32 * 4 + (size_t)(W / 2) * 2048 * 4;
 }
 
-template <int W, bool DOTS>
+// TP: column tiles a wave covers (1 or 2).  With two, each activation
+// fragment serves four MFMAs instead of two (half the activation loads per
+// weight byte), for products wide enough that half as many workgroups still
+// keep every CU streaming.
+template <int W, bool DOTS, int TP>
 __global__ void __launch_bounds__(64 * W)
 gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                     const float *__restrict__ wsc, float *__restrict__ y,
@@ -470,14 +474,21 @@ gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, j = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = blockIdx.x, s = blockIdx.y;
+  const int t0 = blockIdx.x * TP, s = blockIdx.y;
   int b_lo, b_hi;
   split_range(s, split_q, split_r, b_lo, b_hi);
   const int nblk = b_hi - b_lo;
   const int nblk_max = split_q + (split_r > 0 ? 1 : 0);
 
-  const buf_t wr = make_buf(wq + (size_t)t * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
-  const buf_t sr = DOTS ? wr : make_buf(wsc + (size_t)t * NB * kTile, (unsigned)NB * kTile * 4);
+  // tile t0 + tp; a second tile past the last (T odd) streams the first
+  // again and is not stored
+  buf_t wr[TP], sr[TP];
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) {
+    const int tt = t0 + tp < T ? t0 + tp : t0;
+    wr[tp] = make_buf(wq + (size_t)tt * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
+    sr[tp] = DOTS ? wr[tp] : make_buf(wsc + (size_t)tt * NB * kTile, (unsigned)NB * kTile * 4);
+  }
   // the activation's block-interleaved view: block b's rows are m * 32
   // consecutive bytes; lanes of rows past m read zero
   const buf_t xr = make_buf(static_cast<const char *>(xv) + act_view_off,
@@ -487,18 +498,24 @@ gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const unsigned xoff = (unsigned)(row_live ? j : 0) * 32u + (unsigned)h * 16u;
 
   struct Stage {
-    uint4 lo, hi;   // column `lane`'s k = 0..15 and 16..31 of the block
-    uint4 a;        // activation row j, k = 16h .. 16h+15
-    float sc;       // column `lane`'s scale
+    uint4 lo[TP], hi[TP];   // column `lane`'s k = 0..15 and 16..31 of the block
+    uint4 a;                // activation row j, k = 16h .. 16h+15
+    float sc[TP];           // column `lane`'s scale
   };
   auto load = [&](Stage &st, int b) {
     const unsigned wb = (unsigned)b * kChunkBytes;
-    st.lo = buf_ld16(wr, lw, wb);
-    st.hi = buf_ld16(wr, lw + kHalfBytes, wb);
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) {
+      st.lo[tp] = buf_ld16(wr[tp], lw, wb);
+      st.hi[tp] = buf_ld16(wr[tp], lw + kHalfBytes, wb);
+    }
     const u32x4_t v =
         __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (unsigned)b * (unsigned)m * 32u, 0);
     st.a = row_live ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (!DOTS) st.sc = buf_ld4f(sr, ls, (unsigned)b * (kTile * 4));
+    if constexpr (!DOTS) {
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) st.sc[tp] = buf_ld4f(sr[tp], ls, (unsigned)b * (kTile * 4));
+    }
   };
 
   Stage A, B;
@@ -510,51 +527,59 @@ gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     __syncthreads();
   }
 
-  f32x4_t acc0[4], acc1[4];
+  f32x4_t acc0[TP][4], acc1[TP][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    acc0[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    acc1[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  auto compute = [&](const Stage &st, int bb) {
-    // the B operands of the two 32-column groups
-    uint32_t g0[4], g1[4];
-    const uint32_t lo[4] = {st.lo.x, st.lo.y, st.lo.z, st.lo.w};
-    const uint32_t hi[4] = {st.hi.x, st.hi.y, st.hi.z, st.hi.w};
+  for (int tp = 0; tp < TP; ++tp)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
-      g0[d] = r[0];
-      g1[d] = r[1];
+    for (int q = 0; q < 4; ++q) {
+      acc0[tp][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1[tp][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  auto compute = [&](const Stage &st, int bb) {
     const i32x4v_t a = __builtin_bit_cast(i32x4v_t, st.a);
-    const i32x16_t d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-        a, i32x4v_t{(int)g0[0], (int)g0[1], (int)g0[2], (int)g0[3]}, i32x16_t{}, 0, 0, 0);
-    const i32x16_t d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-        a, i32x4v_t{(int)g1[0], (int)g1[1], (int)g1[2], (int)g1[3]}, i32x16_t{}, 0, 0, 0);
-    if constexpr (DOTS) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-        if (r < m) {
-          int32_t *dr = dots + ((size_t)r * NB + bb) * Npad + (size_t)t * kTile + j;
-          dr[0] = d0[v];
-          dr[32] = d1[v];
-        }
+    for (int tp = 0; tp < TP; ++tp) {
+      // the B operands of the tile's two 32-column groups
+      uint32_t g0[4], g1[4];
+      const uint32_t lo[4] = {st.lo[tp].x, st.lo[tp].y, st.lo[tp].z, st.lo[tp].w};
+      const uint32_t hi[4] = {st.hi[tp].x, st.hi[tp].y, st.hi[tp].z, st.hi[tp].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+        g0[d] = r[0];
+        g1[d] = r[1];
       }
-    } else {
-      const unsigned scu = __float_as_uint(st.sc);
-      const auto sp = __builtin_amdgcn_permlane32_swap(scu, scu, false, false);
-      const float s0 = __uint_as_float(sp[0]), s1 = __uint_as_float(sp[1]);
-      const int lb = bb - b_lo;
+      const i32x16_t d0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+          a, i32x4v_t{(int)g0[0], (int)g0[1], (int)g0[2], (int)g0[3]}, i32x16_t{}, 0, 0, 0);
+      const i32x16_t d1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+          a, i32x4v_t{(int)g1[0], (int)g1[1], (int)g1[2], (int)g1[3]}, i32x16_t{}, 0, 0, 0);
+      if constexpr (DOTS) {
+        if (t0 + tp < T) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 dx4 = *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + 8 * q + 4 * h);
-        const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+          for (int v = 0; v < 16; ++v) {
+            const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+            if (r < m) {
+              int32_t *dr = dots + ((size_t)r * NB + bb) * Npad + (size_t)(t0 + tp) * kTile + j;
+              dr[0] = d0[v];
+              dr[32] = d1[v];
+            }
+          }
+        }
+      } else {
+        const unsigned scu = __float_as_uint(st.sc[tp]);
+        const auto sp = __builtin_amdgcn_permlane32_swap(scu, scu, false, false);
+        const float s0 = __uint_as_float(sp[0]), s1 = __uint_as_float(sp[1]);
+        const int lb = bb - b_lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc0[q][e] = fmaf(dxv[e] * s0, (float)d0[4 * q + e], acc0[q][e]);
-          acc1[q][e] = fmaf(dxv[e] * s1, (float)d1[4 * q + e], acc1[q][e]);
+        for (int q = 0; q < 4; ++q) {
+          const float4 dx4 =
+              *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + 8 * q + 4 * h);
+          const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc0[tp][q][e] = fmaf(dxv[e] * s0, (float)d0[4 * q + e], acc0[tp][q][e]);
+            acc1[tp][q][e] = fmaf(dxv[e] * s1, (float)d1[4 * q + e], acc1[tp][q][e]);
+          }
         }
       }
     }
@@ -576,70 +601,86 @@ gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   }
   if constexpr (DOTS) return;
 
-  // carries meet by halves: wave w + half adds into wave w
 #pragma unroll
-  for (int half = W / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-      float *rw = red + (size_t)(wave - half) * 2048;
+  for (int tp = 0; tp < TP; ++tp) {
+    // carries meet by halves: wave w + half adds into wave w
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<f32x4_t *>(rw + q * 256 + lane * 4) = acc0[q];
-        *reinterpret_cast<f32x4_t *>(rw + (4 + q) * 256 + lane * 4) = acc1[q];
+    for (int half = W / 2; half >= 1; half /= 2) {
+      if (wave >= half && wave < 2 * half) {
+        float *rw = red + (size_t)(wave - half) * 2048;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<f32x4_t *>(rw + q * 256 + lane * 4) = acc0[tp][q];
+          *reinterpret_cast<f32x4_t *>(rw + (4 + q) * 256 + lane * 4) = acc1[tp][q];
+        }
       }
+      __syncthreads();
+      if (wave < half) {
+        const float *rw = red + (size_t)wave * 2048;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc0[tp][q] += *reinterpret_cast<const f32x4_t *>(rw + q * 256 + lane * 4);
+          acc1[tp][q] += *reinterpret_cast<const f32x4_t *>(rw + (4 + q) * 256 + lane * 4);
+        }
+      }
+      __syncthreads();
+    }
+    // wave 0 holds the tile's sums: into LDS row-major, and every wave takes
+    // a share of the epilogue, the stores and the split-K combine
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * q + 4 * h + e;
+          red[r * 64 + j] = acc0[tp][q][e];
+          red[r * 64 + 32 + j] = acc1[tp][q][e];
+        }
     }
     __syncthreads();
-    if (wave < half) {
-      const float *rw = red + (size_t)wave * 2048;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc0[q] += *reinterpret_cast<const f32x4_t *>(rw + q * 256 + lane * 4);
-        acc1[q] += *reinterpret_cast<const f32x4_t *>(rw + (4 + q) * 256 + lane * 4);
-      }
-    }
-    __syncthreads();
+    const int t = t0 + tp;
+    if (t < T)
+      finish_tile<MR, 1, false, 64 * W>(
+          red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t},
+          partial, counters, m, s, S, 0, ep);
+    if (TP > 1) __syncthreads();   // red is read by the finish before the next tile's carries
   }
-  // wave 0 holds the tile's sums: into LDS row-major, and every wave takes
-  // a share of the epilogue, the stores and the split-K combine
-  if (wave == 0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 8 * q + 4 * h + e;
-        red[r * 64 + j] = acc0[q][e];
-        red[r * 64 + 32 + j] = acc1[q][e];
-      }
-  }
-  __syncthreads();
-  finish_tile<MR, 1, false, 64 * W>(
-      red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t}, partial,
-      counters, m, s, S, 0, ep);
 }
 
-template <int W, bool DOTS>
+template <int W, bool DOTS, int TP>
 hipError_t launch_m32w(const GemvArgs &a, hipStream_t stream) {
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
   const size_t lds = m32w_lds_bytes<W>(nblk_max);
-  auto kern = gemv_mfma32w_kernel<W, DOTS>;
+  auto kern = gemv_mfma32w_kernel<W, DOTS, TP>;
   static size_t granted = 64 * 1024;
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
   (void)hipGetLastError();
-  kern<<<dim3((unsigned)a.T, (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
+  kern<<<dim3((unsigned)((a.T + TP - 1) / TP), (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
       a.split_k, a.NB / a.split_k, a.NB % a.split_k, a.act_scale_off, a.act_view_off, a.ep);
   return hipGetLastError();
 }
 
+template <int W>
+hipError_t launch_m32w_tp(int tp, bool dots, const GemvArgs &a, hipStream_t stream) {
+  if (tp == 2)
+    return dots ? launch_m32w<W, true, 2>(a, stream) : launch_m32w<W, false, 2>(a, stream);
+  return dots ? launch_m32w<W, true, 1>(a, stream) : launch_m32w<W, false, 1>(a, stream);
+}
+
 }  // namespace
 
 // Kernels 3 and 4, (waves, kslices) built: waves = kslices x tiles side by
-// side.  Kernel 5: 4, 8 or 16 waves (kslices ignored).
+// side.  Kernel 5: 4, 8 or 16 waves; kslices = column tiles a wave covers
+// (1, or 2 with 4 or 8 waves).
 bool mfma32_instantiated(int kernel, int rows, int act, bool write_dots, int waves,
                          int kslices) {
   (void)write_dots;
   if (rows != 32 || act != kActQ8) return false;
-  if (kernel == 5) return waves == 4 || waves == 8 || waves == 16;
+  if (kernel == 5)
+    return (kslices == 1 && (waves == 4 || waves == 8 || waves == 16)) ||
+           (kslices == 2 && (waves == 4 || waves == 8));
   return (waves == 4 && (kslices == 1 || kslices == 2 || kslices == 4)) ||
          (waves == 8 && (kslices == 1 || kslices == 2 || kslices == 4 || kslices == 8));
 }
@@ -660,10 +701,12 @@ hipError_t launch_gemv_mfma32(int kernel, int waves, int kslices, bool write_dot
   if (a.ep.nw != 1 || a.ep.parts.n > 0) return hipErrorInvalidValue;
   if (kernel == 5) {
     switch (waves) {
-      case 4: return write_dots ? launch_m32w<4, true>(a, stream) : launch_m32w<4, false>(a, stream);
-      case 8: return write_dots ? launch_m32w<8, true>(a, stream) : launch_m32w<8, false>(a, stream);
+      case 4: return launch_m32w_tp<4>(kslices, write_dots, a, stream);
+      case 8: return launch_m32w_tp<8>(kslices, write_dots, a, stream);
       case 16:
-        return write_dots ? launch_m32w<16, true>(a, stream) : launch_m32w<16, false>(a, stream);
+        if (kslices != 1) return hipErrorInvalidValue;
+        return write_dots ? launch_m32w<16, true, 1>(a, stream)
+                          : launch_m32w<16, false, 1>(a, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -225,9 +225,10 @@ typedef enum {
                               activation scales are staged in LDS, so a workgroup's
                               K range is not bounded by the LDS                    */
   Q8_KERNEL_MFMA32_TILE = 5, /* the 32x32x32 block dots with the VALU kernel's weight
-                              stream: one workgroup per (tile, K split), waves (4, 8
-                              or 16) split K, the activation fragments loaded with
-                              the weights, kslices ignored                          */
+                              stream: one workgroup per (kslices tiles, K split),
+                              waves (4, 8 or 16; with kslices 2: 4 or 8) split K,
+                              the activation fragments loaded with the weights and
+                              shared by the kslices (1 or 2) tiles of a wave       */
   Q8_KERNEL_MFMA16_TILE = 6 /* 16x16x32 block dots of up to 16 rows (bf16 or one-word
                               Q8_0) with the VALU kernel's weight stream: one
                               workgroup per (tile, K split), waves (4, 8 or 16)
@@ -249,8 +250,8 @@ typedef struct q8_plan {
                       MFMA32(_DIRECT): waves that split one tile's K range (waves 4:
                       1, 2, 4; waves 8: 1, 2, 4, 8; waves = kslices * tiles
                       side by side); MFMA16_TILE: blocks per stage (above);
-                      VALU, MFMA, MFMA32_TILE: ignored (all their waves split
-                      K)                                                       */
+                      MFMA32_TILE: column tiles a wave covers (above); VALU,
+                      MFMA: ignored (all their waves split K)                   */
 } q8_plan;
 
 /* The plan q8_gemv would launch for this shape on the current device. */

@@ -27,8 +27,12 @@ def test_kernel_name_and_grid_of_plans():
     assert bench.plan_grid(p, w) == f"{224 * 64 * 16}x1x1"
     w5 = inputs.WORKLOADS["q8act_m32_k5120_n40"]
     p5 = {"kernel": 5, "rows": 32, "split_k": 4, "waves": 16, "kslices": 1}
-    assert bench.kernel_name(p5, w5) == "gemv_mfma32w_kernel<16, false>"
+    assert bench.kernel_name(p5, w5) == "gemv_mfma32w_kernel<16, false, 1>"
     assert bench.plan_grid(p5, w5) == "1024x4x1"
+    w5b = inputs.WORKLOADS["q8act_m32_k5120_n32000"]
+    p5b = {"kernel": 5, "rows": 32, "split_k": 1, "waves": 8, "kslices": 2}
+    assert bench.kernel_name(p5b, w5b) == "gemv_mfma32w_kernel<8, false, 2>"
+    assert bench.plan_grid(p5b, w5b) == f"{250 * 512}x1x1"
 
 
 def test_summarize_pmc(tmp_path, capsys):

@@ -119,6 +119,7 @@ EXACT_PLANS = [None,
                (q8.Q8_KERNEL_MFMA32, 32, 1, 8, 2), (q8.Q8_KERNEL_MFMA32, 32, 3, 4, 1),
                (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 1, 8, 4), (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 2, 8, 8),
                (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1), (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 16, 1),
+               (q8.Q8_KERNEL_MFMA32_TILE, 32, 2, 8, 2),
                (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1), (q8.Q8_KERNEL_MFMA16_TILE, 16, 4, 4, 1),
                (q8.Q8_KERNEL_MFMA16_TILE, 16, 2, 16, 2)]
 
@@ -172,6 +173,8 @@ RANDOM_PLANS = [
     (19, Q8, (q8.Q8_KERNEL_MFMA32_DIRECT, 32, 3, 4, 2)),
     (32, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1)),
     (25, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 4, 16, 1)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 2)),
+    (19, Q8, (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 4, 2)),
     (16, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1)),
     (5, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 16, 3, 16, 1)),
     (11, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 7, 4, 1)),

@@ -213,10 +213,10 @@ def _plans(m, NB):
                 for split in splits:
                     if split <= NB:
                         out.append((kernel, 32, split, waves, ks))
-        for waves in (4, 8, 16):
+        for (waves, tp) in ((4, 1), (8, 1), (16, 1), (4, 2), (8, 2)):
             for split in splits:
                 if split <= NB:
-                    out.append((q8.Q8_KERNEL_MFMA32_TILE, 32, split, waves, 1))
+                    out.append((q8.Q8_KERNEL_MFMA32_TILE, 32, split, waves, tp))
     if m <= 16:
         for waves in (4, 8, 16):
             for split in splits:
@@ -513,3 +513,25 @@ def test_widest_n_tile_kernels(m, act):
         ref, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
     assert_close(y[:, cols], ref, bnd, f"N=2^24-5 m={m}")
     assert (y[:, N:].view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("m,N,pl", [(32, 130, (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 2)),
+                                    (17, 40, (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 4, 2)),
+                                    (24, 330, (q8.Q8_KERNEL_MFMA32_TILE, 32, 2, 8, 2))])
+def test_two_tile_waves_odd_tiles(m, N, pl):
+    """The 32x32x32 tile kernel with two column tiles a wave on an odd tile
+    count (the last workgroup's second tile is past the weight): every
+    column within the bound, pad columns zero, block dots bit for bit."""
+    K = 1056
+    x, q, s = inputs.random_case(m, K, N, seed=300 + m + N)
+    Wq, Ws = g.pack(q, s)
+    buf = g.quantize(x)
+    xq, dx = oracle.quantize_act(x)
+    plan = g.plan(*pl)
+    y = g.gemv(buf, Wq, Ws, m, K, N, Q8, plan)
+    ref, bnd = oracle.gemv_q8(xq, dx, q, s)
+    assert_close(y[:, :N], ref, bnd, f"two tiles m={m} N={N}")
+    assert (y[:, N:].view(np.uint32) == 0).all()
+    d = g.block_dots(buf, Wq, m, K, N, plan)
+    np.testing.assert_array_equal(d[:, :, :N], oracle.block_dots(xq, q))
+    assert (d[:, :, N:] == 0).all()

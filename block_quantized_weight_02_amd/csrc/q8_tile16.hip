@@ -23,9 +23,11 @@
 // from the rows, one block a stage, or two blocks a stage (a wave takes pairs
 // 2w, 2w+1, then 2w+2W, ...) with the rows' 128 bytes of the pair read as
 // whole cache lines and handed to the MFMA layout through a per-wave LDS
-// scratch (one block of 16 rows touches 16 half-used lines a load); rows
-// past m are zero.  The waves' carries meet by halves in LDS and every
-// wave takes a share of the finish (epilogue, stores, split-K combine).
+// scratch (one block of 16 rows touches 16 half-used lines a load); the
+// rows past m are loaded too (their rows of D are never read).  Two stages
+// are in flight, taking turns in two register sets.  The waves' carries meet
+// by halves in LDS and every wave takes a share of the finish (epilogue,
+// stores, split-K combine).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

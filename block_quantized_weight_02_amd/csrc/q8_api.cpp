@@ -293,6 +293,34 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   return p;
 }
 
+// The many-row product at up to 64 rows of bf16 or one-word Q8_0: the GEMM
+// gives each workgroup 64 rows by four column tiles, so at these rows it runs
+// one workgroup per four tiles, too few to cover the CUs, and its workgroups
+// still compute 64 rows.  Instead each column tile streams once through the
+// tile-per-workgroup kernel (MFMA16_TILE, 16, 32 or 64 rows a wave), without
+// a K split, so that it needs no workspace.  The choice depends on m, K and
+// the format only, so a part of q8_gemm_parts takes the same kernel, with the
+// same per-tile arithmetic, as q8_gemm on it alone.
+struct GemmTileRoute {
+  bool on;
+  int rows, waves;
+};
+GemmTileRoute gemm_tile_route(int64_t m, int64_t K, int act_fmt) {
+  GemmTileRoute r{false, 0, 0};
+  if (m > 64 || (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)) return r;
+  if (act_fmt == Q8_ACT_Q8_0 && act_view_offset(m, K) > 0xffffffffull) return r;
+  r.rows = m <= 16 ? 16 : (m <= 32 ? 32 : 64);
+  const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
+  for (int w : {8, 4}) {
+    if (q8::tile16_lds_bytes(r.rows, act_fmt, w, (int)(K / Q8_BLOCK), 1) <= budget) {
+      r.waves = w;
+      r.on = true;
+      return r;
+    }
+  }
+  return r;
+}
+
 // tiles: the tile-per-workgroup kernels may be chosen (they run one weight:
 // the gated pair and the parts pass false).
 q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tiles = true) {
@@ -1078,6 +1106,34 @@ int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
+  const GemmTileRoute route = gemm_tile_route(m, K, act_fmt);
+  if (route.on) {
+    q8::GemvArgs g{};
+    g.x = x;
+    g.wq = W_q8;
+    g.wsc = W_q8_scale;
+    g.y = y;
+    g.dots = dots;
+    g.m = (int)m;
+    g.K = (int)K;
+    g.NB = (int)(K / Q8_BLOCK);
+    g.Npad = (int)Npad;
+    g.T = (int)(Npad / Q8_TILE_COLS);
+    g.split_k = 1;
+    g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+    g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
+    g.ep.N = (int)N;
+    g.ep.write_y = 1;
+    g.ep.nw = 1;
+    (void)hipGetLastError();
+    hipError_t e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, dots != nullptr,
+                                          g, stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_fail(e, "gemm launch");
+    }
+    return ok();
+  }
   q8::GemmArgs a{};
   a.x = x;
   a.wq = W_q8;
@@ -1120,13 +1176,7 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
   if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
-  q8::GemmArgs a{};
-  a.x = x;
-  a.m = (int)m;
-  a.K = (int)K;
-  a.NB = (int)(K / Q8_BLOCK);
-  a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-  q8::Parts &pp = a.parts;
+  q8::Parts pp{};
   pp.n = n_parts;
   pp.cum[0] = 0;
   for (int i = 0; i < q8::kMaxParts; ++i) {
@@ -1139,8 +1189,34 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
     pp.cum[i + 1] =
         pp.cum[i] + (on ? (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS) : 0);
   }
+  const GemmTileRoute route = gemm_tile_route(m, K, act_fmt);
+  hipError_t e;
   (void)hipGetLastError();
-  hipError_t e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
+  if (route.on) {
+    q8::GemvArgs g{};
+    g.x = x;
+    g.m = (int)m;
+    g.K = (int)K;
+    g.NB = (int)(K / Q8_BLOCK);
+    g.T = pp.cum[n_parts];
+    g.Npad = g.T * Q8_TILE_COLS;
+    g.split_k = 1;
+    g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+    g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
+    g.ep.write_y = 1;
+    g.ep.nw = 1;
+    g.ep.parts = pp;
+    e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, false, g, stream);
+  } else {
+    q8::GemmArgs a{};
+    a.x = x;
+    a.m = (int)m;
+    a.K = (int)K;
+    a.NB = (int)(K / Q8_BLOCK);
+    a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+    a.parts = pp;
+    e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
+  }
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return hip_fail(e, "gemm launch");

@@ -128,12 +128,13 @@ size_t mfma32_lds_bytes(int kernel, int waves, int kslices, int NB, int split_k)
 hipError_t launch_gemv_mfma32(int kernel, int waves, int kslices, bool write_dots,
                               const GemvArgs &a, hipStream_t stream);
 
-// The tile-per-workgroup 16x16x32 product (q8_tile16.hip, kernel 6): up to 16
-// rows of bf16 or one-word Q8_0 activations, 4, 8 or 16 waves; one weight.
+// The tile-per-workgroup 16x16x32 product (q8_tile16.hip, kernel 6): rows 16
+// (4, 8 or 16 waves), 32 (4, 8 or 16) or 64 (4 or 8) of bf16 or one-word
+// Q8_0 activations; one weight, or the parts (ep.parts, no dots).
 bool tile16_instantiated(int rows, int act, bool write_dots, int waves, int kslices);
-size_t tile16_lds_bytes(int act, int waves, int NB, int split_k);
-hipError_t launch_gemv_tile16(int act, int waves, int kslices, bool write_dots, const GemvArgs &a,
-                              hipStream_t stream);
+size_t tile16_lds_bytes(int rows, int act, int waves, int NB, int split_k);
+hipError_t launch_gemv_tile16(int rows, int act, int waves, int kslices, bool write_dots,
+                              const GemvArgs &a, hipStream_t stream);
 
 // The many-row product (q8_gemm.hip): no split, no workspace.
 struct GemmArgs {

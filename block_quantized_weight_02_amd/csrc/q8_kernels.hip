@@ -1341,7 +1341,7 @@ size_t gemv_lds_bytes(int kernel, int rows, int act, int waves, int kslices, int
                       int split_k) {
   if (kernel == 1) return mfma_lds_bytes_of(rows, act, waves, NB, split_k);
   if (kernel >= 3 && kernel <= 5) return mfma32_lds_bytes(kernel, waves, kslices, NB, split_k);
-  if (kernel == 6) return tile16_lds_bytes(act, waves, NB, split_k);
+  if (kernel == 6) return tile16_lds_bytes(rows, act, waves, NB, split_k);
   if (kernel == 2) return cols_lds_bytes_of(rows, act, kslices, NB, split_k);
   return 0;
 }
@@ -1362,7 +1362,7 @@ hipError_t launch_gemv(int kernel, int rows, int act, bool write_dots, int waves
   }
   if (kernel == 6) {
     if (!tile16_instantiated(rows, act, write_dots, waves, kslices)) return hipErrorInvalidValue;
-    return launch_gemv_tile16(act, waves, kslices, write_dots, a, stream);
+    return launch_gemv_tile16(rows, act, waves, kslices, write_dots, a, stream);
   }
   Launcher f = pick(kernel, rows, act, write_dots, waves, kslices);
   if (!f) return hipErrorInvalidValue;

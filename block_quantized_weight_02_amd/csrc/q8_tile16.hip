@@ -44,9 +44,10 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2v_t;
 
 // LDS: int8, the split's activation scales; bf16, a 2 KiB scratch per wave
 // (the activation transpose); then the carries' halves.
-template <int ACT, int W>
+template <int ACT, int W, int RG>
 constexpr size_t t16_lds_bytes(int nblk) {
-  return (ACT == kActQ8 ? (size_t)nblk * 16 * 4 : (size_t)W * 2048) + (size_t)(W / 2) * 1024 * 4;
+  return (ACT == kActQ8 ? (size_t)nblk * 16 * RG * 4 : (size_t)W * 2048) +
+         (size_t)(W / 2) * 1024 * 4 * RG;
 }
 
 
@@ -57,7 +58,10 @@ __device__ __forceinline__ float4 buf_ld16f(buf_t r, unsigned voff, unsigned sof
                      __uint_as_float(v.w));
 }
 
-template <int ACT, int W, bool DOTS, bool PAIRS>
+// RG: row groups of 16 a wave covers (MR = 16 RG rows; RG > 1 serves the
+// many-row product's smaller chunks, up to 64 rows): each block's weight is
+// turned into B operands once and meets RG activation fragments.
+template <int ACT, int W, bool DOTS, bool PAIRS, int RG>
 __global__ void __launch_bounds__(64 * W)
 gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                    const float *__restrict__ wsc, float *__restrict__ y,
@@ -65,7 +69,8 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                    int32_t *__restrict__ dots, int m, int K, int NB, int Npad, int T, int S,
                    int split_q, int split_r, unsigned act_scale_off, unsigned act_view_off,
                    Epi ep) {
-  constexpr int MR = 16;
+  constexpr int MR = 16 * RG;
+  static_assert(!PAIRS || RG == 1, "two-block stages take 16 rows");
   constexpr bool kQ8 = ACT == kActQ8;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
@@ -77,14 +82,26 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int nblk = b_hi - b_lo;
   const int nblk_max = split_q + (split_r > 0 ? 1 : 0);
 
-  const buf_t wr = make_buf(wq + (size_t)t * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
-  const buf_t sr = DOTS ? wr : make_buf(wsc + (size_t)t * NB * kTile, (unsigned)NB * kTile * 4);
+  // a parts launch: the workgroup's tile t is tile tt of one part's weight
+  const int8_t *wt = wq;
+  const float *stt = wsc;
+  int tt = t;
+  if (!DOTS && ep.parts.n > 0) {
+    const int p = part_of(ep.parts, t);
+    tt = t - ep.parts.cum[p];
+    wt = ep.parts.wq[p];
+    stt = ep.parts.wsc[p];
+  }
+  const buf_t wr = make_buf(wt + (size_t)tt * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
+  const buf_t sr = DOTS ? wr : make_buf(stt + (size_t)tt * NB * kTile, (unsigned)NB * kTile * 4);
   const unsigned lw = (unsigned)lane * 16u, ls = (unsigned)i * 16u;
   // the activation: bf16 rows, or the int8 view (block b's m rows at b*m*32).
   // Lanes of rows past m load row 0 (or, for the pair's whole lines, read
   // zero past the buffer's extent): those rows of D are never read, and an
   // unconditional load keeps the stage's loads out of branches.
-  const int ri = i < m ? i : 0;
+  int ri[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) ri[rg] = 16 * rg + i < m ? 16 * rg + i : 0;
   const buf_t xr = kQ8 ? make_buf(static_cast<const char *>(xv) + act_view_off,
                                   (unsigned)m * (unsigned)K)
                        : make_buf(xv, (unsigned)m * (unsigned)K * 2u);
@@ -95,15 +112,18 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   // and handed to the MFMA layout through the wave's LDS scratch.
   constexpr int U = PAIRS ? 2 : 1;
   const int lrow = lane >> 3;
-  const unsigned xoff = kQ8      ? (unsigned)ri * 32u + (unsigned)q * 8u
-                        : PAIRS ? (unsigned)lrow * (unsigned)K * 2u + (unsigned)(lane & 7) * 16u
-                                : (unsigned)ri * (unsigned)K * 2u + (unsigned)q * 16u;
+  unsigned xoff[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+    xoff[rg] = kQ8      ? (unsigned)ri[rg] * 32u + (unsigned)q * 8u
+               : PAIRS ? (unsigned)lrow * (unsigned)K * 2u + (unsigned)(lane & 7) * 16u
+                       : (unsigned)ri[rg] * (unsigned)K * 2u + (unsigned)q * 16u;
   const unsigned xoff8 = (unsigned)8 * (unsigned)K * 2u;   // rows 8 .. 15
 
   struct Stage {
     uint4 lo[U], hi[U];   // column `lane`'s k = 0..15 and 16..31 of each block
     float4 sc[U];         // scales of columns i, i+16, i+32, i+48
-    uint4 a[2];           // int8: a[0].xy; bf16: the two loads of the pair
+    uint4 a[RG > 1 ? RG : 2];   // row group rg's fragment (int8: .xy); pairs: the two loads
   };
   auto load = [&](Stage &st, int bv) {
     const int b = __builtin_amdgcn_readfirstlane(bv);
@@ -116,16 +136,23 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       if constexpr (!DOTS) st.sc[u] = buf_ld16f(sr, ls, (unsigned)bu * (kTile * 4));
     }
     if constexpr (kQ8) {
-      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, xoff, (unsigned)b * (unsigned)m * 32u, 0);
-      st.a[0] = make_uint4(v.x, v.y, 0u, 0u);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, xoff[rg],
+                                                               (unsigned)b * (unsigned)m * 32u, 0);
+        st.a[rg] = make_uint4(v.x, v.y, 0u, 0u);
+      }
     } else if constexpr (!PAIRS) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (unsigned)b * 64u, 0);
-      st.a[0] = make_uint4(v.x, v.y, v.z, v.w);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[rg], (unsigned)b * 64u, 0);
+        st.a[rg] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     } else {
 #pragma unroll
       for (int v2 = 0; v2 < 2; ++v2) {
         const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-            xr, xoff + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
+            xr, xoff[0] + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
         st.a[v2] = make_uint4(v.x, v.y, v.z, v.w);
       }
     }
@@ -147,13 +174,15 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     __syncthreads();
   }
 
-  f32x4_t acc[4];
+  f32x4_t acc[RG][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) acc[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[rg][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // one block of a stage: u its place in the stage, bb the block, a the
-  // activation fragment
-  auto compute1 = [&](const Stage &st, int u, int bb, uint4 afrag) {
+  // one block of a stage: u its place in the stage, bb the block, afrag the
+  // row groups' activation fragments
+  auto compute1 = [&](const Stage &st, int u, int bb, const uint4 (&afrag)[RG]) {
     // pieces: quarter Q holds column 16Q + i, piece p = k 8p .. 8p+7; after
     // the transpose R[g] holds, in quarter q, column 16g + i's piece q
     uint32_t R[4][2] = {{st.lo[u].x, st.lo[u].y}, {st.lo[u].z, st.lo[u].w},
@@ -172,41 +201,53 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
     }
     const float scs[4] = {st.sc[u].x, st.sc[u].y, st.sc[u].z, st.sc[u].w};
     if constexpr (kQ8) {
-      const long a = __builtin_bit_cast(long, make_uint2(afrag.x, afrag.y));
-      float4 dx4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if constexpr (!DOTS) dx4 = *reinterpret_cast<const float4 *>(dxs + (bb - b_lo) * MR + 4 * q);
-      const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const long bw = __builtin_bit_cast(long, make_uint2(R[g][0], R[g][1]));
-        const i32x4_t d = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
-        if constexpr (DOTS) {
+      for (int rg = 0; rg < RG; ++rg) {
+        const long a = __builtin_bit_cast(long, make_uint2(afrag[rg].x, afrag[rg].y));
+        float4 dx4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if constexpr (!DOTS)
+          dx4 = *reinterpret_cast<const float4 *>(dxs + (bb - b_lo) * MR + 16 * rg + 4 * q);
+        const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q + e;
-            if (r < m) dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + 16 * g + i] = d[e];
+        for (int g = 0; g < 4; ++g) {
+          const long bw = __builtin_bit_cast(long, make_uint2(R[g][0], R[g][1]));
+          const i32x4_t d =
+              __builtin_amdgcn_mfma_i32_16x16x32_i8(a, bw, i32x4_t{0, 0, 0, 0}, 0, 0, 0);
+          if constexpr (DOTS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * rg + 4 * q + e;
+              if (r < m) dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + 16 * g + i] = d[e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[rg][g][e] = fmaf(dxv[e] * scs[g], (float)d[e], acc[rg][g][e]);
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[g][e] = fmaf(dxv[e] * scs[g], (float)d[e], acc[g][e]);
         }
       }
     } else {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, afrag);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const bf16x8_t bw = i8x8_to_bf16(make_uint2(R[g][0], R[g][1]));
-        const f32x4_t d =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[g][e] = fmaf(scs[g], d[e], acc[g][e]);
+        for (int rg = 0; rg < RG; ++rg) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, afrag[rg]);
+          const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, bw, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rg][g][e] = fmaf(scs[g], d[e], acc[rg][g][e]);
+        }
       }
     }
   };
 
   auto compute = [&](const Stage &st, int b0) {
     if constexpr (!PAIRS) {
-      compute1(st, 0, b0, st.a[0]);
+      uint4 af[RG];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) af[rg] = st.a[rg];
+      compute1(st, 0, b0, af);
     } else {
       // the pair's rows through LDS: row r's 128 bytes at r * 128, then the
       // MFMA fragment of block u (row i, k = 8q ..) at i * 128 + 64u + 16q
@@ -217,7 +258,8 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (b0 + u >= b_hi) break;
-        const uint4 af = *reinterpret_cast<const uint4 *>(scr + i * 128 + 64 * u + 16 * q);
+        uint4 af[RG];
+        af[0] = *reinterpret_cast<const uint4 *>(scr + i * 128 + 64 * u + 16 * q);
         compute1(st, u, b0 + u, af);
       }
     }
@@ -252,15 +294,21 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int half = W / 2; half >= 1; half /= 2) {
     if (wave >= half && wave < 2 * half) {
-      float *rw = red + (size_t)(wave - half) * 1024;
+      float *rw = red + (size_t)(wave - half) * 1024 * RG;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) *reinterpret_cast<f32x4_t *>(rw + g * 256 + lane * 4) = acc[g];
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4_t *>(rw + (rg * 4 + g) * 256 + lane * 4) = acc[rg][g];
     }
     __syncthreads();
     if (wave < half) {
-      const float *rw = red + (size_t)wave * 1024;
+      const float *rw = red + (size_t)wave * 1024 * RG;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) acc[g] += *reinterpret_cast<const f32x4_t *>(rw + g * 256 + lane * 4);
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          acc[rg][g] += *reinterpret_cast<const f32x4_t *>(rw + (rg * 4 + g) * 256 + lane * 4);
     }
     __syncthreads();
   }
@@ -268,21 +316,28 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   // share of the finish
   if (wave == 0) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[(4 * q + e) * 64 + 16 * g + i] = acc[g][e];
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(16 * rg + 4 * q + e) * 64 + 16 * g + i] = acc[rg][g][e];
   }
   __syncthreads();
-  finish_tile<MR, 1, false, 64 * W>(
-      red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t}, partial,
-      counters, m, s, S, 0, ep);
+  if (ep.parts.n > 0) {
+    const PartUnit u = part_unit(ep, t, T);
+    finish_tile<MR, 1, false, 64 * W>(red, u.out, partial, counters, m, s, S, 0, u.ep);
+  } else {
+    finish_tile<MR, 1, false, 64 * W>(
+        red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t}, partial,
+        counters, m, s, S, 0, ep);
+  }
 }
 
-template <int ACT, int W, bool DOTS, bool PAIRS>
+template <int ACT, int W, bool DOTS, bool PAIRS, int RG>
 hipError_t launch_t16_k(const GemvArgs &a, hipStream_t stream) {
   const int nblk_max = (a.NB + a.split_k - 1) / a.split_k;
-  const size_t lds = t16_lds_bytes<ACT, W>(nblk_max);
-  auto kern = gemv_tile16_kernel<ACT, W, DOTS, PAIRS>;
+  const size_t lds = t16_lds_bytes<ACT, W, RG>(nblk_max);
+  auto kern = gemv_tile16_kernel<ACT, W, DOTS, PAIRS, RG>;
   static size_t granted = 64 * 1024;
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
@@ -293,47 +348,71 @@ hipError_t launch_t16_k(const GemvArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int ACT, int W, bool DOTS>
-hipError_t launch_t16(bool pairs, const GemvArgs &a, hipStream_t stream) {
-  if constexpr (ACT == kActBf16) {
-    if (pairs) return launch_t16_k<ACT, W, DOTS, true>(a, stream);
-  }
-  return launch_t16_k<ACT, W, DOTS, false>(a, stream);
-}
-
+// Instantiated: 16 rows with 4, 8 or 16 waves (bf16 also with two-block
+// stages); 32 rows with 4, 8 or 16 waves; 64 rows with 4 or 8 waves (their
+// accumulators and stages do not fit 16 waves' registers).
 template <int ACT, bool DOTS>
-hipError_t launch_t16_w(int waves, bool pairs, const GemvArgs &a, hipStream_t stream) {
-  switch (waves) {
-    case 4: return launch_t16<ACT, 4, DOTS>(pairs, a, stream);
-    case 8: return launch_t16<ACT, 8, DOTS>(pairs, a, stream);
-    case 16: return launch_t16<ACT, 16, DOTS>(pairs, a, stream);
-    default: return hipErrorInvalidValue;
+hipError_t launch_t16_rw(int rows, int waves, bool pairs, const GemvArgs &a, hipStream_t stream) {
+  if (rows == 16 && pairs && ACT == kActBf16) {
+    switch (waves) {
+      case 4: return launch_t16_k<ACT, 4, DOTS, true, 1>(a, stream);
+      case 8: return launch_t16_k<ACT, 8, DOTS, true, 1>(a, stream);
+      case 16: return launch_t16_k<ACT, 16, DOTS, true, 1>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (pairs) return hipErrorInvalidValue;
+  if (rows == 16) {
+    switch (waves) {
+      case 4: return launch_t16_k<ACT, 4, DOTS, false, 1>(a, stream);
+      case 8: return launch_t16_k<ACT, 8, DOTS, false, 1>(a, stream);
+      case 16: return launch_t16_k<ACT, 16, DOTS, false, 1>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (rows == 32) {
+    switch (waves) {
+      case 4: return launch_t16_k<ACT, 4, DOTS, false, 2>(a, stream);
+      case 8: return launch_t16_k<ACT, 8, DOTS, false, 2>(a, stream);
+      case 16: return launch_t16_k<ACT, 16, DOTS, false, 2>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (rows == 64) {
+    switch (waves) {
+      case 4: return launch_t16_k<ACT, 4, DOTS, false, 4>(a, stream);
+      case 8: return launch_t16_k<ACT, 8, DOTS, false, 4>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool tile16_instantiated(int rows, int act, bool write_dots, int waves, int kslices) {
-  if (rows != 16 || (waves != 4 && waves != 8 && waves != 16)) return false;
+  const bool w = rows == 64 ? (waves == 4 || waves == 8)
+                            : (rows == 16 || rows == 32) && (waves == 4 || waves == 8 || waves == 16);
+  if (!w) return false;
   if (act == kActQ8) return kslices == 1;
-  return act == kActBf16 && !write_dots && (kslices == 1 || kslices == 2);
+  return act == kActBf16 && !write_dots && (kslices == 1 || (kslices == 2 && rows == 16));
 }
 
-size_t tile16_lds_bytes(int act, int waves, int NB, int split_k) {
+size_t tile16_lds_bytes(int rows, int act, int waves, int NB, int split_k) {
   const int nblk = (NB + split_k - 1) / split_k;
-  const size_t first = act == kActQ8 ? (size_t)nblk * 16 * 4 : (size_t)waves * 2048;
-  return first + (size_t)(waves / 2) * 1024 * 4;
+  const int rg = rows / 16;
+  const size_t first = act == kActQ8 ? (size_t)nblk * 16 * rg * 4 : (size_t)waves * 2048;
+  return first + (size_t)(waves / 2) * 1024 * 4 * rg;
 }
 
-hipError_t launch_gemv_tile16(int act, int waves, int kslices, bool write_dots,
+hipError_t launch_gemv_tile16(int rows, int act, int waves, int kslices, bool write_dots,
                               const GemvArgs &a, hipStream_t stream) {
-  if (a.ep.nw != 1 || a.ep.parts.n > 0) return hipErrorInvalidValue;
-  if (act == kActQ8 && kslices == 1)
-    return write_dots ? launch_t16_w<kActQ8, true>(waves, false, a, stream)
-                      : launch_t16_w<kActQ8, false>(waves, false, a, stream);
-  if (act == kActBf16 && !write_dots && (kslices == 1 || kslices == 2))
-    return launch_t16_w<kActBf16, false>(waves, kslices == 2, a, stream);
-  return hipErrorInvalidValue;
+  if (a.ep.nw != 1 || (a.ep.parts.n > 0 && write_dots)) return hipErrorInvalidValue;
+  if (!tile16_instantiated(rows, act, write_dots, waves, kslices)) return hipErrorInvalidValue;
+  if (act == kActQ8)
+    return write_dots ? launch_t16_rw<kActQ8, true>(rows, waves, false, a, stream)
+                      : launch_t16_rw<kActQ8, false>(rows, waves, false, a, stream);
+  return launch_t16_rw<kActBf16, false>(rows, waves, kslices == 2, a, stream);
 }
 
 }  // namespace q8

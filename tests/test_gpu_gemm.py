@@ -67,7 +67,8 @@ def test_gemm_q8(m, K, N):
     assert (y[:, N:].view(np.uint32) == 0).all()
 
 
-@pytest.mark.parametrize("m,K,N", [(1, 32, 1), (33, 96, 40), (130, 320, 130), (200, 1056, 64)])
+@pytest.mark.parametrize("m,K,N", [(1, 32, 1), (33, 96, 40), (17, 2176, 257), (64, 1056, 130),
+                                   (48, 4096, 640), (130, 320, 130), (200, 1056, 64)])
 def test_gemm_block_dots_bit_exact(m, K, N):
     x, q, _ = inputs.random_case(m, K, N, seed=5000 + m + N)
     Wq, _ = g.pack(q, np.ones((K // 32, N), np.float32))
@@ -168,6 +169,31 @@ def test_gemm_most_rows():
     assert_close(y[:, :N], ref, bnd, "gemm int8 m=8192")
 
 
+# Up to 64 rows the product streams each column tile once through the
+# tile-per-workgroup kernel (16, 32 or 64 rows a wave; 8 waves, or 4 where a
+# long K's int8 activation scales fill the LDS); a K whose scales do not fit
+# even then goes to the GEMM.  Full sizes, sampled columns.
+@pytest.mark.parametrize("m,K,N,act", [(17, 4096, 14336, BF16), (48, 4096, 14336, BF16),
+                                       (64, 4096, 14336, BF16), (64, 5120, 32000, BF16),
+                                       (33, 4096, 14336, Q8), (64, 4096, 14336, Q8),
+                                       (64, 14336, 4096, Q8), (64, 16384, 200, Q8)])
+def test_gemm_tile_rows_full_size(m, K, N, act):
+    x, q, s = inputs.random_case(m, K, N, seed=5300 + m + K // 32 + N)
+    Wq, Ws = g.pack(q, s)
+    cols = _sample_cols(N, n=160, seed=m + N)
+    if act == BF16:
+        y = gemm(xdev(x), Wq, Ws, m, K, N, BF16)
+        ref, bnd = oracle.gemv_bf16(x, q, s, cols)
+    else:
+        buf = g.quantize(x)
+        xq, dx = g.act_host(buf, m, K)
+        y = gemm(buf, Wq, Ws, m, K, N, Q8)
+        ref, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
+    assert_close(y[:, cols], ref, bnd, f"gemm m={m} K={K} N={N} act={act}")
+    assert (y[:, N:].view(np.uint32) == 0).all()
+    assert np.isfinite(y).all()
+
+
 # ------------------------------------------------------------------------------
 # the GEMM in parts (plan.rs, GemmParts above the GEMV's rows)
 # ------------------------------------------------------------------------------
@@ -187,7 +213,7 @@ PART_SETS = [(200, 40, 64, 130), (4096, 1024, 1024), (96,), (320, 260)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8, q8.Q8_ACT_Q8_0_TWO_WORDS])
-@pytest.mark.parametrize("m", [1, 33, 100, 200])
+@pytest.mark.parametrize("m", [1, 33, 64, 100, 200])
 @pytest.mark.parametrize("Ns", PART_SETS)
 def test_gemm_parts(act, m, Ns):
     K = 1056 if max(Ns) < 4096 else 512
@@ -239,3 +265,32 @@ def test_gemm_parts_qkv_prefill_full_size():
         z, bnd = oracle.gemv_bf16(x, q, s)
         z, bnd = oracle.epilogue(z, bnd, b)
         assert_close(y[:, :N], z, bnd, f"qkv part {i}")
+
+
+@pytest.mark.parametrize("act", [BF16, Q8])
+def test_gemm_parts_tile_rows_full_size(act):
+    """A gated pair's two 14336-column projections of a 40-row chunk in one
+    launch (tile-per-workgroup kernel): sampled columns against the oracle,
+    and the part without a bias bit for bit equal to q8_gemm on it alone."""
+    m, K, Ns = 40, 4096, (14336, 14336)
+    x = inputs.gen_x(m, K, 5400 + act)
+    ws = [(inputs.gen_q(K, N, 5401 + i), inputs.gen_scales(K, N, 5401 + i)) for i, N in enumerate(Ns)]
+    biases = [inputs.gen_bias(Ns[0], seed=5410), None]
+    packed = [g.pack(q, s) for q, s in ws]
+    if act == BF16:
+        xin = xdev(x)
+    else:
+        xin = g.quantize(x)
+        xq, dx = g.act_host(xin, m, K)
+    ys = gemm_parts(xin, packed, Ns, biases, m, K, act)
+    for i, ((q, s), N, b, y) in enumerate(zip(ws, Ns, biases, ys)):
+        cols = _sample_cols(N, n=128, seed=i)
+        if act == BF16:
+            z, bnd = oracle.gemv_bf16(x, q, s, cols)
+        else:
+            z, bnd = oracle.gemv_q8(xq, dx, q, s, cols)
+        z, bnd = oracle.epilogue(z, bnd, b, cols=cols)
+        assert_close(y[:, cols], z, bnd, f"tile-rows part {i} act={act}")
+        assert (y[:, N:].view(np.uint32) == 0).all()
+    y1 = gemm(xin, *packed[1], m, K, Ns[1], act)
+    np.testing.assert_array_equal(ys[1].view(np.uint32), y1.view(np.uint32))

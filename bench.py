@@ -87,7 +87,8 @@ def kernel_name(plan: dict, w) -> str:
     if plan["kernel"] == 5:
         return f"gemv_mfma32w_kernel<{wv}, false, {ks}>"
     if plan["kernel"] == 6:
-        return f"gemv_tile16_kernel<{act}, {wv}, false, {'true' if ks == 2 else 'false'}>"
+        return (f"gemv_tile16_kernel<{act}, {wv}, false, {'true' if ks == 2 else 'false'}, "
+                f"{r // 16}>")
     return f"gemv_mfma_cols_kernel<{r}, {act}, false, {ks}, {wv // (4 * ks)}, false, false>"
 
 

@@ -255,12 +255,19 @@ q8_plan tile32_plan(int64_t K, int64_t N) {
 // 9.3 / 9.5; N=1024 (8 splits): 6.7 / 6.9 / 7.1 against 8.4 / 8.5 / 8.6.
 // Q8_0, K=4096, N=14336: 13.6 / 13.9 / 14.1 against 15.2 / 15.6 / 16.1;
 // K=5120, N=32000: 31.5 / 31.8 / 32.1 against 31.9 / 33.2 / 34.4.
+//
+// 17-32 bf16 rows take the same kernel with two row groups of 16 (rows 32), 8
+// waves, one-block stages; measured on MI355X against the column-group and
+// block-interleaved kernels the single-product plan took before (loop us):
+// K=4096, N=14336: m=24 18.2 against 23.0, m=32 19.9 against 23.0 (16 waves
+// 20.0); K=5120, N=32000, m=32: 46.8 against 58.0 (4 waves 48.4); K=4096,
+// N=4096 (4 splits), m=32: 11.5 against 12.2.
 q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   const int64_t NB = K / Q8_BLOCK;
   const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
   q8_plan p;
   p.kernel = Q8_KERNEL_MFMA16_TILE;
-  p.rows = 16;
+  p.rows = m <= 16 ? 16 : 32;
   p.kslices = 1;
   p.waves = 16;
   // bf16, swept on MI355X (loop us, best plan against the next form):
@@ -272,7 +279,9 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   //     against 32.8, 34.3);
   //   K = 4096, N = 4096 (4 splits): one-block stages, 8 waves up to 8 rows
   //     (m = 3: 8.0 against 8.2), 16 above (m = 16: 8.4 against 8.8).
-  if (act_fmt == Q8_ACT_BF16) {
+  if (act_fmt == Q8_ACT_BF16 && m > 16) {
+    p.waves = 8;
+  } else if (act_fmt == Q8_ACT_BF16) {
     if (T >= 384) {
       p.kslices = m >= 12 ? 2 : 1;
       p.waves = m >= 12 ? 4 : 8;
@@ -329,7 +338,7 @@ q8_plan default_plan(int64_t m, int64_t K, int64_t N, int act_fmt, bool tiles = 
   const DeviceFacts dev = device_facts();
   const int64_t smax = NB / 40 > 0 ? NB / 40 : 1;
   if (tiles && act_fmt == Q8_ACT_Q8_0 && m > 16) return tile32_plan(K, N);
-  if (tiles && act_fmt != Q8_ACT_Q8_0_TWO_WORDS && m > 2 && m <= 16)
+  if (tiles && act_fmt != Q8_ACT_Q8_0_TWO_WORDS && m > 2 && (m <= 16 || act_fmt == Q8_ACT_BF16))
     return tile16_plan(m, K, N, act_fmt);
   q8_plan p;
   p.kslices = 1;
@@ -753,10 +762,28 @@ int check_parts_args(const void *x, const q8_part *parts, int n_parts, int64_t m
 // keeps at least 32 blocks (measured on
 // MI355X, m = 16, K = 4096, N = 4096 + 1024 + 1024: one split 14.7 us, two
 // 12.1 us, three 16.0 us).
+//
+// From 3 rows of bf16 or one-word Q8_0 activations the parts take the
+// 16x16x32 tile kernel (its workgroups walk the parts' tiles), with the
+// single product's rows and K split; below 128 tiles 16 waves and one-block
+// stages.  Measured on MI355X, K = 4096, N = 4096 + 1024 + 1024 (2 splits,
+// loop us, against the block-interleaved MFMA kernel): bf16 m = 3, 8, 16:
+// 9.9, 10.1, 10.8 against 11.5, 11.6, 11.8 (8 waves 10.1-11.4; two-block
+// stages 10.2-10.9); m = 24: 13.2 against 14.1; Q8_0 m = 16: 10.8 against
+// 12.5; m = 32: 14.1 against 15.6 (8 waves 14.5; 3 splits 16.3).
 q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
-  q8_plan p = default_plan(m, K, cols, act_fmt, false);
   const int64_t NB = K / Q8_BLOCK;
   const int64_t units = cols / Q8_TILE_COLS;
+  if (act_fmt != Q8_ACT_Q8_0_TWO_WORDS && m > 2) {
+    q8_plan t = tile16_plan(m, K, cols, act_fmt);
+    if (units < 128) {
+      t.waves = 16;
+      t.kslices = 1;
+      fit_tile_lds(t, NB, act_fmt);
+    }
+    return t;
+  }
+  q8_plan p = default_plan(m, K, cols, act_fmt, false);
   const DeviceFacts dev = device_facts();
   if (p.kernel == Q8_KERNEL_MFMA_COLS) {
     p.kernel = Q8_KERNEL_MFMA;
@@ -781,12 +808,14 @@ q8_plan parts_default_plan(int64_t m, int64_t K, int64_t cols, int act_fmt) {
 int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64_t K,
               int64_t cols, int act_fmt, const q8_plan &plan, hipStream_t stream,
               void *workspace, size_t ws_bytes) {
-  if (plan.kernel == Q8_KERNEL_MFMA_COLS || plan.kernel >= Q8_KERNEL_MFMA32)
+  if (plan.kernel == Q8_KERNEL_MFMA_COLS ||
+      (plan.kernel >= Q8_KERNEL_MFMA32 && plan.kernel != Q8_KERNEL_MFMA16_TILE))
     return fail(Q8_ERR_PLAN, "the MFMA_COLS and MFMA32 kernels do not run parts: "
-                "use the VALU or MFMA kernel");
+                "use the VALU, MFMA or MFMA16_TILE kernel");
   int st = check_plan(&plan, m, K, act_fmt, false);
   if (st) return st;
-  if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
+  if (act_fmt != Q8_ACT_BF16 && (act_scales_offset_of(act_fmt, m, K) > 0xffffffffull ||
+                                 act_view_offset(m, K) > 0xffffffffull))
     return fail(Q8_ERR_SHAPE, "activation too large");
   q8::GemvArgs a{};
   a.x = x;
@@ -800,6 +829,7 @@ int run_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, int64
   a.T = (int)(cols / Q8_TILE_COLS);
   a.split_k = plan.split_k;
   a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+  a.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
   a.ep.N = (int)parts[0].N;
   a.ep.write_y = 1;
   a.ep.nw = 1;

@@ -247,21 +247,33 @@ def test_parts_validation():
 
 
 def test_parts_plan_is_the_side_by_side_product():
-    # the parts' columns side by side are one product's work; the column-group
-    # and 32x32 tile kernels (which do not walk parts) are replaced by the
-    # MFMA kernel
+    # the parts' columns side by side are one product's work: 1-2 rows the
+    # single product's VALU plan; from 3 rows of bf16 or one-word Q8_0 the
+    # 16x16x32 tile kernel (which walks parts) with 16 or 32 rows and the
+    # split its single-product plan takes, below 128 tiles 16 waves of
+    # one-block stages; two-word activations the block-interleaved MFMA kernel
     for (m, K, Ns, act) in ((1, 4096, (4096, 1024, 1024), 0), (8, 4096, (4096, 1024, 1024), 1),
                             (16, 4096, (4096, 1024, 1024), 0), (32, 4096, (100, 30), 1),
-                            (4, 2048, (200,), 1)):
+                            (4, 2048, (200,), 1), (24, 4096, (8192, 8192), 0),
+                            (12, 4096, (14336, 14336), 0)):
         parts = [_part(N) for N in Ns]
         got = q8.q8_gemv_parts_default_plan(parts, m, K, act)
-        wide = q8.q8_gemv_default_plan(m, K, sum(q8.q8_padded_cols(N) for N in Ns), act)
-        if wide.kernel != q8.Q8_KERNEL_MFMA_COLS and wide.kernel < q8.Q8_KERNEL_MFMA32:
+        cols = sum(q8.q8_padded_cols(N) for N in Ns)
+        wide = q8.q8_gemv_default_plan(m, K, cols, act)
+        if m <= 2:
             assert (got.kernel, got.rows, got.split_k) == (wide.kernel, wide.rows, wide.split_k)
+            continue
+        assert got.kernel == q8.Q8_KERNEL_MFMA16_TILE and got.rows == (16 if m <= 16 else 32)
+        if wide.kernel == q8.Q8_KERNEL_MFMA16_TILE:
+            assert (got.rows, got.split_k) == (wide.rows, wide.split_k)
+        if cols // 64 < 128:
+            assert (got.waves, got.kslices) == (16, 1)
         else:
-            # these kernels walk no parts: the MFMA kernel instead
-            assert got.kernel in (q8.Q8_KERNEL_VALU, q8.Q8_KERNEL_MFMA) and got.rows >= m
-            assert 1 <= got.split_k <= K // 32
+            assert (got.waves, got.kslices) == (wide.waves, wide.kslices)
+        assert 1 <= got.split_k <= K // 32
+    got = q8.q8_gemv_parts_default_plan([_part(4096), _part(1024)], 8, 4096,
+                                        q8.Q8_ACT_Q8_0_TWO_WORDS)
+    assert got.kernel == q8.Q8_KERNEL_MFMA
 
 
 def test_two_word_rules():

@@ -23,7 +23,9 @@ def _write(path, header, rows):
 def test_kernel_name_and_grid_of_plans():
     w = inputs.WORKLOADS["batch16_k4096_n14336"]
     p = {"kernel": 6, "rows": 16, "split_k": 1, "waves": 16, "kslices": 2}
-    assert bench.kernel_name(p, w) == "gemv_tile16_kernel<0, 16, false, true>"
+    assert bench.kernel_name(p, w) == "gemv_tile16_kernel<0, 16, false, true, 1>"
+    p32 = {"kernel": 6, "rows": 32, "split_k": 1, "waves": 8, "kslices": 1}
+    assert bench.kernel_name(p32, w) == "gemv_tile16_kernel<0, 8, false, false, 2>"
     assert bench.plan_grid(p, w) == f"{224 * 64 * 16}x1x1"
     w5 = inputs.WORKLOADS["q8act_m32_k5120_n40"]
     p5 = {"kernel": 5, "rows": 32, "split_k": 4, "waves": 16, "kslices": 1}
@@ -59,7 +61,7 @@ def test_summarize_kernel_trace_labels_configs(tmp_path, capsys):
     hdr = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Grid_Size_Y",
            "Grid_Size_Z", "Workgroup_Size_X"]
     k0 = "void q8::(anonymous namespace)::gemv_valu_kernel<1, 0, false, 8, false, false>(...)"
-    k6 = "void q8::(anonymous namespace)::gemv_tile16_kernel<0, 16, false, true>(...)"
+    k6 = "void q8::(anonymous namespace)::gemv_tile16_kernel<0, 16, false, true, 1>(...)"
     rows = [[k0, 0, 11000 + i, 224 * 512, 1, 1, 512] for i in range(10)]
     rows += [[k0, 0, 3000, 16 * 512, 1, 1, 512] for _ in range(4)]
     rows += [[k6, 0, 14000, 224 * 1024, 1, 1, 1024] for _ in range(6)]

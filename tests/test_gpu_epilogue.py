@@ -121,7 +121,7 @@ EXACT_PLANS = [None,
                (q8.Q8_KERNEL_MFMA32_TILE, 32, 1, 8, 1), (q8.Q8_KERNEL_MFMA32_TILE, 32, 3, 16, 1),
                (q8.Q8_KERNEL_MFMA32_TILE, 32, 2, 8, 2),
                (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 1), (q8.Q8_KERNEL_MFMA16_TILE, 16, 4, 4, 1),
-               (q8.Q8_KERNEL_MFMA16_TILE, 16, 2, 16, 2)]
+               (q8.Q8_KERNEL_MFMA16_TILE, 16, 2, 16, 2), (q8.Q8_KERNEL_MFMA16_TILE, 32, 3, 8, 1)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8])
@@ -181,6 +181,9 @@ RANDOM_PLANS = [
     (16, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 8, 2)),
     (9, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 3, 4, 2)),
     (3, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 16, 2)),
+    (32, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 32, 1, 8, 1)),
+    (20, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 32, 4, 16, 1)),
+    (25, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 32, 2, 4, 1)),
 ]
 
 

@@ -223,6 +223,11 @@ def _plans(m, NB):
                 if split <= NB:
                     for ks in (1, 2):
                         out.append((q8.Q8_KERNEL_MFMA16_TILE, 16, split, waves, ks))
+    if m <= 32:
+        for waves in (4, 8, 16):
+            for split in splits:
+                if split <= NB:
+                    out.append((q8.Q8_KERNEL_MFMA16_TILE, 32, split, waves, 1))
     return out
 
 
@@ -471,16 +476,22 @@ def test_widest_n():
 
 def test_long_k_tile_kernels():
     """K = 2^20 on the tile kernels' default plans (their LDS of the split's
-    activation scales raises the K split): 20 int8 rows (32x32x32 kernel) and
-    16 bf16 rows (16x16x32 kernel, both stage sizes)."""
+    activation scales raises the K split): 20 int8 rows (32x32x32 kernel),
+    16 bf16 rows (16x16x32 kernel, both stage sizes) and 24 bf16 rows (its two
+    row groups)."""
     K, N = 1 << 20, 70
-    for m, act in ((20, Q8), (16, BF16)):
+    for m, act in ((20, Q8), (16, BF16), (24, BF16)):
         x, q, s = inputs.random_case(m, K, N, seed=99 + m)
         Wq, Ws = g.pack(q, s)
         if act == BF16:
             ref, bnd = oracle.gemv_bf16(x, q, s)
-            for plan in (None, g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 16, 2),
-                         g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 8, 1)):
+            p = q8.q8_gemv_default_plan(m, K, N, BF16)
+            assert p.kernel == q8.Q8_KERNEL_MFMA16_TILE and p.rows == (16 if m <= 16 else 32)
+            plans = [None]
+            if m <= 16:
+                plans += [g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 16, 2),
+                          g.plan(q8.Q8_KERNEL_MFMA16_TILE, 16, 64, 8, 1)]
+            for plan in plans:
                 y = g.gemv(xdev(x), Wq, Ws, m, K, N, BF16, plan)
                 assert_close(y[:, :N], ref, bnd, f"K=2^20 bf16 m={m} plan={plan}")
                 assert (y[:, N:].view(np.uint32) == 0).all()
@@ -495,7 +506,7 @@ def test_long_k_tile_kernels():
             assert (y[:, N:].view(np.uint32) == 0).all()
 
 
-@pytest.mark.parametrize("m,act", [(3, BF16), (17, Q8)])
+@pytest.mark.parametrize("m,act", [(3, BF16), (17, Q8), (29, BF16)])
 def test_widest_n_tile_kernels(m, act):
     """N = 2^24 - 5 on the tile kernels (2^18 workgroups, the last tile
     ragged), one block of K; sampled columns and the tile edges."""

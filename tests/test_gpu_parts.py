@@ -81,6 +81,12 @@ PLANS = [
     (16, BF16, (q8.Q8_KERNEL_MFMA, 16, 2, 8, 1)),
     (32, Q8, (q8.Q8_KERNEL_MFMA, 32, 1, 16, 1)),
     (32, Q8, (q8.Q8_KERNEL_MFMA, 32, 5, 4, 1)),
+    (3, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 2, 16, 1)),
+    (16, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 16, 3, 8, 1)),
+    (13, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 4, 2)),
+    (24, BF16, (q8.Q8_KERNEL_MFMA16_TILE, 32, 2, 16, 1)),
+    (32, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 32, 5, 8, 1)),
+    (17, Q8, (q8.Q8_KERNEL_MFMA16_TILE, 32, 1, 4, 1)),
 ]
 SHAPES = [(200, 40, 64, 130), (96,), (40, 300)]
 

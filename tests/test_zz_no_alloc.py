@@ -73,12 +73,12 @@ def test_noalloc_without_split_and_repeated():
 
 
 def test_noalloc_rejects_a_workspace_beyond_the_scratch():
-    # a long K of 32 bf16 rows: the MFMA plan splits K in ~26 for the LDS,
-    # ~27 MB of partial carries
-    m, K, N = 32, 65536, 8192
-    need = q8.q8_gemv_workspace_bytes(m, K, N, BF16)
+    # K = 2^20 for 16 int8 rows: the tile kernel splits K in ~17 so that the
+    # split's activation scales fit the LDS, ~18 MB of partial carries
+    m, K, N = 16, 1 << 20, 16384
+    need = q8.q8_gemv_workspace_bytes(m, K, N, Q8)
     assert need > q8.q8_noalloc_scratch_bytes()
     A = 1 << 20                           # host-side refusal: never dereferenced
     with pytest.raises(q8.Q8Error) as e:
-        q8.q8_gemv_noalloc(A, A, A, A, m, K, N, BF16, 0)
+        q8.q8_gemv_noalloc(A, A, A, A, m, K, N, Q8, 0)
     assert e.value.status == 5 and "scratch" in e.value.message

@@ -302,22 +302,37 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   return p;
 }
 
-// The many-row product at up to 64 rows of bf16 or one-word Q8_0: the GEMM
-// gives each workgroup 64 rows by four column tiles, so at these rows it runs
-// one workgroup per four tiles, too few to cover the CUs, and its workgroups
-// still compute 64 rows.  Instead each column tile streams once through the
-// tile-per-workgroup kernel (MFMA16_TILE, 16, 32 or 64 rows a wave), without
-// a K split, so that it needs no workspace.  The choice depends on m, K and
-// the format only, so a part of q8_gemm_parts takes the same kernel, with the
-// same per-tile arithmetic, as q8_gemm on it alone.
+// The many-row product at few rows of bf16 or one-word Q8_0: the GEMM gives
+// each workgroup 64 or 128 rows by four or two column tiles, so at these rows
+// it runs one workgroup per several tiles, too few to cover the CUs.  Instead
+// each column tile streams through the tile-per-workgroup kernel (MFMA16_TILE,
+// 16, 32 or 64 rows a wave; above 64 rows one workgroup per tile and chunk of
+// 64 rows), without a K split, so that it needs no workspace.  Up to 64 rows
+// always; up to 256 while the workgroups (tiles x chunks) stay within 512
+// (bf16) or 1024 (int8, whose GEMM is slower).  Measured on MI355X (loop us,
+// tile kernel against the GEMM), K = 4096: bf16 N = 14336: m = 65 45.8
+// against 69.9, m = 128 54.8 against 70.8, m = 160 72.8 against 72.9, m = 192
+// 80.9 against 73.4; bf16 m = 128: N = 4096 26.5 against 68.2, N = 8192 27.8
+// against 69.2, N = 20480 80.1 against 72.4; bf16 m = 96, N = 24576 77.9
+// against 73.0; m = 256, N = 4096 27.3 against 68.3 (int8 28.3 against
+// 125.6); int8 N = 14336: m = 128 54.0 against 129.0, m = 192 79.5 against
+// 129.2, m = 256 106.8 against 130.5; K = 5120, N = 32000: bf16 m = 64 70.9
+// against 98.9, m = 96 124.3 against 93.4, m = 128 140.3 against 96.1; int8
+// m = 128 133.3 against 168.2, m = 160 190.8 against 191.6.  The choice
+// depends on m, K, the format and the product's own width, so q8_gemm_parts
+// routes each part as q8_gemm would route it alone.
 struct GemmTileRoute {
   bool on;
   int rows, waves;
 };
-GemmTileRoute gemm_tile_route(int64_t m, int64_t K, int act_fmt) {
+constexpr int64_t kTileRouteRows = 256;
+GemmTileRoute gemm_tile_route(int64_t m, int64_t K, int64_t N, int act_fmt) {
   GemmTileRoute r{false, 0, 0};
-  if (m > 64 || (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)) return r;
+  if (m > kTileRouteRows || (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)) return r;
   if (act_fmt == Q8_ACT_Q8_0 && act_view_offset(m, K) > 0xffffffffull) return r;
+  const int64_t chunks = (m + 63) / 64;
+  const int64_t T = round_up(N, Q8_TILE_COLS) / Q8_TILE_COLS;
+  if (chunks > 1 && T * chunks > (act_fmt == Q8_ACT_BF16 ? 512 : 1024)) return r;
   r.rows = m <= 16 ? 16 : (m <= 32 ? 32 : 64);
   const size_t budget = (size_t)device_facts().lds_per_block - kStaticLdsReserve;
   for (int w : {8, 4}) {
@@ -1136,7 +1151,7 @@ int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
   const int64_t Npad = round_up(N, Q8_TILE_COLS);
-  const GemmTileRoute route = gemm_tile_route(m, K, act_fmt);
+  const GemmTileRoute route = gemm_tile_route(m, K, N, act_fmt);
   if (route.on) {
     q8::GemvArgs g{};
     g.x = x;
@@ -1206,46 +1221,58 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
   if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
-  q8::Parts pp{};
-  pp.n = n_parts;
-  pp.cum[0] = 0;
-  for (int i = 0; i < q8::kMaxParts; ++i) {
-    const bool on = i < n_parts;
-    pp.wq[i] = on ? parts[i].W_q8 : nullptr;
-    pp.wsc[i] = on ? parts[i].W_q8_scale : nullptr;
-    pp.y[i] = on ? parts[i].y : nullptr;
-    pp.bias[i] = on ? parts[i].bias : nullptr;
-    pp.N[i] = on ? (int)parts[i].N : 0;
-    pp.cum[i + 1] =
-        pp.cum[i] + (on ? (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS) : 0);
+  // Each part goes where q8_gemm would take it alone: the parts of each kind
+  // side by side in one launch (so at most two launches).
+  GemmTileRoute route{false, 0, 0};
+  bool tile_part[q8::kMaxParts] = {};
+  for (int i = 0; i < n_parts; ++i) {
+    const GemmTileRoute r = gemm_tile_route(m, K, parts[i].N, act_fmt);
+    tile_part[i] = r.on;
+    if (r.on) route = r;   // rows and waves depend on m, K and the format only
   }
-  const GemmTileRoute route = gemm_tile_route(m, K, act_fmt);
-  hipError_t e;
-  (void)hipGetLastError();
-  if (route.on) {
-    q8::GemvArgs g{};
-    g.x = x;
-    g.m = (int)m;
-    g.K = (int)K;
-    g.NB = (int)(K / Q8_BLOCK);
-    g.T = pp.cum[n_parts];
-    g.Npad = g.T * Q8_TILE_COLS;
-    g.split_k = 1;
-    g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-    g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
-    g.ep.write_y = 1;
-    g.ep.nw = 1;
-    g.ep.parts = pp;
-    e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, false, g, stream);
-  } else {
-    q8::GemmArgs a{};
-    a.x = x;
-    a.m = (int)m;
-    a.K = (int)K;
-    a.NB = (int)(K / Q8_BLOCK);
-    a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-    a.parts = pp;
-    e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
+  hipError_t e = hipSuccess;
+  for (int kind = 0; kind < 2 && e == hipSuccess; ++kind) {
+    const bool tile = kind == 0;
+    q8::Parts pp{};
+    pp.cum[0] = 0;
+    for (int i = 0; i < n_parts; ++i) {
+      if (tile_part[i] != tile) continue;
+      const int k = pp.n++;
+      pp.wq[k] = parts[i].W_q8;
+      pp.wsc[k] = parts[i].W_q8_scale;
+      pp.y[k] = parts[i].y;
+      pp.bias[k] = parts[i].bias;
+      pp.N[k] = (int)parts[i].N;
+      pp.cum[k + 1] = pp.cum[k] + (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS);
+    }
+    for (int k = pp.n; k < q8::kMaxParts; ++k) pp.cum[k + 1] = pp.cum[k];
+    if (pp.n == 0) continue;
+    (void)hipGetLastError();
+    if (tile) {
+      q8::GemvArgs g{};
+      g.x = x;
+      g.m = (int)m;
+      g.K = (int)K;
+      g.NB = (int)(K / Q8_BLOCK);
+      g.T = pp.cum[pp.n];
+      g.Npad = g.T * Q8_TILE_COLS;
+      g.split_k = 1;
+      g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+      g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
+      g.ep.write_y = 1;
+      g.ep.nw = 1;
+      g.ep.parts = pp;
+      e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, false, g, stream);
+    } else {
+      q8::GemmArgs a{};
+      a.x = x;
+      a.m = (int)m;
+      a.K = (int)K;
+      a.NB = (int)(K / Q8_BLOCK);
+      a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+      a.parts = pp;
+      e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
+    }
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();

@@ -77,6 +77,9 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const int q = lane >> 4, i = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x, s = blockIdx.y;
+  // rows r0 .. r0 + mz - 1 of the activation: a chunk of MR rows (grid z)
+  const int r0 = blockIdx.z * MR;
+  const int mz = min(m - r0, MR);
   int b_lo, b_hi;
   split_range(s, split_q, split_r, b_lo, b_hi);
   const int nblk = b_hi - b_lo;
@@ -95,16 +98,19 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   const buf_t wr = make_buf(wt + (size_t)tt * NB * kChunkBytes, (unsigned)NB * kChunkBytes);
   const buf_t sr = DOTS ? wr : make_buf(stt + (size_t)tt * NB * kTile, (unsigned)NB * kTile * 4);
   const unsigned lw = (unsigned)lane * 16u, ls = (unsigned)i * 16u;
-  // the activation: bf16 rows, or the int8 view (block b's m rows at b*m*32).
-  // Lanes of rows past m load row 0 (or, for the pair's whole lines, read
-  // zero past the buffer's extent): those rows of D are never read, and an
-  // unconditional load keeps the stage's loads out of branches.
+  // the activation: the chunk's bf16 rows, or the int8 view (block b's m
+  // rows at b*m*32; row r0 + r of the chunk).  Lanes of rows past the chunk
+  // load its first row (or, for the pair's whole lines, read zero past the
+  // buffer's extent): those rows of D are never read, and an unconditional
+  // load keeps the stage's loads out of branches.
   int ri[RG];
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) ri[rg] = 16 * rg + i < m ? 16 * rg + i : 0;
+  for (int rg = 0; rg < RG; ++rg)
+    ri[rg] = (kQ8 ? r0 : 0) + (16 * rg + i < mz ? 16 * rg + i : 0);
   const buf_t xr = kQ8 ? make_buf(static_cast<const char *>(xv) + act_view_off,
                                   (unsigned)m * (unsigned)K)
-                       : make_buf(xv, (unsigned)m * (unsigned)K * 2u);
+                       : make_buf(static_cast<const char *>(xv) + (size_t)r0 * K * 2,
+                                  (unsigned)mz * (unsigned)K * 2u);
   // int8: the view, 8 bytes a lane (row i, k = 8q ..).  bf16 single blocks:
   // 16 bytes a lane (row i, k = 8q ..) from the rows.  bf16 pairs: a stage
   // holds two consecutive blocks; its activation is read as whole cache lines
@@ -164,12 +170,13 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
   char *scr = lds + (size_t)wave * 2048;   // bf16: this wave's transpose scratch
   float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4 : (size_t)W * 2048));
   if constexpr (kQ8 && !DOTS) {
-    // the split's activation scales, [block][row], rows past m zero
+    // the split's activation scales of the chunk's rows, [block][row], rows
+    // past the chunk zero
     const float *dxp =
         reinterpret_cast<const float *>(static_cast<const char *>(xv) + act_scale_off);
     for (int p = threadIdx.x; p < nblk * MR; p += 64 * W) {
       const int r = p / nblk, bb = p - r * nblk;
-      dxs[bb * MR + r] = (r < m) ? dxp[(size_t)r * NB + b_lo + bb] : 0.0f;
+      dxs[bb * MR + r] = (r < mz) ? dxp[(size_t)(r0 + r) * NB + b_lo + bb] : 0.0f;
     }
     __syncthreads();
   }
@@ -217,7 +224,8 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 16 * rg + 4 * q + e;
-              if (r < m) dots[((size_t)r * NB + bb) * Npad + (size_t)t * kTile + 16 * g + i] = d[e];
+              if (r < mz)
+                dots[((size_t)(r0 + r) * NB + bb) * Npad + (size_t)t * kTile + 16 * g + i] = d[e];
             }
           } else {
 #pragma unroll
@@ -323,13 +331,17 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         for (int e = 0; e < 4; ++e) red[(16 * rg + 4 * q + e) * 64 + 16 * g + i] = acc[rg][g][e];
   }
   __syncthreads();
+  // the chunk's rows of the output (a launch of several chunks has one split
+  // and a plain epilogue)
   if (ep.parts.n > 0) {
-    const PartUnit u = part_unit(ep, t, T);
-    finish_tile<MR, 1, false, 64 * W>(red, u.out, partial, counters, m, s, S, 0, u.ep);
+    PartUnit u = part_unit(ep, t, T);
+    u.out.y += (size_t)r0 * u.out.Npad;
+    finish_tile<MR, 1, false, 64 * W>(red, u.out, partial, counters, mz, s, S, 0, u.ep);
   } else {
     finish_tile<MR, 1, false, 64 * W>(
-        red, TileOut{y, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad, (unsigned)t}, partial,
-        counters, m, s, S, 0, ep);
+        red, TileOut{y + (size_t)r0 * Npad, Npad, (size_t)t * kTile, (size_t)t * kTile, Npad,
+                     (unsigned)t},
+        partial, counters, mz, s, S, 0, ep);
   }
 }
 
@@ -342,7 +354,8 @@ hipError_t launch_t16_k(const GemvArgs &a, hipStream_t stream) {
   hipError_t e = grant_lds(kern, lds, granted);
   if (e != hipSuccess) return e;
   (void)hipGetLastError();
-  kern<<<dim3((unsigned)a.T, (unsigned)a.split_k), dim3(64 * W), lds, stream>>>(
+  const unsigned chunks = (unsigned)((a.m + 16 * RG - 1) / (16 * RG));
+  kern<<<dim3((unsigned)a.T, (unsigned)a.split_k, chunks), dim3(64 * W), lds, stream>>>(
       a.x, a.wq, a.wsc, a.y, a.partial, a.counters, a.dots, a.m, a.K, a.NB, a.Npad, a.T,
       a.split_k, a.NB / a.split_k, a.NB % a.split_k, a.act_scale_off, a.act_view_off, a.ep);
   return hipGetLastError();
@@ -408,6 +421,10 @@ size_t tile16_lds_bytes(int rows, int act, int waves, int NB, int split_k) {
 hipError_t launch_gemv_tile16(int rows, int act, int waves, int kslices, bool write_dots,
                               const GemvArgs &a, hipStream_t stream) {
   if (a.ep.nw != 1 || (a.ep.parts.n > 0 && write_dots)) return hipErrorInvalidValue;
+  // more rows than a wave covers: chunks of rows in grid z, one split and no
+  // row-wise epilogue (residual, output quantizer)
+  if (a.m > rows && (a.split_k != 1 || kslices != 1 || a.ep.residual || a.ep.yq))
+    return hipErrorInvalidValue;
   if (!tile16_instantiated(rows, act, write_dots, waves, kslices)) return hipErrorInvalidValue;
   if (act == kActQ8)
     return write_dots ? launch_t16_rw<kActQ8, true>(rows, waves, false, a, stream)

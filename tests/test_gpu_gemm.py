@@ -38,7 +38,7 @@ def gemm_dots(xbuf, Wq, m, K, N):
     return d.cpu().numpy()
 
 
-SHAPES = [(m, K, N) for m in (1, 7, 33, 64, 65, 130, 200)
+SHAPES = [(m, K, N) for m in (1, 7, 33, 64, 65, 130, 200, 257, 300)
           for (K, N) in ((32, 1), (96, 40), (1056, 200), (2176, 257))]
 
 
@@ -68,7 +68,8 @@ def test_gemm_q8(m, K, N):
 
 
 @pytest.mark.parametrize("m,K,N", [(1, 32, 1), (33, 96, 40), (17, 2176, 257), (64, 1056, 130),
-                                   (48, 4096, 640), (130, 320, 130), (200, 1056, 64)])
+                                   (48, 4096, 640), (100, 1056, 130), (130, 320, 130),
+                                   (200, 1056, 64), (300, 320, 130)])
 def test_gemm_block_dots_bit_exact(m, K, N):
     x, q, _ = inputs.random_case(m, K, N, seed=5000 + m + N)
     Wq, _ = g.pack(q, np.ones((K // 32, N), np.float32))
@@ -172,11 +173,16 @@ def test_gemm_most_rows():
 # Up to 64 rows the product streams each column tile once through the
 # tile-per-workgroup kernel (16, 32 or 64 rows a wave; 8 waves, or 4 where a
 # long K's int8 activation scales fill the LDS); a K whose scales do not fit
-# even then goes to the GEMM.  Full sizes, sampled columns.
+# even then goes to the GEMM.  Up to 256 rows, chunks of 64 rows in workgroups
+# of their own while tiles x chunks stay within 512 (bf16) or 1024 (int8).
+# Full sizes, sampled columns.
 @pytest.mark.parametrize("m,K,N,act", [(17, 4096, 14336, BF16), (48, 4096, 14336, BF16),
                                        (64, 4096, 14336, BF16), (64, 5120, 32000, BF16),
                                        (33, 4096, 14336, Q8), (64, 4096, 14336, Q8),
-                                       (64, 14336, 4096, Q8), (64, 16384, 200, Q8)])
+                                       (64, 14336, 4096, Q8), (64, 16384, 200, Q8),
+                                       (128, 4096, 14336, BF16), (200, 4096, 14336, Q8),
+                                       (256, 4096, 4096, BF16), (96, 4096, 24576, BF16),
+                                       (250, 5120, 1000, Q8)])
 def test_gemm_tile_rows_full_size(m, K, N, act):
     x, q, s = inputs.random_case(m, K, N, seed=5300 + m + K // 32 + N)
     Wq, Ws = g.pack(q, s)
@@ -213,7 +219,7 @@ PART_SETS = [(200, 40, 64, 130), (4096, 1024, 1024), (96,), (320, 260)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8, q8.Q8_ACT_Q8_0_TWO_WORDS])
-@pytest.mark.parametrize("m", [1, 33, 64, 100, 200])
+@pytest.mark.parametrize("m", [1, 33, 64, 100, 200, 300])
 @pytest.mark.parametrize("Ns", PART_SETS)
 def test_gemm_parts(act, m, Ns):
     K = 1056 if max(Ns) < 4096 else 512
@@ -294,3 +300,22 @@ def test_gemm_parts_tile_rows_full_size(act):
         assert (y[:, N:].view(np.uint32) == 0).all()
     y1 = gemm(xin, *packed[1], m, K, Ns[1], act)
     np.testing.assert_array_equal(ys[1].view(np.uint32), y1.view(np.uint32))
+
+
+def test_gemm_parts_split_between_kernels():
+    """Parts whose widths put them on different kernels (128 bf16 rows: 14336
+    columns on the tile kernel, 24576 on the GEMM) run as two launches; each
+    part against the oracle on sampled columns and bit for bit equal to
+    q8_gemm on it alone."""
+    m, K, Ns = 128, 4096, (14336, 24576)
+    x = inputs.gen_x(m, K, 5500)
+    ws = [(inputs.gen_q(K, N, 5501 + i), inputs.gen_scales(K, N, 5501 + i)) for i, N in enumerate(Ns)]
+    packed = [g.pack(q, s) for q, s in ws]
+    xin = xdev(x)
+    ys = gemm_parts(xin, packed, Ns, [None, None], m, K, BF16)
+    for i, ((q, s), N, y) in enumerate(zip(ws, Ns, ys)):
+        cols = _sample_cols(N, n=96, seed=10 + i)
+        z, bnd = oracle.gemv_bf16(x, q, s, cols)
+        assert_close(y[:, cols], z, bnd, f"split part {i}")
+        y1 = gemm(xin, *packed[i], m, K, N, BF16)
+        np.testing.assert_array_equal(y.view(np.uint32), y1.view(np.uint32))

@@ -420,14 +420,15 @@ size_t q8_parts_workspace_bytes(const q8_plan *plan, const q8_part *parts,
  * m x K bf16 or the q8_quantize_act buffer of m rows, y m x N_pad fp32 (pad
  * columns 0).  The pages' CUDA planner runs the product as a tensor-core GEMM
  * above its GEMV's rows (codegen_cuda/lane/plan.rs, Launch::on_tensor_cores,
- * gemm_blk_rows); this is its matrix-core form on gfx950.  Up to 64 rows of
+ * gemm_blk_rows); this is its matrix-core form on gfx950.  At few rows of
  * bf16 or one-word Q8_0 activations each 64-column tile of the weight is
- * streamed once by one workgroup (the GEMV's 16x16x32 tile kernel, 16, 32 or
- * 64 rows a wave), unless K is so long that its int8 activation scales do
- * not fit a workgroup's LDS (with 160 KiB: K above 16256, 36608 or 77312 at
- * 64, 32 or 16 rows); above 64 rows, and for two-word activations, a GEMM of
- * 64- or 128-row blocks.  No workspace; the call
- * allocates nothing.  Requires K > 0, K % 32 == 0, N >= 1.  Two-word
+ * streamed by one workgroup per chunk of up to 64 rows (the GEMV's 16x16x32
+ * tile kernel, 16, 32 or 64 rows a wave): up to 64 rows always, up to 256
+ * while tiles x chunks stay within 512 (bf16) or 1024 (int8), unless K is so
+ * long that its int8 activation scales do not fit a workgroup's LDS (with
+ * 160 KiB: K above 16256, 36608 or 77312 at 64, 32 or 16 rows a chunk);
+ * otherwise, and for two-word activations, a GEMM of 64- or 128-row blocks.
+ * No workspace; the call allocates nothing.  Requires K > 0, K % 32 == 0, N >= 1.  Two-word
  * activations (act_fmt 2, the pages' two-pass numerics, whose GEMM plan.rs
  * runs with fewer rows per block): each block's first and second words run
  * as two int8 matrix-core passes joined exactly in int32 before the scale,
@@ -452,11 +453,13 @@ int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
  *     y_i[r, n] = (x . W_i)[r, n] + bias_i[n]        n < N_i (pad columns 0)
  * with q8_gemm's arithmetic; the parts (a host array, 1 <= n_parts <=
  * Q8_MAX_PARTS, padded widths summing to at most 2^24), x and act_fmt as in
- * q8_gemv_parts, for 1 <= m <= Q8_MAX_GEMM_ROWS.  Each part's columns start a
- * new column block of the GEMM (up to 64 rows: each tile is its own
- * workgroup, as in q8_gemm), so a part's outputs are bit-identical to q8_gemm
- * on that part alone (before the bias).  No workspace; allocates nothing.
- * Errors as q8_gemv_parts.
+ * q8_gemv_parts, for 1 <= m <= Q8_MAX_GEMM_ROWS.  Each part takes the kernel
+ * q8_gemm would take for it alone (so the parts run as one launch, or two
+ * when their widths put them on both kernels), and each part's columns start
+ * a new column block of the GEMM (on the tile kernel every tile is its own
+ * workgroup), so a part's outputs are bit-identical to q8_gemm on that part
+ * alone (before the bias).  No workspace; allocates nothing.  Errors as
+ * q8_gemv_parts.
  */
 int q8_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m,
                   int64_t K, int act_fmt, hipStream_t stream);

@@ -34,7 +34,8 @@ and m = 16; `context` gives
 the read ceiling (q8_stream_read over the headline's bytes, best of a grid
 sweep), the headline with one weight copy reused and a 1 GiB device copy's
 rate;
-`prefill` times the many-row product (m = 512) against the MFMA peak, with
+`prefill` times the many-row product (m = 512, and m = 128 on the tile
+kernel's row chunks) against the MFMA peak, with
 bf16, one-word and two-word int8 activations.
 """
 import argparse
@@ -927,6 +928,10 @@ def main():
     if not args.no_prefill:
         for other in ("prefill_m512_k4096_n14336", "prefill_q8act_m512_k4096_n14336"):
             prefill[inputs.WORKLOADS[other].act] = measure_gemm(
+                inputs.WORKLOADS[other], max(100, args.steps // 10), max(10, args.warmup // 10),
+                rotate=not args.no_rotate)
+        for other in ("prefill_m128_k4096_n14336", "prefill_q8act_m128_k4096_n14336"):
+            prefill[inputs.WORKLOADS[other].act + "_m128"] = measure_gemm(
                 inputs.WORKLOADS[other], max(100, args.steps // 10), max(10, args.warmup // 10),
                 rotate=not args.no_rotate)
         prefill["q8_0_two_words"] = measure_gemm(

@@ -61,6 +61,12 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill_q8act_m512_k4096_n14336": Workload("prefill_q8act_m512_k4096_n14336", 512, 4096, 14336,
                                                 "q8_0", 1008, 1008,
                                                 note="the same chunk with Q8_0 activations"),
+    "prefill_m128_k4096_n14336": Workload("prefill_m128_k4096_n14336", 128, 4096, 14336, "bf16",
+                                          1013, 1013,
+                                          note="m=128 prefill chunk (the tile kernel's row chunks)"),
+    "prefill_q8act_m128_k4096_n14336": Workload("prefill_q8act_m128_k4096_n14336", 128, 4096,
+                                                14336, "q8_0", 1014, 1014,
+                                                note="the m=128 chunk with Q8_0 activations"),
 }
 
 HEADLINE = "decode_k4096_n14336"

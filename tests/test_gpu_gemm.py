@@ -124,7 +124,8 @@ def test_gemm_shape_errors():
     assert e.value.status == 1
 
 
-@pytest.mark.parametrize("name", ["prefill_m512_k4096_n14336", "prefill_q8act_m512_k4096_n14336"])
+@pytest.mark.parametrize("name", ["prefill_m512_k4096_n14336", "prefill_q8act_m512_k4096_n14336",
+                                  "prefill_m128_k4096_n14336", "prefill_q8act_m128_k4096_n14336"])
 def test_prefill_full_size(name):
     w = inputs.WORKLOADS[name]
     x, q, s = inputs.generate(w)

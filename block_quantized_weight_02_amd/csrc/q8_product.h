@@ -156,6 +156,42 @@ __device__ __forceinline__ void finish_tile(const float *red, const TileOut &o,
                                             unsigned *__restrict__ counters, int m, int s, int S,
                                             int wsel, const Epi &ep) {
   const int arrivals = S * (PAIR ? 2 : 1);
+  if (!PAIR && arrivals == 1) {
+    // One split, one weight: the bias and residual of all the thread's
+    // elements are loaded first, so that their round trips overlap rather
+    // than one per element (the stores in between may alias them for the
+    // compiler); the additions keep final_value's order.
+    constexpr int kIt = (MR * 64 + NT - 1) / NT;
+    float bz[kIt], rz[kIt];
+#pragma unroll
+    for (int k = 0; k < kIt; ++k) {
+      const int idx = (int)threadIdx.x + k * NT;
+      const int r = idx >> 6;
+      const size_t col = o.col0 + (idx & 63);
+      const bool live = idx < MR * 64 && r < m && (int)col < ep.N;
+      bz[k] = (live && ep.bias) ? ep.bias[col] : 0.0f;
+      rz[k] = (live && ep.residual) ? ep.residual[(size_t)r * o.Npad + col] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kIt; ++k) {
+      const int idx = (int)threadIdx.x + k * NT;
+      const int r = idx >> 6, c = idx & 63;
+      if (idx < MR * 64 && r < m) {
+        float v = red[idx];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += red[w * MR * 64 + idx];
+        const size_t col = o.col0 + c;
+        float z = 0.0f;
+        if ((int)col < ep.N) {
+          z = v;
+          if (ep.bias) z += bz[k];
+          if (ep.residual) z += rz[k];
+        }
+        store_final(ep, o.y, o.Npad, m, r, col, z);
+      }
+    }
+    return;
+  }
   for (int idx = threadIdx.x; idx < MR * 64; idx += NT) {
     const int r = idx >> 6, c = idx & 63;
     if (r < m) {

@@ -299,6 +299,11 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
   if (S < 1) S = 1;
   p.split_k = (int32_t)S;
   fit_tile_lds(p, NB, act_fmt);
+  // two-block stages only where the last K split has an even block count
+  if (p.kslices == 2 && (NB / p.split_k) % 2 != 0) {
+    p.kslices = 1;
+    p.waves = 8;
+  }
   return p;
 }
 
@@ -323,11 +328,11 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
 // routes each part as q8_gemm would route it alone.
 struct GemmTileRoute {
   bool on;
-  int rows, waves;
+  int rows, waves, kslices;
 };
 constexpr int64_t kTileRouteRows = 256;
 GemmTileRoute gemm_tile_route(int64_t m, int64_t K, int64_t N, int act_fmt) {
-  GemmTileRoute r{false, 0, 0};
+  GemmTileRoute r{false, 0, 0, 1};
   if (m > kTileRouteRows || (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)) return r;
   if (act_fmt == Q8_ACT_Q8_0 && act_view_offset(m, K) > 0xffffffffull) return r;
   const int64_t chunks = (m + 63) / 64;
@@ -462,6 +467,15 @@ int check_plan(const q8_plan *p, int64_t m, int64_t K, int act, bool dots) {
     return fail(Q8_ERR_PLAN,
                 "no kernel built for kernel=%d rows=%d act=%d dots=%d waves=%d kslices=%d",
                 p->kernel, p->rows, act, (int)dots, p->waves, p->kslices);
+  // Two-block stages of the 16x16x32 tile kernel read a pair's two blocks of
+  // every row as whole lines: a pair that started at the rows' last block
+  // would read past the last row.  Its waves' pairs start at the split's
+  // first block plus even offsets, so the last split (K/32 / split_k blocks)
+  // must have an even count.
+  if (p->kernel == Q8_KERNEL_MFMA16_TILE && p->kslices == 2 && (NB / p->split_k) % 2 != 0)
+    return fail(Q8_ERR_PLAN, "two-block stages need an even block count in the last K split "
+                "(K/32 / split_k = %lld): use kslices 1 or another split_k",
+                (long long)(NB / p->split_k));
   if (p->kernel != Q8_KERNEL_VALU) {
     const size_t need =
         q8::gemv_lds_bytes(p->kernel, p->rows, act, p->waves, p->kslices, (int)NB, p->split_k);
@@ -1171,8 +1185,8 @@ int run_gemm(const void *x, const int8_t *W_q8, const float *W_q8_scale, float *
     g.ep.write_y = 1;
     g.ep.nw = 1;
     (void)hipGetLastError();
-    hipError_t e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, dots != nullptr,
-                                          g, stream);
+    hipError_t e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, route.kslices,
+                                          dots != nullptr, g, stream);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return hip_fail(e, "gemm launch");
@@ -1223,7 +1237,7 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
                 (long long)(m * K));
   // Each part goes where q8_gemm would take it alone: the parts of each kind
   // side by side in one launch (so at most two launches).
-  GemmTileRoute route{false, 0, 0};
+  GemmTileRoute route{false, 0, 0, 1};
   bool tile_part[q8::kMaxParts] = {};
   for (int i = 0; i < n_parts; ++i) {
     const GemmTileRoute r = gemm_tile_route(m, K, parts[i].N, act_fmt);
@@ -1262,7 +1276,8 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
       g.ep.write_y = 1;
       g.ep.nw = 1;
       g.ep.parts = pp;
-      e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, 1, false, g, stream);
+      e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, route.kslices, false, g,
+                                 stream);
     } else {
       q8::GemmArgs a{};
       a.x = x;

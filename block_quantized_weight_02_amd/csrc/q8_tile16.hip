@@ -46,7 +46,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2v_t;
 // (the activation transpose); then the carries' halves.
 template <int ACT, int W, int RG>
 constexpr size_t t16_lds_bytes(int nblk) {
-  return (ACT == kActQ8 ? (size_t)nblk * 16 * RG * 4 : (size_t)W * 2048) +
+  return (ACT == kActQ8 ? (size_t)nblk * 16 * RG * 4 : (size_t)W * 2048 * RG) +
          (size_t)(W / 2) * 1024 * 4 * RG;
 }
 
@@ -70,7 +70,6 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
                    int split_q, int split_r, unsigned act_scale_off, unsigned act_view_off,
                    Epi ep) {
   constexpr int MR = 16 * RG;
-  static_assert(!PAIRS || RG == 1, "two-block stages take 16 rows");
   constexpr bool kQ8 = ACT == kActQ8;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
@@ -122,14 +121,15 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
     xoff[rg] = kQ8      ? (unsigned)ri[rg] * 32u + (unsigned)q * 8u
-               : PAIRS ? (unsigned)lrow * (unsigned)K * 2u + (unsigned)(lane & 7) * 16u
+               : PAIRS ? (unsigned)(16 * rg + lrow) * (unsigned)K * 2u + (unsigned)(lane & 7) * 16u
                        : (unsigned)ri[rg] * (unsigned)K * 2u + (unsigned)q * 16u;
   const unsigned xoff8 = (unsigned)8 * (unsigned)K * 2u;   // rows 8 .. 15
 
   struct Stage {
     uint4 lo[U], hi[U];   // column `lane`'s k = 0..15 and 16..31 of each block
     float4 sc[U];         // scales of columns i, i+16, i+32, i+48
-    uint4 a[RG > 1 ? RG : 2];   // row group rg's fragment (int8: .xy); pairs: the two loads
+    uint4 a[PAIRS ? 2 * RG : (RG > 1 ? RG : 2)];   // row group rg's fragment (int8: .xy);
+                                                   // pairs: row group rg's two loads
   };
   auto load = [&](Stage &st, int bv) {
     const int b = __builtin_amdgcn_readfirstlane(bv);
@@ -155,20 +155,26 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         st.a[rg] = make_uint4(v.x, v.y, v.z, v.w);
       }
     } else {
+      // (a pair never starts at the rows' last block: the host allows
+      // two-block stages only where the last split has an even number of
+      // blocks, so no read runs past the last row's end)
 #pragma unroll
-      for (int v2 = 0; v2 < 2; ++v2) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-            xr, xoff[0] + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
-        st.a[v2] = make_uint4(v.x, v.y, v.z, v.w);
-      }
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+              xr, xoff[rg] + (unsigned)v2 * xoff8, (unsigned)b * 64u, 0);
+          st.a[2 * rg + v2] = make_uint4(v.x, v.y, v.z, v.w);
+        }
     }
   };
 
   Stage A, B;
   if (b_lo + U * wave < b_hi) load(A, b_lo + U * wave);
   float *dxs = reinterpret_cast<float *>(lds);
-  char *scr = lds + (size_t)wave * 2048;   // bf16: this wave's transpose scratch
-  float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4 : (size_t)W * 2048));
+  char *scr = lds + (size_t)wave * 2048 * RG;   // bf16: this wave's transpose scratch
+  float *red = reinterpret_cast<float *>(lds + (kQ8 ? (size_t)nblk_max * MR * 4
+                                                     : (size_t)W * 2048 * RG));
   if constexpr (kQ8 && !DOTS) {
     // the split's activation scales of the chunk's rows, [block][row], rows
     // past the chunk zero
@@ -260,14 +266,19 @@ gemv_tile16_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
       // the pair's rows through LDS: row r's 128 bytes at r * 128, then the
       // MFMA fragment of block u (row i, k = 8q ..) at i * 128 + 64u + 16q
 #pragma unroll
-      for (int v2 = 0; v2 < 2; ++v2)
-        *reinterpret_cast<uint4 *>(scr + (8 * v2 + lrow) * 128 + (lane & 7) * 16) = st.a[v2];
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2)
+          *reinterpret_cast<uint4 *>(scr + rg * 2048 + (8 * v2 + lrow) * 128 + (lane & 7) * 16) =
+              st.a[2 * rg + v2];
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes are done
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (b0 + u >= b_hi) break;
         uint4 af[RG];
-        af[0] = *reinterpret_cast<const uint4 *>(scr + i * 128 + 64 * u + 16 * q);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg)
+          af[rg] = *reinterpret_cast<const uint4 *>(scr + rg * 2048 + i * 128 + 64 * u + 16 * q);
         compute1(st, u, b0 + u, af);
       }
     }
@@ -362,8 +373,9 @@ hipError_t launch_t16_k(const GemvArgs &a, hipStream_t stream) {
 }
 
 // Instantiated: 16 rows with 4, 8 or 16 waves (bf16 also with two-block
-// stages); 32 rows with 4, 8 or 16 waves; 64 rows with 4 or 8 waves (their
-// accumulators and stages do not fit 16 waves' registers).
+// stages); 32 rows with 4, 8 or 16 waves (bf16 two-block stages with 4 or 8);
+// 64 rows with 4 or 8 waves (their accumulators and stages do not fit 16
+// waves' registers; with two-block stages not even 8 waves').
 template <int ACT, bool DOTS>
 hipError_t launch_t16_rw(int rows, int waves, bool pairs, const GemvArgs &a, hipStream_t stream) {
   if (rows == 16 && pairs && ACT == kActBf16) {
@@ -371,6 +383,13 @@ hipError_t launch_t16_rw(int rows, int waves, bool pairs, const GemvArgs &a, hip
       case 4: return launch_t16_k<ACT, 4, DOTS, true, 1>(a, stream);
       case 8: return launch_t16_k<ACT, 8, DOTS, true, 1>(a, stream);
       case 16: return launch_t16_k<ACT, 16, DOTS, true, 1>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (rows == 32 && pairs && ACT == kActBf16) {
+    switch (waves) {
+      case 4: return launch_t16_k<ACT, 4, DOTS, true, 2>(a, stream);
+      case 8: return launch_t16_k<ACT, 8, DOTS, true, 2>(a, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -408,13 +427,14 @@ bool tile16_instantiated(int rows, int act, bool write_dots, int waves, int ksli
                             : (rows == 16 || rows == 32) && (waves == 4 || waves == 8 || waves == 16);
   if (!w) return false;
   if (act == kActQ8) return kslices == 1;
-  return act == kActBf16 && !write_dots && (kslices == 1 || (kslices == 2 && rows == 16));
+  return act == kActBf16 && !write_dots &&
+         (kslices == 1 || (kslices == 2 && (rows == 16 || (rows == 32 && waves <= 8))));
 }
 
 size_t tile16_lds_bytes(int rows, int act, int waves, int NB, int split_k) {
   const int nblk = (NB + split_k - 1) / split_k;
   const int rg = rows / 16;
-  const size_t first = act == kActQ8 ? (size_t)nblk * 16 * rg * 4 : (size_t)waves * 2048;
+  const size_t first = act == kActQ8 ? (size_t)nblk * 16 * rg * 4 : (size_t)waves * 2048 * rg;
   return first + (size_t)(waves / 2) * 1024 * 4 * rg;
 }
 
@@ -423,7 +443,7 @@ hipError_t launch_gemv_tile16(int rows, int act, int waves, int kslices, bool wr
   if (a.ep.nw != 1 || (a.ep.parts.n > 0 && write_dots)) return hipErrorInvalidValue;
   // more rows than a wave covers: chunks of rows in grid z, one split and no
   // row-wise epilogue (residual, output quantizer)
-  if (a.m > rows && (a.split_k != 1 || kslices != 1 || a.ep.residual || a.ep.yq))
+  if (a.m > rows && (a.split_k != 1 || a.ep.residual || a.ep.yq))
     return hipErrorInvalidValue;
   if (!tile16_instantiated(rows, act, write_dots, waves, kslices)) return hipErrorInvalidValue;
   if (act == kActQ8)

@@ -323,3 +323,20 @@ def test_stream_read_argument_errors():
     expect(1, q8.q8_stream_read, A, 1024, 256, 8, 3, A, S0)
     msg = expect(1, q8.q8_stream_read, A, 1 << 33, 1, 8, 2, A, S0)  # an 8 GiB slice
     assert "slice" in msg
+
+
+def test_two_block_stages_need_an_even_last_split():
+    # the 16x16x32 tile kernel's two-block stages read a pair's two blocks of
+    # every row as whole lines; a pair starting at the rows' last block would
+    # read past the last row, so plans whose last K split has an odd block
+    # count are refused, and the default plan takes one-block stages there
+    p = q8.q8_plan()
+    p.kernel, p.rows, p.split_k, p.waves, p.kslices = q8.Q8_KERNEL_MFMA16_TILE, 16, 1, 16, 2
+    msg = expect(7, q8.q8_gemv_planned, A, A, A, A, 16, 1056, 14336, 0, p, S0, A, 1 << 30)
+    assert "even" in msg
+    p.split_k = 3          # 33 blocks: splits of 11 -> odd
+    expect(7, q8.q8_gemv_planned, A, A, A, A, 16, 1056, 14336, 0, p, S0, A, 1 << 30)
+    for (K, N) in ((1056, 14336), (1056, 32000), (4128, 14336)):
+        d = q8.q8_gemv_default_plan(16, K, N, 0)
+        if d.kernel == q8.Q8_KERNEL_MFMA16_TILE and d.kslices == 2:
+            assert (K // 32 // d.split_k) % 2 == 0

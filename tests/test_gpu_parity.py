@@ -227,7 +227,8 @@ def _plans(m, NB):
         for waves in (4, 8, 16):
             for split in splits:
                 if split <= NB:
-                    out.append((q8.Q8_KERNEL_MFMA16_TILE, 32, split, waves, 1))
+                    for ks in (1, 2):
+                        out.append((q8.Q8_KERNEL_MFMA16_TILE, 32, split, waves, ks))
     return out
 
 

@@ -229,13 +229,16 @@ typedef enum {
                               waves (4, 8 or 16; with kslices 2: 4 or 8) split K,
                               the activation fragments loaded with the weights and
                               shared by the kslices (1 or 2) tiles of a wave       */
-  Q8_KERNEL_MFMA16_TILE = 6 /* 16x16x32 block dots of up to 16 rows (bf16 or one-word
-                              Q8_0) with the VALU kernel's weight stream: one
-                              workgroup per (tile, K split), waves (4, 8 or 16)
-                              split K, kslices = blocks a wave's stage holds (bf16:
-                              1, or 2 with the activation read as whole lines and
-                              moved into place through the LDS; Q8_0: 1); one
-                              weight                                                */
+  Q8_KERNEL_MFMA16_TILE = 6 /* 16x16x32 block dots of 16 or 32 rows (bf16 or
+                              one-word Q8_0; rows 32 as two groups of 16) with the
+                              VALU kernel's weight stream: one workgroup per (tile,
+                              K split), waves (4, 8 or 16) split K, kslices =
+                              blocks a wave's stage holds (bf16: 1, or 2 with the
+                              activation read as whole lines and moved into place
+                              through the LDS, 32 rows with 4 or 8 waves only, and
+                              only where the last K split, K/32 / split_k blocks,
+                              is even, else Q8_ERR_PLAN; Q8_0: 1); one weight, or
+                              the parts                                             */
 } q8_kernel;
 
 typedef struct q8_plan {

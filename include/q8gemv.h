@@ -245,7 +245,7 @@ typedef struct q8_plan {
   int32_t kernel;  /* q8_kernel                                                */
   int32_t rows;    /* row count the kernel is built for: VALU 1,2,4,8,16,32
                       (two-word activations: 1, 2, 4); MFMA 16 or 32 (two-word
-                      activations: 32); >= m                                    */
+                      activations: 32); MFMA32* 32; MFMA16_TILE 16 or 32; >= m  */
   int32_t split_k; /* K splits across workgroups, 1..K/32                      */
   int32_t waves;   /* waves (64 lanes) per workgroup: 4, 8 or 16               */
   int32_t kslices; /* MFMA_COLS: waves that split one 16-column group's K range

@@ -313,7 +313,7 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
 // each column tile streams through the tile-per-workgroup kernel (MFMA16_TILE,
 // 16, 32 or 64 rows a wave; above 64 rows one workgroup per tile and chunk of
 // 64 rows), without a K split, so that it needs no workspace.  Up to 64 rows
-// always; up to 256 while the workgroups (tiles x chunks) stay within 512
+// always; up to 1024 while the workgroups (tiles x chunks) stay within 512
 // (bf16) or 1024 (int8, whose GEMM is slower).  Measured on MI355X (loop us,
 // tile kernel against the GEMM), K = 4096: bf16 N = 14336: m = 65 45.8
 // against 69.9, m = 128 54.8 against 70.8, m = 160 72.8 against 72.9, m = 192
@@ -323,14 +323,19 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
 // 125.6); int8 N = 14336: m = 128 54.0 against 129.0, m = 192 79.5 against
 // 129.2, m = 256 106.8 against 130.5; K = 5120, N = 32000: bf16 m = 64 70.9
 // against 98.9, m = 96 124.3 against 93.4, m = 128 140.3 against 96.1; int8
-// m = 128 133.3 against 168.2, m = 160 190.8 against 191.6.  The choice
+// m = 128 133.3 against 168.2, m = 160 190.8 against 191.6; bf16 m = 384 and
+// 512, N = 4096: 51.8 and 53.8 against 69.2 and 70.0; m = 512, N = 2048 and
+// 1024: 27.5 and 25.8 against 68.2 and 67.5; m = 1024, N = 1024: 27.4
+// against 66.5; K = 14336, m = 512, N = 4096: 164.5 against 228.8; int8
+// m = 512, N = 4096 and 8192: 55.2 and 109.2 against 126.2 and 129.6;
+// m = 1024, N = 2048: 57.3 against 126.0.  The choice
 // depends on m, K, the format and the product's own width, so q8_gemm_parts
 // routes each part as q8_gemm would route it alone.
 struct GemmTileRoute {
   bool on;
   int rows, waves, kslices;
 };
-constexpr int64_t kTileRouteRows = 256;
+constexpr int64_t kTileRouteRows = 1024;
 GemmTileRoute gemm_tile_route(int64_t m, int64_t K, int64_t N, int act_fmt) {
   GemmTileRoute r{false, 0, 0, 1};
   if (m > kTileRouteRows || (act_fmt != Q8_ACT_BF16 && act_fmt != Q8_ACT_Q8_0)) return r;

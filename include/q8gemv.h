@@ -426,7 +426,7 @@ size_t q8_parts_workspace_bytes(const q8_plan *plan, const q8_part *parts,
  * gemm_blk_rows); this is its matrix-core form on gfx950.  At few rows of
  * bf16 or one-word Q8_0 activations each 64-column tile of the weight is
  * streamed by one workgroup per chunk of up to 64 rows (the GEMV's 16x16x32
- * tile kernel, 16, 32 or 64 rows a wave): up to 64 rows always, up to 256
+ * tile kernel, 16, 32 or 64 rows a wave): up to 64 rows always, up to 1024
  * while tiles x chunks stay within 512 (bf16) or 1024 (int8), unless K is so
  * long that its int8 activation scales do not fit a workgroup's LDS (with
  * 160 KiB: K above 16256, 36608 or 77312 at 64, 32 or 16 rows a chunk);

@@ -38,7 +38,7 @@ def gemm_dots(xbuf, Wq, m, K, N):
     return d.cpu().numpy()
 
 
-SHAPES = [(m, K, N) for m in (1, 7, 33, 64, 65, 130, 200, 257, 300)
+SHAPES = [(m, K, N) for m in (1, 7, 33, 64, 65, 130, 200, 257, 300, 1100)
           for (K, N) in ((32, 1), (96, 40), (1056, 200), (2176, 257))]
 
 
@@ -69,7 +69,7 @@ def test_gemm_q8(m, K, N):
 
 @pytest.mark.parametrize("m,K,N", [(1, 32, 1), (33, 96, 40), (17, 2176, 257), (64, 1056, 130),
                                    (48, 4096, 640), (100, 1056, 130), (130, 320, 130),
-                                   (200, 1056, 64), (300, 320, 130)])
+                                   (200, 1056, 64), (300, 320, 130), (1100, 320, 130)])
 def test_gemm_block_dots_bit_exact(m, K, N):
     x, q, _ = inputs.random_case(m, K, N, seed=5000 + m + N)
     Wq, _ = g.pack(q, np.ones((K // 32, N), np.float32))
@@ -174,8 +174,9 @@ def test_gemm_most_rows():
 # Up to 64 rows the product streams each column tile once through the
 # tile-per-workgroup kernel (16, 32 or 64 rows a wave; 8 waves, or 4 where a
 # long K's int8 activation scales fill the LDS); a K whose scales do not fit
-# even then goes to the GEMM.  Up to 256 rows, chunks of 64 rows in workgroups
-# of their own while tiles x chunks stay within 512 (bf16) or 1024 (int8).
+# even then goes to the GEMM.  Up to 1024 rows, chunks of 64 rows in
+# workgroups of their own while tiles x chunks stay within 512 (bf16) or 1024
+# (int8).
 # Full sizes, sampled columns.
 @pytest.mark.parametrize("m,K,N,act", [(17, 4096, 14336, BF16), (48, 4096, 14336, BF16),
                                        (64, 4096, 14336, BF16), (64, 5120, 32000, BF16),
@@ -183,7 +184,8 @@ def test_gemm_most_rows():
                                        (64, 14336, 4096, Q8), (64, 16384, 200, Q8),
                                        (128, 4096, 14336, BF16), (200, 4096, 14336, Q8),
                                        (256, 4096, 4096, BF16), (96, 4096, 24576, BF16),
-                                       (250, 5120, 1000, Q8)])
+                                       (250, 5120, 1000, Q8), (512, 4096, 2048, BF16),
+                                       (1024, 4096, 1024, BF16), (1000, 2048, 2048, Q8)])
 def test_gemm_tile_rows_full_size(m, K, N, act):
     x, q, s = inputs.random_case(m, K, N, seed=5300 + m + K // 32 + N)
     Wq, Ws = g.pack(q, s)
@@ -220,7 +222,7 @@ PART_SETS = [(200, 40, 64, 130), (4096, 1024, 1024), (96,), (320, 260)]
 
 
 @pytest.mark.parametrize("act", [BF16, Q8, q8.Q8_ACT_Q8_0_TWO_WORDS])
-@pytest.mark.parametrize("m", [1, 33, 64, 100, 200, 300])
+@pytest.mark.parametrize("m", [1, 33, 64, 100, 200, 300, 1100])
 @pytest.mark.parametrize("Ns", PART_SETS)
 def test_gemm_parts(act, m, Ns):
     K = 1056 if max(Ns) < 4096 else 512

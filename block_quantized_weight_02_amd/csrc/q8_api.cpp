@@ -328,9 +328,10 @@ q8_plan tile16_plan(int64_t m, int64_t K, int64_t N, int act_fmt) {
 // 1024: 27.5 and 25.8 against 68.2 and 67.5; m = 1024, N = 1024: 27.4
 // against 66.5; K = 14336, m = 512, N = 4096: 164.5 against 228.8; int8
 // m = 512, N = 4096 and 8192: 55.2 and 109.2 against 126.2 and 129.6;
-// m = 1024, N = 2048: 57.3 against 126.0.  The choice
-// depends on m, K, the format and the product's own width, so q8_gemm_parts
-// routes each part as q8_gemm would route it alone.
+// m = 1024, N = 2048: 57.3 against 126.0.  The choice depends on m, K, the
+// format and the width; q8_gemm_parts takes it for all its parts' columns
+// (q/k/v at m = 512, N = 4096 + 1024 + 1024, 768 workgroups: each part on
+// the tile kernel in one launch 80.7 us, the GEMM 73.4).
 struct GemmTileRoute {
   bool on;
   int rows, waves, kslices;
@@ -1240,59 +1241,49 @@ int run_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m, 
   if (act_fmt != Q8_ACT_BF16 && act_scales_offset_of(act_fmt, m, K) > 0xffffffffull)
     return fail(Q8_ERR_SHAPE, "m*K = %lld too large for the quantized layout",
                 (long long)(m * K));
-  // Each part goes where q8_gemm would take it alone: the parts of each kind
-  // side by side in one launch (so at most two launches).
-  GemmTileRoute route{false, 0, 0, 1};
-  bool tile_part[q8::kMaxParts] = {};
-  for (int i = 0; i < n_parts; ++i) {
-    const GemmTileRoute r = gemm_tile_route(m, K, parts[i].N, act_fmt);
-    tile_part[i] = r.on;
-    if (r.on) route = r;   // rows and waves depend on m, K and the format only
+  // One launch over the parts' tiles side by side, on the kernel q8_gemm
+  // would take for one product of all their columns.
+  q8::Parts pp{};
+  pp.n = n_parts;
+  pp.cum[0] = 0;
+  for (int i = 0; i < q8::kMaxParts; ++i) {
+    const bool on = i < n_parts;
+    pp.wq[i] = on ? parts[i].W_q8 : nullptr;
+    pp.wsc[i] = on ? parts[i].W_q8_scale : nullptr;
+    pp.y[i] = on ? parts[i].y : nullptr;
+    pp.bias[i] = on ? parts[i].bias : nullptr;
+    pp.N[i] = on ? (int)parts[i].N : 0;
+    pp.cum[i + 1] =
+        pp.cum[i] + (on ? (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS) : 0);
   }
-  hipError_t e = hipSuccess;
-  for (int kind = 0; kind < 2 && e == hipSuccess; ++kind) {
-    const bool tile = kind == 0;
-    q8::Parts pp{};
-    pp.cum[0] = 0;
-    for (int i = 0; i < n_parts; ++i) {
-      if (tile_part[i] != tile) continue;
-      const int k = pp.n++;
-      pp.wq[k] = parts[i].W_q8;
-      pp.wsc[k] = parts[i].W_q8_scale;
-      pp.y[k] = parts[i].y;
-      pp.bias[k] = parts[i].bias;
-      pp.N[k] = (int)parts[i].N;
-      pp.cum[k + 1] = pp.cum[k] + (int)(round_up(parts[i].N, Q8_TILE_COLS) / Q8_TILE_COLS);
-    }
-    for (int k = pp.n; k < q8::kMaxParts; ++k) pp.cum[k + 1] = pp.cum[k];
-    if (pp.n == 0) continue;
-    (void)hipGetLastError();
-    if (tile) {
-      q8::GemvArgs g{};
-      g.x = x;
-      g.m = (int)m;
-      g.K = (int)K;
-      g.NB = (int)(K / Q8_BLOCK);
-      g.T = pp.cum[pp.n];
-      g.Npad = g.T * Q8_TILE_COLS;
-      g.split_k = 1;
-      g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-      g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
-      g.ep.write_y = 1;
-      g.ep.nw = 1;
-      g.ep.parts = pp;
-      e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, route.kslices, false, g,
-                                 stream);
-    } else {
-      q8::GemmArgs a{};
-      a.x = x;
-      a.m = (int)m;
-      a.K = (int)K;
-      a.NB = (int)(K / Q8_BLOCK);
-      a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
-      a.parts = pp;
-      e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
-    }
+  const GemmTileRoute route = gemm_tile_route(m, K, cols, act_fmt);
+  hipError_t e;
+  (void)hipGetLastError();
+  if (route.on) {
+    q8::GemvArgs g{};
+    g.x = x;
+    g.m = (int)m;
+    g.K = (int)K;
+    g.NB = (int)(K / Q8_BLOCK);
+    g.T = pp.cum[n_parts];
+    g.Npad = g.T * Q8_TILE_COLS;
+    g.split_k = 1;
+    g.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+    g.act_view_off = act_fmt == Q8_ACT_Q8_0 ? (unsigned)act_view_offset(m, K) : 0u;
+    g.ep.write_y = 1;
+    g.ep.nw = 1;
+    g.ep.parts = pp;
+    e = q8::launch_gemv_tile16(route.rows, act_fmt, route.waves, route.kslices, false, g,
+                               stream);
+  } else {
+    q8::GemmArgs a{};
+    a.x = x;
+    a.m = (int)m;
+    a.K = (int)K;
+    a.NB = (int)(K / Q8_BLOCK);
+    a.act_scale_off = (unsigned)act_scales_offset_of(act_fmt, m, K);
+    a.parts = pp;
+    e = q8::launch_gemm(act_fmt, false, q8::gemm_rows_per_block(m), a, stream);
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();

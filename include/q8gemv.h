@@ -456,13 +456,14 @@ int q8_gemm_block_dots(const void *x_q8, const int8_t *W_q8, int32_t *dots,
  *     y_i[r, n] = (x . W_i)[r, n] + bias_i[n]        n < N_i (pad columns 0)
  * with q8_gemm's arithmetic; the parts (a host array, 1 <= n_parts <=
  * Q8_MAX_PARTS, padded widths summing to at most 2^24), x and act_fmt as in
- * q8_gemv_parts, for 1 <= m <= Q8_MAX_GEMM_ROWS.  Each part takes the kernel
- * q8_gemm would take for it alone (so the parts run as one launch, or two
- * when their widths put them on both kernels), and each part's columns start
- * a new column block of the GEMM (on the tile kernel every tile is its own
- * workgroup), so a part's outputs are bit-identical to q8_gemm on that part
- * alone (before the bias).  No workspace; allocates nothing.  Errors as
- * q8_gemv_parts.
+ * q8_gemv_parts, for 1 <= m <= Q8_MAX_GEMM_ROWS.  The launch takes the kernel
+ * q8_gemm would take for one product of all the parts' columns, and each
+ * part's columns start a new column block of the GEMM (on the tile kernel
+ * every tile is its own workgroup), so a part's outputs are bit-identical to
+ * q8_gemm on that part alone (before the bias) whenever q8_gemm takes the
+ * same kernel for it -- always up to 64 rows, and whenever the parts take
+ * the tile kernel -- and within the product's tolerance otherwise.  No
+ * workspace; allocates nothing.  Errors as q8_gemv_parts.
  */
 int q8_gemm_parts(const void *x, const q8_part *parts, int n_parts, int64_t m,
                   int64_t K, int act_fmt, hipStream_t stream);

@@ -1,5 +1,8 @@
-// q8_tile16.hip -- the product for up to 16 activation rows (bf16, or the
-// Q8_0 form) on the 16x16x32 matrix core, one workgroup per column tile.
+// q8_tile16.hip -- the product for few activation rows (bf16, or the Q8_0
+// form) on the 16x16x32 matrix core, one workgroup per column tile: 16, 32
+// or 64 rows a wave (RG row groups of 16, each block's weight turned into B
+// operands once for all of them), more rows in chunks of 64 (grid z), and
+// the parts' tiles side by side (a parts launch).
 //
 // The product (docs.logicaffeine.com, logicaffeine_compile/spatial/passes/
 // from_q8.rs, module doc and fn q8_fold): per Q8_0 block b the dot
@@ -42,8 +45,9 @@ using namespace dev;
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2v_t;
 
-// LDS: int8, the split's activation scales; bf16, a 2 KiB scratch per wave
-// (the activation transpose); then the carries' halves.
+// LDS: int8, the split's activation scales of the chunk's rows; bf16, a 2 KiB
+// scratch per wave and row group (the activation transpose); then the
+// carries' halves.
 template <int ACT, int W, int RG>
 constexpr size_t t16_lds_bytes(int nblk) {
   return (ACT == kActQ8 ? (size_t)nblk * 16 * RG * 4 : (size_t)W * 2048 * RG) +

@@ -173,7 +173,8 @@ def test_gemm_most_rows():
 
 # Up to 64 rows the product streams each column tile once through the
 # tile-per-workgroup kernel (16, 32 or 64 rows a wave; 8 waves, or 4 where a
-# long K's int8 activation scales fill the LDS); a K whose scales do not fit
+# long K's int8 activation scales fill the LDS, as at K = 14336, also in row
+# chunks); a K whose scales do not fit
 # even then goes to the GEMM.  Up to 1024 rows, chunks of 64 rows in
 # workgroups of their own while tiles x chunks stay within 512 (bf16) or 1024
 # (int8).
@@ -185,7 +186,8 @@ def test_gemm_most_rows():
                                        (128, 4096, 14336, BF16), (200, 4096, 14336, Q8),
                                        (256, 4096, 4096, BF16), (96, 4096, 24576, BF16),
                                        (250, 5120, 1000, Q8), (512, 4096, 2048, BF16),
-                                       (1024, 4096, 1024, BF16), (1000, 2048, 2048, Q8)])
+                                       (1024, 4096, 1024, BF16), (1000, 2048, 2048, Q8),
+                                       (130, 14336, 512, Q8)])
 def test_gemm_tile_rows_full_size(m, K, N, act):
     x, q, s = inputs.random_case(m, K, N, seed=5300 + m + K // 32 + N)
     Wq, Ws = g.pack(q, s)

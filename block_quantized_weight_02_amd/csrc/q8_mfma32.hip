@@ -52,8 +52,18 @@ struct M32Stage {
   uint4 a[AG ? U : 1];  // direct form: the activation fragment (row j, k = 16h ..)
 };
 
+// Place of row r's scale of block lb in the stage below: [block][row], the
+// row's group of four (r / 4) stored at group (r / 4) ^ (lb % 8).  The
+// stage's writes go down a column (consecutive blocks of one row), which
+// unswizzled all fall into one LDS bank (a 128-byte stride); the swizzle
+// spreads them over eight.  A group stays whole, so a reader's float4 of
+// rows 4g .. 4g+3 is still one 16-byte load.
+__device__ __forceinline__ int dx_slot(int lb, int r) {
+  return lb * 32 + ((((r >> 2) ^ (lb & 7)) << 2) | (r & 3));
+}
+
 // The direct form's stage of the activation scales of blocks [b_lo, b_lo +
-// nblk) into LDS, [block][row] fp32, rows m..31 zero.
+// nblk) into LDS (dx_slot order), rows m..31 zero.
 // Consecutive threads read consecutive blocks of one row (the buffer's
 // scales are row-major), so the loads are coalesced; the LDS write is the
 // transpose.
@@ -65,7 +75,7 @@ __device__ __forceinline__ void stage_act_scales(float *dxs, const void *__restr
       reinterpret_cast<const float *>(static_cast<const char *>(xv) + act_scale_off);
   for (int p = threadIdx.x; p < nblk * 32; p += NTHREADS) {
     const int r = p / nblk, bb = p - r * nblk;
-    dxs[bb * 32 + r] = (r < m) ? dxp[(size_t)r * NB + b_lo + bb] : 0.0f;
+    dxs[dx_slot(bb, r)] = (r < m) ? dxp[(size_t)r * NB + b_lo + bb] : 0.0f;
   }
 }
 
@@ -323,8 +333,8 @@ gemv_mfma32_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 dx4 =
-                *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + 8 * q + 4 * h);
+            const float4 dx4 = *reinterpret_cast<const float4 *>(
+                dxs + (AG ? (size_t)dx_slot(lb, 8 * q + 4 * h) : (size_t)lb * MR + 8 * q + 4 * h));
             const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -573,7 +583,7 @@ gemv_mfma32w_kernel(const void *__restrict__ xv, const int8_t *__restrict__ wq,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float4 dx4 =
-              *reinterpret_cast<const float4 *>(dxs + (size_t)lb * MR + 8 * q + 4 * h);
+              *reinterpret_cast<const float4 *>(dxs + dx_slot(lb, 8 * q + 4 * h));
           const float dxv[4] = {dx4.x, dx4.y, dx4.z, dx4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
